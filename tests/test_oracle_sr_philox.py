@@ -1,0 +1,154 @@
+"""Pins of the oracle's stochastic rounding and its Philox stream.
+
+Stochastic rounding is defined on the aibr.jp stochastic-rounding explainer
+(core-technique paragraph): one of the two neighbouring representable values is
+chosen with a probability set by the distance, so the expected value equals the
+input. The Philox4x32-10 stream is pinned against two independent
+implementations: numpy's Philox4x64-10 (same round structure and key schedule,
+one shared body in the oracle) and rocRAND's Philox4x32-10 engine, built here
+from its header as a host program.
+"""
+
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from test_oracle_formats import nearest_code, torch_e4m3_table
+
+HELPER = os.path.join(os.path.dirname(__file__), "helpers", "rocrand_philox_words.cpp")
+
+
+# ---------------------------------------------------------------- Philox
+
+def test_philox4x64_matches_numpy(orc):
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        key = int(rng.integers(0, 2**63)) << 65 | int(rng.integers(0, 2**63))
+        key &= (1 << 128) - 1
+        ctr = int(rng.integers(0, 2**63)) * (trial % 5)
+        if trial == 3:
+            ctr = (1 << 64) - 1          # carry into the second word
+        bg = np.random.Philox(key=key, counter=ctr)
+        raw = bg.random_raw(4)
+        c = ctr + 1                      # numpy encrypts the incremented counter
+        words = [(c >> (64 * i)) & (2**64 - 1) for i in range(4)]
+        got = orc.philox4x64(words, [key & (2**64 - 1), key >> 64])
+        assert [int(v) for v in got] == [int(v) for v in raw]
+
+
+@pytest.fixture(scope="module")
+def rocrand_words(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND helper")
+    exe = str(tmp_path_factory.mktemp("rocrand") / "rp")
+    subprocess.check_call([hipcc, "-O1", "-o", exe, HELPER], cwd="/tmp")
+
+    def run(seed, sub, off, n):
+        out = subprocess.check_output([exe, str(seed), str(sub), str(off), str(n)], text=True)
+        return np.array([int(v) for v in out.split()], dtype=np.uint64)
+    return run
+
+
+def test_philox4x32_stream_matches_rocrand(orc, rocrand_words):
+    # the stochastic-rounding word of element n under (seed, offset) is word
+    # n of rocRAND's engine seeded with `seed` at subsequence `offset`
+    cases = [(0x5EED, 0, 0, 4096), (0, 0, 0, 64), (0xFFFFFFFFFFFFFFFF, 7, 123, 257),
+             (0x123456789ABCDEF0, 1 << 40, (1 << 34) + 5, 300), (42, 3, (1 << 32) - 2, 64)]
+    for seed, offset, n0, count in cases:
+        want = rocrand_words(seed, offset, n0, count)
+        got = orc.sr_words(seed, offset, n0, count).astype(np.uint64)
+        assert (got == want).all(), (seed, offset, n0)
+
+
+def test_philox4x32_uniformity(orc):
+    w = orc.sr_words(0x5EED, 0, 0, 1 << 18)
+    for shift in (0, 8, 16, 24):
+        byte = (w >> shift) & 0xFF
+        counts = np.bincount(byte, minlength=256)
+        expect = w.size / 256
+        chi2 = ((counts - expect) ** 2 / expect).sum()
+        assert chi2 < 255 + 8 * np.sqrt(2 * 255)  # ~8 sigma band for 255 dof
+    bits = np.unpackbits(w.view(np.uint8))
+    assert abs(bits.mean() - 0.5) < 5 * 0.5 / np.sqrt(bits.size)
+
+
+# ---------------------------------------------------------------- SR
+
+def _neighbours(pos, v):
+    """Round-down and round-up neighbours of |v| on the finite grid (brute force)."""
+    a = np.abs(v)
+    hi = np.searchsorted(pos, a, side="left")
+    hi = np.clip(hi, 0, len(pos) - 1)
+    exact = pos[hi] == a
+    lo = np.where(exact, hi, np.clip(hi - 1, 0, len(pos) - 1))
+    return lo, hi
+
+
+def test_sr_result_is_a_neighbour(orc):
+    tab = torch_e4m3_table()
+    pos = tab[:127]
+    rng = np.random.default_rng(22)
+    v = np.ldexp(rng.uniform(1, 2, 200_000), rng.integers(-12, 9, 200_000))
+    v = np.clip(v, 0, 448) * np.where(rng.random(v.size) < 0.5, -1, 1)
+    r = orc.sr_words(7, 0, 0, v.size)
+    got = orc.encode_array("e4m3", "sr", v, r)
+    lo, hi = _neighbours(pos, v)
+    mag = got & 0x7F
+    assert np.all((mag == lo) | (mag == hi))
+    assert np.all((got >> 7) == np.signbit(v))
+
+
+def test_sr_exact_on_grid(orc):
+    tab = torch_e4m3_table()
+    fin = np.array([c for c in range(256) if not np.isnan(tab[c])])
+    for r in (0, 1, 12345, 0xFFFFFFFF):
+        got = orc.encode_array("e4m3", "sr", tab[fin], np.full(fin.size, r))
+        assert (got == fin).all()
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("frac", [0.001, 0.1, 0.25, 0.5, 0.75, 0.9])
+def test_sr_probability_follows_distance(orc, elem, frac):
+    # value between two neighbours at fractional distance `frac`; P(up) must be frac
+    if elem == "e4m3":
+        lo, hi = 1.25, 1.375
+    else:
+        lo, hi = 1.0, 1.5
+    v = lo + frac * (hi - lo)
+    n = 200_000
+    r = orc.sr_words(0xABC, 1, 0, n)
+    got = orc.encode_array(elem, "sr", np.full(n, v), r)
+    up = orc.encode(elem, "rne", hi)
+    down = orc.encode(elem, "rne", lo)
+    assert set(np.unique(got)) <= {up, down}
+    p_hat = (got == up).mean()
+    sigma = np.sqrt(frac * (1 - frac) / n)
+    assert abs(p_hat - frac) < 5 * sigma + 1e-9
+
+
+def test_sr_is_unbiased(orc):
+    tab = torch_e4m3_table()
+    rng = np.random.default_rng(23)
+    n = 1_000_000
+    v = np.ldexp(rng.uniform(1, 2, n), rng.integers(-9, 8, n))
+    r = orc.sr_words(0x5EED, 0, 0, n)
+    got = tab[orc.encode_array("e4m3", "sr", v, r)]
+    # error in units of the local quantum (2^(floor(log2 v) - 3), min 2^-9)
+    q = np.ldexp(1.0, np.maximum(np.floor(np.log2(v)).astype(int), -6) - 3)
+    e = (got - v) / q
+    assert np.all(np.abs(e) < 1)
+    assert abs(e.mean()) < 5 * e.std() / np.sqrt(n)
+    # RNE on the same values is biased only by ties; SR spreads both ways
+    assert (e > 0).mean() > 0.3 and (e < 0).mean() > 0.3
+
+
+def test_sr_saturates(orc):
+    r = np.array([0, 1 << 31, 0xFFFFFFFF], np.uint32)
+    got = orc.encode_array("e4m3", "sr", np.full(3, 470.0), r)
+    assert (got == 0x7E).all()
+    got = orc.encode_array("e2m1", "sr", np.full(3, -7.5), r)
+    assert (got == 0xF).all()
