@@ -1,0 +1,152 @@
+/*
+ * mxq.h - C ABI of libmxq: MXNorm fused with the MX cast, the two-pass
+ * RMSNorm -> MXCast comparison path, and MXCast on its own, for AMD MI355X
+ * (gfx950).
+ *
+ * What the operations compute is defined on the page "MXNorm: Reusing MXFP
+ * block scales for efficient tensor normalisation" (gist.science technical
+ * summary):
+ *   §1.1  RMSNorm computes its statistic over the hidden dimension;
+ *   §1.2  RMSNorm and the cast to MXFP (MXCast) normally run as separate
+ *         steps, both aggregating statistics along the hidden dimension;
+ *   §2.1  MX formats split a tensor into blocks of size B, each with one
+ *         E8M0 scale derived from the block absmax; MXNorm takes the block
+ *         absmaxes m_k, forms the power mean G = ((1/K) sum_k m_k^p)^(1/p)
+ *         as the stand-in for the RMS, normalises by it and casts to MXFP in
+ *         the same pass;
+ *   §2.3  the gain gamma may be folded into the next linear layer's weights
+ *         (pass gamma = NULL);
+ *   §4    a drop-in for pre-norm RMSNorm whose only new knob is p.
+ * The element formats follow the page "Recipes for Pre-training LLMs with
+ * MXFP8" (E4M3 elements) and its related entries "FP8 Formats for Deep
+ * Learning" (E4M3 without infinities, one NaN pattern) and "Microscaling Data
+ * Formats for Deep Learning" (per-block scale with narrow elements); FP4 is the
+ * E2M1 element. Stochastic rounding follows the aibr.jp stochastic-rounding
+ * explainer (a neighbour chosen with probability by distance, unbiased).
+ *
+ * Fixed conventions (the pages leave these open):
+ *   - bf16 input x [T, D] row-major with row stride ldx (elements); B = 32
+ *     contiguous elements along D; K = D / 32; D must be a multiple of 32.
+ *   - E8M0 scale of a block with absmax a: s = floor(log2 a) - emax clamped
+ *     to [-127, 127], stored as s + 127 (emax 8 for E4M3, 2 for E2M1);
+ *     a == 0 stores 0; a block holding NaN/Inf stores 0xFF and all its codes
+ *     are 0x7F (E4M3) or 0x7 (E2M1).
+ *   - elements are x / 2^s rounded to nearest-even (or stochastically),
+ *     saturating at 448 (E4M3) or 6 (E2M1); the sign of zero is kept.
+ *   - E2M1 codes are packed two per byte, element 2j in bits 3:0.
+ *   - MXNorm normaliser: inv = RN32(1 / G) with G computed in fp32 from the
+ *     exact block maxima (no epsilon, no c(p,B) factor); G == 0 gives inv = 0;
+ *     a row holding NaN/Inf gives inv = NaN. y = RN32(RN32(x * gamma) * inv).
+ *     inv is accurate to 1e-5 relative while G lies in [2^-126, 2^126].
+ *   - RMSNorm: inv = 1 / sqrt(sum(x^2) / D + eps) in fp32 and
+ *     y = bf16_rne(RN32(RN32(x * gamma) * inv)).
+ *   - Stochastic rounding: element n = t * D + d draws word (n & 3) of
+ *     Philox4x32-10 (Salmon et al., SC'11) with key = seed (low word first)
+ *     and counter = (n >> 2 as two words, offset as two words); it rounds up
+ *     iff word < floor(frac * 2^32), frac the distance above the lower
+ *     neighbour in units of the local quantum.
+ *
+ * Memory and execution:
+ *   - every pointer is a device pointer owned by the caller; the library
+ *     never allocates, frees, or keeps a pointer after returning.
+ *   - outputs are contiguous: codes [T, D] bytes (E4M3) or [T, D/2] bytes
+ *     (E2M1), scales [T, D/32] bytes, per-row normalisers [T] fp32.
+ *   - alignment: x, gamma, codes and y_workspace 16 bytes; ldx % 8 == 0 and
+ *     ldx >= D; scales and the normaliser arrays need none beyond their type.
+ *   - calls enqueue work on `stream` (a hipStream_t; NULL is the default
+ *     stream) and return without waiting. Arguments are validated before any
+ *     HIP call; a launch failure returns MXQ_ERR_HIP; a device fault shows at
+ *     the caller's next synchronisation.
+ *   - T == 0 is a valid empty call (pointers are not read).
+ *   - no global mutable state: calls are thread-safe.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MXQ_ERR_SHAPE = 2,       /* T < 0, D <= 0, D % 32 != 0, or ldx < D             */
+  MXQ_ERR_ALIGN = 3,       /* a pointer or ldx breaks the alignment rules above  */
+  MXQ_ERR_ARG = 4,         /* bad p / eps / element / rounding / flags / rng     */
+  MXQ_ERR_UNSUPPORTED = 5, /* D beyond the largest row the kernels hold         */
+  MXQ_ERR_HIP = 6          /* the HIP runtime refused the launch                 */
+} mxq_status;
+
+typedef enum { MXQ_E4M3 = 0, MXQ_E2M1 = 1 } mxq_elem;
+typedef enum { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
+
+/* Stochastic-rounding stream: read only when rnd == MXQ_SR. The same
+ * (seed, offset) reproduces the same bits; callers advance offset per call. */
+typedef struct {
+  uint64_t seed;
+  uint64_t offset;
+} mxq_rng;
+
+/* mxnorm_fwd variant selection (0 = automatic by D). */
+enum {
+  MXQ_FLAG_FORCE_REG = 1u, /* row held in registers (D <= 8192)               */
+  MXQ_FLAG_FORCE_LDS = 2u  /* row staged in LDS (D <= MXQ_MAX_D)              */
+};
+
+/* Largest D of the register-resident MXNorm path and of any path. */
+#define MXQ_MAX_D_REG 8192
+#define MXQ_MAX_D 65536
+
+/*
+ * Fused MXNorm -> MX cast (MXNorm page, §2.1 and §2.3).
+ *   x        [T, D] bf16 bits, row stride ldx.
+ *   gamma    [D] bf16 bits, or NULL for gamma == 1 (folded into the next layer).
+ *   p        power of the mean: > 0, or +INFINITY for the block-max maximum.
+ *   elem     MXQ_E4M3 (codes [T, D]) or MXQ_E2M1 (codes [T, D/2]).
+ *   rnd      MXQ_RNE, or MXQ_SR with rng != NULL.
+ *   flags    0, MXQ_FLAG_FORCE_REG or MXQ_FLAG_FORCE_LDS; both variants give
+ *            bit-identical results.
+ *   codes, scales  outputs; inv_norm [T] fp32 output, may be NULL.
+ * Errors: NULL (x, codes, scales), SHAPE, ALIGN, ARG (p <= 0 or NaN, unknown
+ * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large), HIP.
+ */
+mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                      int64_t D, float p, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
+                      uint32_t flags, uint8_t* codes, uint8_t* scales, float* inv_norm,
+                      void* stream);
+
+/*
+ * Two-pass comparison path (MXNorm page, §1.1 and §1.2): RMSNorm writes bf16
+ * y to y_workspace [T, D] (contiguous, caller-owned), then MXCast reads it.
+ *   eps      >= 0 and finite.
+ *   inv_rms  [T] fp32 output, may be NULL.
+ * Other arguments and errors as for mxnorm_fwd (y_workspace NULL -> NULL).
+ */
+mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                              int64_t T, int64_t D, float eps, mxq_elem elem, mxq_round rnd,
+                              const mxq_rng* rng, uint16_t* y_workspace, uint8_t* codes,
+                              uint8_t* scales, float* inv_rms, void* stream);
+
+/*
+ * MXCast of a bf16 activation (MXNorm page, §1.2 and §2.1): block absmax,
+ * E8M0 scale and element cast, with no normalisation.
+ */
+mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
+                      mxq_round rnd, const mxq_rng* rng, uint8_t* codes, uint8_t* scales,
+                      void* stream);
+
+/* Static message for a status code (never NULL). */
+const char* mxq_strerror(mxq_status status);
+
+/* MXQ_ABI_VERSION of the built library. */
+int mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,199 @@
+"""norm_mx_quantisation_amd: MXNorm fused with the MX cast on MI355X (gfx950).
+
+Thin ctypes binding of libmxq.so. The functions named like the C entry points
+(mxnorm_fwd, rmsnorm_mxcast_fwd, mxcast_fwd, mxq_strerror, mxq_abi_version)
+take raw device pointers and sizes and return the status code, exactly as the
+C ABI does. The torch helpers (mxnorm, rmsnorm_mxcast, mxcast) only check
+tensor metadata, allocate the outputs and pass pointers; every step of the
+computation runs in the HIP kernels. There is no CPU fallback: without the
+built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmxq.so")
+
+MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_HIP = range(7)
+MXQ_E4M3, MXQ_E2M1 = 0, 1
+MXQ_RNE, MXQ_SR = 0, 1
+MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS = 1, 2
+MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 65536
+ABI_VERSION = 1
+
+EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "mxcast_fwd", "mxq_strerror", "mxq_abi_version")
+
+
+class mxq_rng(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({mxq_strerror(status)})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded libmxq.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"libmxq.so is not built ({LIB_PATH}); run "
+                    "`python -m norm_mx_quantisation_amd.build` or __graft_entry__.build()")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i64, f32, i32, u32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_uint32)
+            rp = ctypes.POINTER(mxq_rng)
+            L.mxnorm_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, u32, vp, vp, vp, vp]
+            L.mxnorm_fwd.restype = i32
+            L.rmsnorm_mxcast_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, vp, vp, vp,
+                                             vp, vp]
+            L.rmsnorm_mxcast_fwd.restype = i32
+            L.mxcast_fwd.argtypes = [vp, i64, i64, i64, i32, i32, rp, vp, vp, vp]
+            L.mxcast_fwd.restype = i32
+            L.mxq_strerror.argtypes = [i32]
+            L.mxq_strerror.restype = ctypes.c_char_p
+            L.mxq_abi_version.argtypes = []
+            L.mxq_abi_version.restype = i32
+            if L.mxq_abi_version() != ABI_VERSION:
+                raise RuntimeError("libmxq.so ABI version mismatch")
+            _lib = L
+    return _lib
+
+
+def _rng(rng) -> Optional[ctypes.POINTER(mxq_rng)]:
+    if rng is None:
+        return None
+    if isinstance(rng, mxq_rng):
+        return ctypes.pointer(rng)
+    seed, offset = rng
+    return ctypes.pointer(mxq_rng(seed, offset))
+
+
+# ---------------------------------------------------------------- raw C entry points
+
+def mxnorm_fwd(x, ldx, gamma, T, D, p, elem, rnd, rng, flags, codes, scales, inv_norm,
+               stream) -> int:
+    return lib().mxnorm_fwd(x, ldx, gamma, T, D, p, elem, rnd, _rng(rng), flags, codes, scales,
+                            inv_norm, stream)
+
+
+def rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, y_workspace, codes, scales,
+                       inv_rms, stream) -> int:
+    return lib().rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, _rng(rng), y_workspace,
+                                    codes, scales, inv_rms, stream)
+
+
+def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, codes, scales, stream) -> int:
+    return lib().mxcast_fwd(x, ldx, T, D, elem, rnd, _rng(rng), codes, scales, stream)
+
+
+def mxq_strerror(status: int) -> str:
+    return lib().mxq_strerror(status).decode()
+
+
+def mxq_abi_version() -> int:
+    return lib().mxq_abi_version()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+_ELEM = {"e4m3": MXQ_E4M3, "e2m1": MXQ_E2M1}
+_RND = {"rne": MXQ_RNE, "sr": MXQ_SR}
+
+
+def _check_x(x):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must live on the GPU (there is no CPU path)")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    T, D = x.shape
+    return T, D, (x.stride(0) if T > 1 else D)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _outputs(x, T, D, elem, want_inv):
+    import torch
+    cb = D // 2 if elem == MXQ_E2M1 else D
+    codes = torch.empty((T, cb), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, D // 32), dtype=torch.uint8, device=x.device)
+    inv = torch.empty((T,), dtype=torch.float32, device=x.device) if want_inv else None
+    return codes, scales, inv
+
+
+def mxnorm(x, gamma=None, p: float = 2.0, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0,
+           offset: int = 0, flags: int = 0, stream=None, out=None):
+    """Fused MXNorm -> MX cast. Returns (codes uint8, scales uint8 E8M0, inv_norm fp32)."""
+    T, D, ldx = _check_x(x)
+    elem, rnd = _ELEM[fmt], _RND[rounding]
+    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
+    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    st = mxnorm_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(p), elem, rnd,
+                    (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(codes), _ptr(scales),
+                    _ptr(inv), _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "mxnorm_fwd")
+    return codes, scales, inv
+
+
+def rmsnorm_mxcast(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3", rounding: str = "rne",
+                   seed: int = 0, offset: int = 0, stream=None, out=None, y=None):
+    """Two-pass RMSNorm (bf16 y) -> MXCast. Returns (codes, scales, inv_rms, y)."""
+    import torch
+    T, D, ldx = _check_x(x)
+    elem, rnd = _ELEM[fmt], _RND[rounding]
+    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
+    if y is None:
+        y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    st = rmsnorm_mxcast_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(eps), elem, rnd,
+                            (seed, offset) if rnd == MXQ_SR else None, _ptr(y), _ptr(codes),
+                            _ptr(scales), _ptr(inv), _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "rmsnorm_mxcast_fwd")
+    return codes, scales, inv, y
+
+
+def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: int = 0,
+           stream=None, out=None):
+    """MXCast. Returns (codes, scales)."""
+    T, D, ldx = _check_x(x)
+    elem, rnd = _ELEM[fmt], _RND[rounding]
+    codes, scales, _ = out if out is not None else _outputs(x, T, D, elem, False)
+    st = mxcast_fwd(_ptr(x), ldx, T, D, elem, rnd, (seed, offset) if rnd == MXQ_SR else None,
+                    _ptr(codes), _ptr(scales), _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "mxcast_fwd")
+    return codes, scales
+
+
+def as_torch_mx(codes, scales, fmt: str = "e4m3"):
+    """Views of the outputs as torch's float8_e4m3fn / float4_e2m1fn_x2 and float8_e8m0fnu."""
+    import torch
+    c = codes.view(torch.float8_e4m3fn) if fmt == "e4m3" else codes.view(torch.float4_e2m1fn_x2)
+    return c, scales.view(torch.float8_e8m0fnu)

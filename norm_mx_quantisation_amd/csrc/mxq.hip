@@ -1,0 +1,820 @@
+// mxq.hip - gfx950 kernels and the C ABI of libmxq (see include/mxq.h).
+//
+// Operations (page "MXNorm: Reusing MXFP block scales for efficient tensor
+// normalisation", gist.science technical summary):
+//   * mxnorm_fwd         §2.1: block absmax m_k, power mean G of the m_k,
+//                        y = x * gamma / G, E8M0 scale per 32-block and the
+//                        element cast, in one read of x and one write;
+//   * rmsnorm_mxcast_fwd §1.1/§1.2: RMSNorm to a bf16 tensor, then MXCast
+//                        (two kernels, the comparison path);
+//   * mxcast_fwd         §1.2/§2.1: MXCast alone.
+//
+// Work layout (one wavefront = 64 lanes; one "chunk" = 512 contiguous
+// elements of a row, one 16-byte load per lane; a 32-element MX block is the
+// 4 lanes of a quad):
+//   * MXNorm / RMSNorm: one wavefront per row, 4 rows per 256-thread
+//     workgroup. Block maxima come from packed-u16 max on the bf16 bit
+//     patterns plus two DPP quad steps; the row statistic is a butterfly
+//     over the 16 quads; nothing crosses waves, so there is no barrier.
+//     The register variant keeps the row in VGPRs (D <= 8192); the LDS
+//     variant stages it with direct-to-LDS 16-byte loads and uses the same
+//     reduction order, so both give identical bits.
+//   * MXCast: every chunk is independent; each wavefront handles 4 chunks.
+//   * Element casts use the gfx950 scaled converts (the E8M0 code is the
+//     exponent field of the fp32 scale operand, which divides). The FP8
+//     convert does not saturate, so values are clamped to +-448 * 2^s first;
+//     the FP4 convert saturates by itself. Stochastic rounding is integer
+//     code on Philox4x32-10 words.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mxq.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 512;           // elements per wave-wide chunk
+constexpr int kRowsPerBlock = 4;      // wavefronts (rows) per workgroup
+constexpr int kThreads = kWave * kRowsPerBlock;
+constexpr int kCastChunksPerWave = 4; // MXCast chunks per wavefront
+
+enum PMode { P_ONE = 0, P_TWO = 1, P_INF = 2, P_GEN = 3 };
+
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4& r, float v[8]) {
+  v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+  v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+  v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+  v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+}
+
+// Largest |x| of 8 bf16 values as a bit pattern with the sign cleared. For
+// non-negative bf16 the integer order is the magnitude order, with +Inf
+// (0x7F80) below every NaN, so a non-finite element always surfaces.
+__device__ __forceinline__ uint32_t absmax_bits8(const uint4& r) {
+  const uint32_t k = 0x7FFF7FFFu;
+  u16x2 a = __builtin_bit_cast(u16x2, r.x & k);
+  u16x2 b = __builtin_bit_cast(u16x2, r.y & k);
+  u16x2 c = __builtin_bit_cast(u16x2, r.z & k);
+  u16x2 d = __builtin_bit_cast(u16x2, r.w & k);
+  u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                      __builtin_elementwise_max(c, d));
+  uint32_t mm = __builtin_bit_cast(uint32_t, m);
+  return max(mm & 0xFFFFu, mm >> 16);
+}
+
+// Max over the 4 lanes of a quad (one MX block); exact, so any order is fine.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false)); // [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false)); // [2,3,0,1]
+  return v;
+}
+
+// Sum of a value held identically by the 4 lanes of each quad, over the 16
+// quads. XOR butterflies make every lane compute the same bits.
+__device__ __forceinline__ float sum_over_quads(float v) {
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ uint32_t max_over_quads(uint32_t v) {
+  v = max(v, (uint32_t)__shfl_xor((int)v, 4));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 8));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ float sum_over_wave(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  return sum_over_quads(v);
+}
+
+// ------------------------------------------------------------------ p-mean
+
+// Term of the power mean for one block maximum m (m >= 0).
+__device__ __forceinline__ float pmean_add(float s, float m, int pmode, float p) {
+  if (pmode == P_ONE) return s + m;
+  if (pmode == P_TWO) return __builtin_fmaf(m, m, s);
+  return s + exp2f(p * log2f(m));  // m == 0 -> exp2(-inf) == 0
+}
+
+__device__ __forceinline__ float pmean_finish(float s, int pmode, float p, float K) {
+  float q = s / K;
+  if (pmode == P_ONE) return q;
+  if (pmode == P_TWO) return sqrtf(q);
+  return exp2f(log2f(q) / p);
+}
+
+// Sum of the power-mean terms of this lane's chunks, in chunk order, of the
+// block maxima scaled by 2^shift. NCT > 0 gives a compile-time (unrolled)
+// chunk count, NCT == 0 the runtime count.
+template <int NCT, class BlockMax>
+__device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift, int pmode, float p) {
+  float s = 0.0f;
+  if constexpr (NCT > 0) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), pmode, p);
+  } else {
+    for (int c = 0; c < nchunks; ++c)
+      s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), pmode, p);
+  }
+  return s;
+}
+
+// Normaliser 1/G of a row from its block maxima (bf16 bit patterns, one per
+// chunk for this lane's quad, zero for blocks past the row end). rmax is the
+// row maximum of the patterns. Terms are added chunk by chunk in each lane,
+// then over the quads; every variant uses exactly this order.
+template <int NCT, class BlockMax>
+__device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, uint32_t rmax, int pmode,
+                                                float p, float K) {
+  if (rmax >= 0x7F80u) return __builtin_nanf("");  // the row holds NaN or Inf
+  if (rmax == 0u) return 0.0f;                      // all-zero row
+  if (pmode == P_INF) return 1.0f / __uint_as_float(rmax << 16);
+  float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, 0, pmode, p));
+  if (s >= 0x1p-96f && s <= 0x1p96f) return 1.0f / pmean_finish(s, pmode, p, K);
+  // The p-th powers left the range where fp32 holds them accurately (an
+  // underflowing or overflowing sum): rescale the maxima by 2^-E, E the
+  // exponent of the row maximum, and undo it on G.
+  int E = (int)((rmax >> 7) & 0xFFu) - 127;
+  if (E < -126) E = -126;
+  s = sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p));
+  return 1.0f / ldexpf(pmean_finish(s, pmode, p, K), E);
+}
+
+// ------------------------------------------------------------------ scales
+
+template <int ELEM>
+__device__ __forceinline__ uint32_t e8m0_code(float amax) {
+  // floor(log2 a) - emax + 127 from the fp32 exponent field, clamped at 0;
+  // exponent 0xFF (NaN / Inf) gives 0xFF. a >= 0 here.
+  constexpr int kEmax = (ELEM == MXQ_E4M3) ? 8 : 2;
+  uint32_t e = (__float_as_uint(amax) >> 23) & 0xFFu;
+  if (e == 0xFFu) return 0xFFu;
+  return e > (uint32_t)kEmax ? e - kEmax : 0u;
+}
+
+// ------------------------------------------------------------------ Philox
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53
+// and 0xCD9E8D57, key increments 0x9E3779B9 and 0xBB67AE85.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+struct SrStream {
+  uint32_t k0, k1, o0, o1;
+  // Words for logical elements n0 .. n0+7 (n0 % 8 == 0).
+  __device__ __forceinline__ void words8(uint64_t n0, uint32_t r[8]) const {
+    const uint64_t b = n0 >> 2;
+    const uint4 a = philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), o0, o1, k0, k1);
+    const uint4 c = philox4x32_10((uint32_t)(b + 1), (uint32_t)((b + 1) >> 32), o0, o1, k0, k1);
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = c.x; r[5] = c.y; r[6] = c.z; r[7] = c.w;
+  }
+};
+
+// ------------------------------------------------------------------ encode
+
+// 8 values y (not yet divided by the scale) -> 8 E4M3 codes, RNE, saturating.
+__device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], uint32_t code) {
+  if (code == 0xFFu) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const float scale = __uint_as_float(code << 23);                  // 2^(code-127)
+  const float lim = __uint_as_float(((code + 8u) << 23) | 0x00600000u); // 448 * 2^(code-127)
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = __builtin_amdgcn_fmed3f(y[j], -lim, lim);
+  short2_t a = {0, 0}, b = {0, 0};
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, w[0], w[1], scale, false);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, w[2], w[3], scale, true);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[4], w[5], scale, false);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[6], w[7], scale, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+// 8 values -> 8 E2M1 codes packed in one word (element 2j in the low nibble).
+__device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], uint32_t code) {
+  if (code == 0xFFu) return 0x77777777u;
+  const float scale = __uint_as_float(code << 23);
+  uint32_t q = 0;
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[0], y[1], scale, 0);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[2], y[3], scale, 1);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[4], y[5], scale, 2);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[6], y[7], scale, 3);
+  return q;
+}
+
+// Stochastic rounding of v (already divided by the scale, |v| < 2^(emax+1)):
+// with M the 24-bit significand and the quantum 2^sh units of it, n = M >> sh
+// and frac32 = floor(frac * 2^32) are the bits below; round up iff r < frac32.
+template <int ELEM>
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
+  // E4M3: normal binades keep 3 of 23 mantissa bits (sh = 20); below 2^-6 the
+  // quantum is 2^-9 (sh = 141 - e). E2M1: sh = 22 and quantum 2^-1 below 1.
+  constexpr int kShNorm = (ELEM == MXQ_E4M3) ? 20 : 22;
+  constexpr int kShBase = (ELEM == MXQ_E4M3) ? 141 : 149;
+  constexpr int kEmin = (ELEM == MXQ_E4M3) ? 121 : 127;  // biased fp32 exponent of min normal
+  constexpr int kMbits = (ELEM == MXQ_E4M3) ? 3 : 1;
+  constexpr uint32_t kMaxCode = (ELEM == MXQ_E4M3) ? 0x7Eu : 0x7u;
+  constexpr int kSignBit = (ELEM == MXQ_E4M3) ? 7 : 3;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 31) << kSignBit;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const int e = (int)(a >> 23);
+  const uint32_t m24 = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  const int ee = e ? e : 1;
+  const int sh = max(kShBase - ee, kShNorm);
+  const uint32_t n = sh < 32 ? (m24 >> sh) : 0u;
+  const uint32_t frac = (uint32_t)(((uint64_t)m24 << 32) >> min(sh, 63));
+  const uint32_t up = r < frac ? 1u : 0u;
+  uint32_t code = (ee > kEmin ? (uint32_t)(ee - kEmin) << kMbits : 0u) + n + up;
+  code = min(code, kMaxCode);
+  return code | sign;
+}
+
+__device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], uint32_t code, const uint32_t r[8]) {
+  if (code == 0xFFu) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const float inv_scale = __uint_as_float((254u - code) << 23);  // 2^-(code-127), a normal float
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = sr_code<MXQ_E4M3>(y[j] * inv_scale, r[j]);
+  return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                    c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+}
+
+__device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], uint32_t code, const uint32_t r[8]) {
+  if (code == 0xFFu) return 0x77777777u;
+  const float inv_scale = __uint_as_float((254u - code) << 23);
+  uint32_t q = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q |= sr_code<MXQ_E2M1>(y[j] * inv_scale, r[j]) << (4 * j);
+  return q;
+}
+
+// Encode and store 8 elements at element offset n_row + d of a contiguous
+// [T, D] code tensor (n_row = t * D).
+template <int ELEM, int RND>
+__device__ __forceinline__ void encode_store8(uint8_t* codes, uint64_t n, const float y[8],
+                                              uint32_t code, const SrStream& rng) {
+  if (RND == MXQ_SR) {
+    uint32_t r[8];
+    rng.words8(n, r);
+    if (ELEM == MXQ_E4M3)
+      *reinterpret_cast<uint2*>(codes + n) = encode8_e4m3_sr(y, code, r);
+    else
+      *reinterpret_cast<uint32_t*>(codes + (n >> 1)) = encode8_e2m1_sr(y, code, r);
+  } else {
+    if (ELEM == MXQ_E4M3)
+      *reinterpret_cast<uint2*>(codes + n) = encode8_e4m3_rne(y, code);
+    else
+      *reinterpret_cast<uint32_t*>(codes + (n >> 1)) = encode8_e2m1_rne(y, code);
+  }
+}
+
+// ------------------------------------------------------------------ MXNorm
+
+struct NormArgs {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* inv_out;
+  int64_t ldx;
+  int64_t T;
+  int D;
+  int K;
+  float Kf;
+  float p;
+  int pmode;
+  SrStream rng;
+};
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Second half of a row: normalise, scale, cast and store one chunk. xb is the
+// chunk's raw bf16, mbits the quad's block maximum of |x| (bit pattern).
+template <int ELEM, int RND, bool GAMMA>
+__device__ __forceinline__ void mxnorm_chunk_out(const NormArgs& A, int64_t row, int d,
+                                                 const uint4& xb, uint32_t mbits, float inv,
+                                                 int lane) {
+  float v[8];
+  unpack8(xb, v);
+  float amax;
+  if (GAMMA) {
+    float g[8];
+    unpack8(load16(A.gamma + d), g);
+    uint32_t mp = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = v[j] * g[j];  // exact: a product of two bf16 values fits fp32
+      mp = max(mp, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+    }
+    // max |y| = RN(max |x*gamma| * inv): rounding is monotone
+    amax = __uint_as_float(quad_max_u32(mp)) * inv;
+  } else {
+    amax = __uint_as_float(mbits << 16) * inv;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
+  const uint32_t code = e8m0_code<ELEM>(amax);
+  const uint64_t n = (uint64_t)row * (uint64_t)A.D + (uint64_t)d;
+  encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
+  if ((lane & 3) == 0) A.scales[(uint64_t)row * (uint64_t)A.K + (uint64_t)(d >> 5)] = (uint8_t)code;
+}
+
+// Register-resident row: NC chunks of 512 elements held in VGPRs.
+template <int NC, int ELEM, int RND, bool GAMMA>
+__global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= A.T) return;
+  const uint16_t* xr = A.x + row * A.ldx;
+  const int dl = lane * 8;
+
+  uint4 raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    raw[c] = (c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
+
+  uint32_t mb[NC];
+  uint32_t rmax = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    mb[c] = quad_max_u32(absmax_bits8(raw[c]));
+    rmax = max(rmax, mb[c]);
+  }
+  rmax = max_over_quads(rmax);
+  const float inv = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, rmax, A.pmode, A.p, A.Kf);
+  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int d = c * kChunk + dl;
+    if (d < A.D) mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, raw[c], mb[c], inv, lane);
+  }
+}
+
+// LDS-staged row: each wavefront copies its row into its own LDS slice with
+// direct-to-LDS loads (no VGPR staging), then runs the same two halves
+// reading chunks back from LDS. The chunk loop is not unrolled, so rows up to
+// MXQ_MAX_D fit; a lane only ever reads back the 16 bytes it loaded.
+template <int ELEM, int RND, bool GAMMA>
+__global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nchunks) {
+  extern __shared__ uint4 lds_rows[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (row >= A.T) return;
+  const uint16_t* xr = A.x + row * A.ldx;
+  const int dl = lane * 8;
+  uint4* slice = lds_rows + (size_t)wave * nchunks * kWave;
+
+  for (int c = 0; c < nchunks; ++c) {
+    if (c * kChunk + dl < A.D)
+      __builtin_amdgcn_global_load_lds((const void*)(xr + c * kChunk + dl),
+                                       (lds_void*)(slice + c * kWave), 16, 0, 0);
+    else
+      slice[c * kWave + lane] = make_uint4(0, 0, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  auto mb = [&](int c) { return quad_max_u32(absmax_bits8(slice[c * kWave + lane])); };
+  uint32_t rmax = 0;
+  for (int c = 0; c < nchunks; ++c) rmax = max(rmax, mb(c));
+  rmax = max_over_quads(rmax);
+  const float inv = row_normaliser<0>(nchunks, mb, rmax, A.pmode, A.p, A.Kf);
+  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int d = c * kChunk + dl;
+    if (d < A.D) {
+      const uint4 xb = slice[c * kWave + lane];
+      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, xb, GAMMA ? 0u : mb(c), inv, lane);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ RMSNorm
+
+struct RmsArgs {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  uint16_t* y;
+  float* inv_out;
+  int64_t ldx;
+  int64_t T;
+  int D;
+  float Df;
+  float eps;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)a);  // round to nearest even
+  const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+template <bool GAMMA>
+__device__ __forceinline__ void rms_chunk_out(const RmsArgs& A, int64_t row, int d, const uint4& xb,
+                                              float inv) {
+  float v[8];
+  unpack8(xb, v);
+  if (GAMMA) {
+    float g[8];
+    unpack8(load16(A.gamma + d), g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * g[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
+  uint4 o;
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
+  o.z = pack_bf16x2(v[4], v[5]);
+  o.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(A.y + (uint64_t)row * (uint64_t)A.D + (uint64_t)d) = o;
+}
+
+__device__ __forceinline__ float sumsq8(const uint4& r, float s) {
+  float v[8];
+  unpack8(r, v);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = __builtin_fmaf(v[j], v[j], s);
+  return s;
+}
+
+// Row in registers (D <= NC * 512).
+template <int NC, bool GAMMA>
+__global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= A.T) return;
+  const uint16_t* xr = A.x + row * A.ldx;
+  const int dl = lane * 8;
+  uint4 raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    raw[c] = (c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) s = sumsq8(raw[c], s);
+  s = sum_over_wave(s);
+  const float inv = 1.0f / sqrtf(s / A.Df + A.eps);
+  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int d = c * kChunk + dl;
+    if (d < A.D) rms_chunk_out<GAMMA>(A, row, d, raw[c], inv);
+  }
+}
+
+// Wide rows: the second half reads x again (from cache or HBM).
+template <bool GAMMA>
+__global__ __launch_bounds__(kThreads) void rmsnorm_wide_kernel(RmsArgs A, int nchunks) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= A.T) return;
+  const uint16_t* xr = A.x + row * A.ldx;
+  const int dl = lane * 8;
+  float s = 0.0f;
+  for (int c = 0; c < nchunks; ++c)
+    if (c * kChunk + dl < A.D) s = sumsq8(load16(xr + c * kChunk + dl), s);
+  s = sum_over_wave(s);
+  const float inv = 1.0f / sqrtf(s / A.Df + A.eps);
+  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  for (int c = 0; c < nchunks; ++c) {
+    const int d = c * kChunk + dl;
+    if (d < A.D) rms_chunk_out<GAMMA>(A, row, d, load16(xr + d), inv);
+  }
+}
+
+// ------------------------------------------------------------------ MXCast
+
+struct CastArgs {
+  const uint16_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t ldx;
+  uint32_t total_chunks;  // T * chunks_per_row
+  uint32_t chunks_per_row;
+  int D;
+  int K;
+  SrStream rng;
+};
+
+template <int ELEM, int RND>
+__global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t g0 = (blockIdx.x * kRowsPerBlock + wave) * kCastChunksPerWave;
+  const int dl = lane * 8;
+  uint4 raw[kCastChunksPerWave];
+  uint32_t rows[kCastChunksPerWave];
+  int ds[kCastChunksPerWave];
+#pragma unroll
+  for (int u = 0; u < kCastChunksPerWave; ++u) {
+    const uint32_t g = g0 + u;
+    const uint32_t r = g / A.chunks_per_row;
+    rows[u] = r;
+    ds[u] = (int)(g - r * A.chunks_per_row) * kChunk + dl;
+    raw[u] = (g < A.total_chunks && ds[u] < A.D)
+                 ? load16(A.x + (int64_t)r * A.ldx + ds[u]) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kCastChunksPerWave; ++u) {
+    if (g0 + u < A.total_chunks && ds[u] < A.D) {
+      const uint32_t mbits = quad_max_u32(absmax_bits8(raw[u]));
+      const uint32_t code = e8m0_code<ELEM>(__uint_as_float(mbits << 16));
+      float v[8];
+      unpack8(raw[u], v);
+      const uint64_t n = (uint64_t)rows[u] * (uint64_t)A.D + (uint64_t)ds[u];
+      encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
+      if ((lane & 3) == 0)
+        A.scales[(uint64_t)rows[u] * (uint64_t)A.K + (uint64_t)(ds[u] >> 5)] = (uint8_t)code;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+#define MXQ_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP; \
+  } while (0)
+
+template <int NC, int ELEM, int RND, bool GAMMA>
+mxq_status launch_mxnorm_reg(const NormArgs& A, hipStream_t s) {
+  const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL((mxnorm_reg_kernel<NC, ELEM, RND, GAMMA>), dim3(grid), dim3(kThreads), 0, s, A);
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+template <int ELEM, int RND, bool GAMMA>
+mxq_status dispatch_mxnorm_reg(const NormArgs& A, int nc, hipStream_t s) {
+  switch (nc) {
+#define MXQ_CASE(N) \
+  case N:           \
+    return launch_mxnorm_reg<N, ELEM, RND, GAMMA>(A, s);
+    MXQ_CASE(1) MXQ_CASE(2) MXQ_CASE(3) MXQ_CASE(4) MXQ_CASE(5) MXQ_CASE(6) MXQ_CASE(7)
+    MXQ_CASE(8) MXQ_CASE(9) MXQ_CASE(10) MXQ_CASE(11) MXQ_CASE(12) MXQ_CASE(13) MXQ_CASE(14)
+    MXQ_CASE(15) MXQ_CASE(16)
+#undef MXQ_CASE
+    default:
+      return MXQ_ERR_UNSUPPORTED;
+  }
+}
+
+constexpr size_t kLdsPerBlockMax = 160 * 1024;  // gfx950 LDS per workgroup
+
+template <int ELEM, int RND, bool GAMMA>
+mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
+  const size_t per_row = (size_t)nc * kWave * sizeof(uint4);
+  int rows = (int)(kLdsPerBlockMax / per_row);
+  if (rows < 1) return MXQ_ERR_UNSUPPORTED;
+  if (rows > kRowsPerBlock) rows = kRowsPerBlock;
+  const size_t bytes = per_row * rows;
+  auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA>;
+  if (bytes > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes) != hipSuccess)
+    return MXQ_ERR_HIP;
+  const unsigned grid = (unsigned)((A.T + rows - 1) / rows);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * rows), bytes, s, A, nc);
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+template <int ELEM, int RND>
+mxq_status dispatch_mxnorm(const NormArgs& A, bool gamma, bool lds, int nc, hipStream_t s) {
+  if (lds)
+    return gamma ? launch_mxnorm_lds<ELEM, RND, true>(A, nc, s)
+                 : launch_mxnorm_lds<ELEM, RND, false>(A, nc, s);
+  return gamma ? dispatch_mxnorm_reg<ELEM, RND, true>(A, nc, s)
+               : dispatch_mxnorm_reg<ELEM, RND, false>(A, nc, s);
+}
+
+template <int NC, bool GAMMA>
+mxq_status launch_rms_reg(const RmsArgs& A, hipStream_t s) {
+  const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL((rmsnorm_reg_kernel<NC, GAMMA>), dim3(grid), dim3(kThreads), 0, s, A);
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+template <bool GAMMA>
+mxq_status dispatch_rms(const RmsArgs& A, int nc, hipStream_t s) {
+  switch (nc) {
+#define MXQ_CASE(N) \
+  case N:           \
+    return launch_rms_reg<N, GAMMA>(A, s);
+    MXQ_CASE(1) MXQ_CASE(2) MXQ_CASE(3) MXQ_CASE(4) MXQ_CASE(5) MXQ_CASE(6) MXQ_CASE(7)
+    MXQ_CASE(8) MXQ_CASE(9) MXQ_CASE(10) MXQ_CASE(11) MXQ_CASE(12) MXQ_CASE(13) MXQ_CASE(14)
+    MXQ_CASE(15) MXQ_CASE(16)
+#undef MXQ_CASE
+    default: {
+      const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
+      hipLaunchKernelGGL((rmsnorm_wide_kernel<GAMMA>), dim3(grid), dim3(kThreads), 0, s, A, nc);
+      MXQ_LAUNCH_CHECK();
+      return MXQ_OK;
+    }
+  }
+}
+
+template <int ELEM, int RND>
+mxq_status launch_cast(const CastArgs& A, hipStream_t s) {
+  const uint32_t per_block = kRowsPerBlock * kCastChunksPerWave;
+  const unsigned grid = (A.total_chunks + per_block - 1) / per_block;
+  hipLaunchKernelGGL((mxcast_kernel<ELEM, RND>), dim3(grid), dim3(kThreads), 0, s, A);
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+mxq_status dispatch_cast(const CastArgs& A, mxq_elem elem, mxq_round rnd, hipStream_t s) {
+  if (elem == MXQ_E4M3)
+    return rnd == MXQ_SR ? launch_cast<MXQ_E4M3, MXQ_SR>(A, s) : launch_cast<MXQ_E4M3, MXQ_RNE>(A, s);
+  return rnd == MXQ_SR ? launch_cast<MXQ_E2M1, MXQ_SR>(A, s) : launch_cast<MXQ_E2M1, MXQ_RNE>(A, s);
+}
+
+// ------------------------------------------------------------------ validation
+
+mxq_status check_common(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
+                        mxq_round rnd, const mxq_rng* rng, const uint8_t* codes,
+                        const uint8_t* scales) {
+  if (T < 0 || D <= 0 || D % 32 != 0 || ldx < D) return MXQ_ERR_SHAPE;
+  if (elem != MXQ_E4M3 && elem != MXQ_E2M1) return MXQ_ERR_ARG;
+  if (rnd != MXQ_RNE && rnd != MXQ_SR) return MXQ_ERR_ARG;
+  if (rnd == MXQ_SR && rng == nullptr) return MXQ_ERR_ARG;
+  if (T == 0) return MXQ_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(codes, 16)) return MXQ_ERR_ALIGN;
+  if ((uint64_t)T * (uint64_t)D >= (1ull << 40)) return MXQ_ERR_UNSUPPORTED;
+  return MXQ_OK;
+}
+
+SrStream make_stream(const mxq_rng* rng) {
+  SrStream s{0, 0, 0, 0};
+  if (rng) {
+    s.k0 = (uint32_t)rng->seed;
+    s.k1 = (uint32_t)(rng->seed >> 32);
+    s.o0 = (uint32_t)rng->offset;
+    s.o1 = (uint32_t)(rng->offset >> 32);
+  }
+  return s;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                      int64_t D, float p, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
+                      uint32_t flags, uint8_t* codes, uint8_t* scales, float* inv_norm,
+                      void* stream) {
+  mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (!(p > 0.0f)) return MXQ_ERR_ARG;  // also rejects NaN
+  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  if ((flags & MXQ_FLAG_FORCE_REG) && (flags & MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
+  if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
+  if (T == 0) return MXQ_OK;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
+  if (inv_norm != nullptr && !aligned(inv_norm, 4)) return MXQ_ERR_ALIGN;
+
+  NormArgs A;
+  A.x = x;
+  A.gamma = gamma;
+  A.codes = codes;
+  A.scales = scales;
+  A.inv_out = inv_norm;
+  A.ldx = ldx;
+  A.T = T;
+  A.D = (int)D;
+  A.K = (int)(D / 32);
+  A.Kf = (float)(D / 32);
+  A.p = p;
+  A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
+  A.rng = make_stream(rng);
+  const int nc = (int)((D + kChunk - 1) / kChunk);
+  const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
+  hipStream_t s = (hipStream_t)stream;
+  const bool g = gamma != nullptr;
+  if (elem == MXQ_E4M3)
+    return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E4M3, MXQ_SR>(A, g, lds, nc, s)
+                         : dispatch_mxnorm<MXQ_E4M3, MXQ_RNE>(A, g, lds, nc, s);
+  return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E2M1, MXQ_SR>(A, g, lds, nc, s)
+                       : dispatch_mxnorm<MXQ_E2M1, MXQ_RNE>(A, g, lds, nc, s);
+}
+
+mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                              int64_t T, int64_t D, float eps, mxq_elem elem, mxq_round rnd,
+                              const mxq_rng* rng, uint16_t* y_workspace, uint8_t* codes,
+                              uint8_t* scales, float* inv_rms, void* stream) {
+  mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (!(eps >= 0.0f) || isinf(eps)) return MXQ_ERR_ARG;
+  if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
+  if (T == 0) return MXQ_OK;
+  if (y_workspace == nullptr) return MXQ_ERR_NULL;
+  if (!aligned(y_workspace, 16)) return MXQ_ERR_ALIGN;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
+  if (inv_rms != nullptr && !aligned(inv_rms, 4)) return MXQ_ERR_ALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  RmsArgs R;
+  R.x = x;
+  R.gamma = gamma;
+  R.y = y_workspace;
+  R.inv_out = inv_rms;
+  R.ldx = ldx;
+  R.T = T;
+  R.D = (int)D;
+  R.Df = (float)D;
+  R.eps = eps;
+  const int nc = (int)((D + kChunk - 1) / kChunk);
+  st = gamma ? dispatch_rms<true>(R, nc, s) : dispatch_rms<false>(R, nc, s);
+  if (st != MXQ_OK) return st;
+
+  CastArgs C;
+  C.x = y_workspace;
+  C.codes = codes;
+  C.scales = scales;
+  C.ldx = D;
+  C.chunks_per_row = (uint32_t)nc;
+  C.total_chunks = (uint32_t)(T * nc);
+  C.D = (int)D;
+  C.K = (int)(D / 32);
+  C.rng = make_stream(rng);
+  return dispatch_cast(C, elem, rnd, s);
+}
+
+mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
+                      mxq_round rnd, const mxq_rng* rng, uint8_t* codes, uint8_t* scales,
+                      void* stream) {
+  mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (T == 0) return MXQ_OK;
+  const uint64_t nc = (uint64_t)((D + kChunk - 1) / kChunk);
+  if ((uint64_t)T * nc >= (1ull << 32) - kThreads) return MXQ_ERR_UNSUPPORTED;
+  CastArgs C;
+  C.x = x;
+  C.codes = codes;
+  C.scales = scales;
+  C.ldx = ldx;
+  C.chunks_per_row = (uint32_t)nc;
+  C.total_chunks = (uint32_t)(T * nc);
+  C.D = (int)D;
+  C.K = (int)(D / 32);
+  C.rng = make_stream(rng);
+  return dispatch_cast(C, elem, rnd, (hipStream_t)stream);
+}
+
+const char* mxq_strerror(mxq_status status) {
+  switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "a required pointer is NULL";
+    case MXQ_ERR_SHAPE: return "bad shape: need T >= 0, D > 0, D % 32 == 0, ldx >= D";
+    case MXQ_ERR_ALIGN: return "misaligned pointer or row stride (16-byte rows and buffers)";
+    case MXQ_ERR_ARG: return "bad argument (p, eps, element format, rounding, flags or rng)";
+    case MXQ_ERR_UNSUPPORTED: return "unsupported size for this path";
+    case MXQ_ERR_HIP: return "HIP runtime refused the kernel launch";
+  }
+  return "unknown status";
+}
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+}  // extern "C"

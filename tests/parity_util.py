@@ -1,0 +1,95 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the oracle).
+
+The tolerance for the normalising ops in reference mode: the per-row
+normaliser within 1e-5 relative; dequantised outputs equal except on at most
+0.1% of the elements, each of those within one element ulp at the larger of
+the two block scales (a block scale can legitimately flip at a power-of-two
+boundary when the fp32 and fp64 normalisers differ in the last bits).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+NORM_RTOL = 1e-5
+MAX_DIFF_FRACTION = 1e-3
+
+
+def table(elem):
+    return oracle.decode_table(elem)
+
+
+def unpack_e2m1(packed):
+    packed = np.asarray(packed)
+    return np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(packed.shape[0], -1)
+
+
+def unpacked(codes, elem):
+    return unpack_e2m1(codes) if elem == "e2m1" else np.asarray(codes)
+
+
+def ulp(u, elem):
+    """Spacing of the element grid at |u| (u in element units)."""
+    a = np.abs(u)
+    emin, mbits = (-6, 3) if elem == "e4m3" else (0, 1)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(np.where(a > 0, e, emin), emin)
+    return np.ldexp(1.0, (e - mbits).astype(np.int64))
+
+
+def compare_reference(codes_g, scales_g, codes_r, scales_r, elem, what=""):
+    """Tolerance check against mode (R). Returns the number of differing elements."""
+    cg, cr = unpacked(codes_g, elem), unpacked(codes_r, elem)
+    sg, sr = np.asarray(scales_g).astype(np.int64), np.asarray(scales_r).astype(np.int64)
+    assert cg.shape == cr.shape and sg.shape == sr.shape
+    nan_g, nan_r = sg == 255, sr == 255
+    assert np.array_equal(nan_g, nan_r), f"{what}: NaN blocks differ"
+    tab = table(elem)
+    smax = np.maximum(sg, sr)
+    smax_e = np.repeat(smax, 32, axis=1)
+    ug = tab[cg] * np.ldexp(1.0, np.repeat(sg, 32, axis=1) - smax_e)
+    ur = tab[cr] * np.ldexp(1.0, np.repeat(sr, 32, axis=1) - smax_e)
+    live = ~np.repeat(nan_g, 32, axis=1)
+    diff = live & (ug != ur)
+    n = int(diff.sum())
+    if n:
+        d = np.abs(ug[diff] - ur[diff])
+        lim = ulp(np.maximum(np.abs(ug[diff]), np.abs(ur[diff])), elem)
+        worst = float((d / lim).max())
+        assert worst <= 1.0, f"{what}: {n} elements differ, worst {worst} ulp"
+    # at most 0.1% of the elements, read as ceil(0.001 * N): a tensor of a few
+    # hundred elements may show one rounding flip
+    assert n <= math.ceil(MAX_DIFF_FRACTION * cg.size), f"{what}: {n} of {cg.size} elements differ"
+    return n
+
+
+def check_normaliser(inv_g, inv_r, what=""):
+    inv_g = np.asarray(inv_g, np.float64)
+    inv_r = np.asarray(inv_r, np.float64)
+    assert np.array_equal(np.isnan(inv_g), np.isnan(inv_r)), f"{what}: NaN rows differ"
+    ok = ~np.isnan(inv_r)
+    assert np.array_equal(inv_g[ok] == 0, inv_r[ok] == 0), f"{what}: zero rows differ"
+    nz = ok & (inv_r != 0)
+    if nz.any():
+        rel = np.abs(inv_g[nz] - inv_r[nz]) / np.abs(inv_r[nz])
+        assert rel.max() <= NORM_RTOL, f"{what}: normaliser off by {rel.max():.3g} relative"
+
+
+def assert_bits(a, b, what=""):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, what
+    bad = np.argwhere(a != b)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:3].tolist()}: " \
+                          f"{a[tuple(bad[0])]} vs {b[tuple(bad[0])]}"
+
+
+def host(t):
+    return None if t is None else t.detach().cpu()
+
+
+def np_(t):
+    return t.detach().cpu().numpy()

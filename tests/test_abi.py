@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mxq.h declares, and rejects bad arguments before any HIP call.
+
+Every call here fails validation, so no kernel is ever launched (fake device
+pointers are never dereferenced).
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import norm_mx_quantisation_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+A16 = 0x10000       # a 16-byte aligned fake device address (never dereferenced)
+A8 = A16 + 8        # 8-byte aligned, not 16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(mxq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.check_output(["nm", "-D", "--defined-only", mxq.LIB_PATH], text=True)
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for fn in declared_functions():
+        assert fn in names, fn
+        assert hasattr(mxq.lib(), fn)
+
+
+def test_abi_version_and_messages():
+    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 1
+    for st in range(7):
+        assert isinstance(mxq.mxq_strerror(st), str) and mxq.mxq_strerror(st)
+    assert mxq.mxq_strerror(99) == "unknown status"
+
+
+def norm(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, T=8, D=4096, p=2.0, elem=0, rnd=0, rng=None, flags=0,
+             codes=A16, scales=A16, inv_norm=None, stream=None)
+    a.update(kw)
+    return mxq.mxnorm_fwd(a["x"], a["ldx"], a["gamma"], a["T"], a["D"], a["p"], a["elem"], a["rnd"],
+                          a["rng"], a["flags"], a["codes"], a["scales"], a["inv_norm"], a["stream"])
+
+
+def rms(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, T=8, D=4096, eps=1e-5, elem=0, rnd=0, rng=None,
+             y=A16, codes=A16, scales=A16, inv=None, stream=None)
+    a.update(kw)
+    return mxq.rmsnorm_mxcast_fwd(a["x"], a["ldx"], a["gamma"], a["T"], a["D"], a["eps"], a["elem"],
+                                  a["rnd"], a["rng"], a["y"], a["codes"], a["scales"], a["inv"],
+                                  a["stream"])
+
+
+def cast(**kw):
+    a = dict(x=A16, ldx=4096, T=8, D=4096, elem=0, rnd=0, rng=None, codes=A16, scales=A16, stream=None)
+    a.update(kw)
+    return mxq.mxcast_fwd(a["x"], a["ldx"], a["T"], a["D"], a["elem"], a["rnd"], a["rng"],
+                          a["codes"], a["scales"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [norm, rms, cast])
+def test_shape_errors(call):
+    assert call(D=0) == mxq.MXQ_ERR_SHAPE
+    assert call(D=-32) == mxq.MXQ_ERR_SHAPE
+    assert call(D=4000 + 16) == mxq.MXQ_ERR_SHAPE       # not a multiple of 32
+    assert call(T=-1) == mxq.MXQ_ERR_SHAPE
+    assert call(ldx=2048) == mxq.MXQ_ERR_SHAPE          # ldx < D
+
+
+@pytest.mark.parametrize("call", [norm, rms, cast])
+def test_null_and_alignment_errors(call):
+    assert call(x=None) == mxq.MXQ_ERR_NULL
+    assert call(codes=None) == mxq.MXQ_ERR_NULL
+    assert call(scales=None) == mxq.MXQ_ERR_NULL
+    assert call(x=A8) == mxq.MXQ_ERR_ALIGN
+    assert call(codes=A8) == mxq.MXQ_ERR_ALIGN
+    assert call(ldx=4100) == mxq.MXQ_ERR_ALIGN          # rows not 16-byte aligned
+
+
+@pytest.mark.parametrize("call", [norm, rms, cast])
+def test_format_rounding_rng_errors(call):
+    assert call(elem=2) == mxq.MXQ_ERR_ARG
+    assert call(rnd=5) == mxq.MXQ_ERR_ARG
+    assert call(rnd=1, rng=None) == mxq.MXQ_ERR_ARG     # SR needs a stream
+
+
+def test_mxnorm_argument_errors():
+    assert norm(p=0.0) == mxq.MXQ_ERR_ARG
+    assert norm(p=-1.0) == mxq.MXQ_ERR_ARG
+    assert norm(p=float("nan")) == mxq.MXQ_ERR_ARG
+    assert norm(flags=3) == mxq.MXQ_ERR_ARG
+    assert norm(flags=8) == mxq.MXQ_ERR_ARG
+    assert norm(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
+    assert norm(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
+    assert norm(gamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert norm(inv_norm=A16 + 2) == mxq.MXQ_ERR_ALIGN
+
+
+def test_rmsnorm_argument_errors():
+    assert rms(eps=-1e-6) == mxq.MXQ_ERR_ARG
+    assert rms(eps=float("nan")) == mxq.MXQ_ERR_ARG
+    assert rms(eps=float("inf")) == mxq.MXQ_ERR_ARG
+    assert rms(y=None) == mxq.MXQ_ERR_NULL
+    assert rms(y=A8) == mxq.MXQ_ERR_ALIGN
+    assert rms(gamma=A8) == mxq.MXQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("call", [norm, rms, cast])
+def test_empty_input_is_a_no_op(call):
+    # T == 0 returns before any pointer is read or kernel launched
+    assert call(T=0, x=None, codes=None, scales=None) == mxq.MXQ_OK
+
+
+def test_torch_helpers_refuse_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mxq.mxnorm(x)
+    with pytest.raises(TypeError):
+        mxq.mxcast(x.float())
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # the package and its sources never import or load the oracle
+    pkg = os.path.join(ROOT, "norm_mx_quantisation_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "liboracle" not in text, f
