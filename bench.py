@@ -1,0 +1,231 @@
+"""Benchmark: fused MXNorm + MXFP8 cast on the Llama-3-8B pre-attention shape.
+
+One step = one call of the fused hot path (mxnorm_fwd, p = 2, gamma given,
+E4M3 + E8M0) over one [T=8192, D=4096] bf16 activation already resident in
+HBM. Ten input/output buffer sets (~1 GB) are used round-robin so the 256 MB
+MALL cannot serve a step from cache. Prints one JSON line.
+
+The same line carries, for context: the p = 1 variant, the two-pass
+RMSNorm -> MXCast comparison path (each timed the same way), a plain
+device-to-device copy of the same byte count, the roofline of the fused
+kernel (per-launch HIP-event durations on the launch stream) and the CPU
+oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "llama3_8b_preattn"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE = 10
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_mxnorm_fwd_llama3_8b.json")
+KERNEL_SRC = os.path.join(ROOT, "norm_mx_quantisation_amd", "csrc", "mxq.hip")
+
+
+def fused_bytes(T, D, elem="e4m3"):
+    """Algorithmic bytes of one fused call: read x (2D/row), write codes and scales."""
+    code = D if elem == "e4m3" else D // 2
+    return T * (2 * D + code + D // 32)
+
+
+def two_pass_bytes(T, D):
+    """RMSNorm reads x and writes bf16 y; MXCast reads y, writes codes and scales."""
+    return T * (2 * D + 2 * D + 2 * D + D + D // 32)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """Per-launch HBM bytes from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_launches(torch, launch, steps, warmup):
+    """Warm up, then time `steps` launches: whole-region wall time between two
+    synchronisations, plus per-launch HIP events recorded on the launch stream."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
+    return {
+        "wall_s": wall,
+        "s_per_step": wall / steps,
+        "kernel_mean_s": sum(per) / len(per),
+        "kernel_median_s": per[len(per) // 2],
+        "kernel_p10_s": per[len(per) // 10],
+        "kernel_p90_s": per[(9 * len(per)) // 10],
+    }
+
+
+def cpu_baseline(x_cpu, g_cpu, T, D, min_seconds=10.0):
+    """The oracle (reference mode, p = 2, E4M3) on the workload's rows, repeated
+    until at least min_seconds of CPU work; all host threads up to 16."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.lib()
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.mxnorm(x_cpu, g_cpu, 2.0, "e4m3", "rne", threads=threads)
+        rows += x_cpu.shape[0]
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    rows_per_s = rows / el
+    return {
+        "value": rows_per_s * fused_bytes(1, D) / 1e9,
+        "unit": "GB/s",
+        "rows_per_s": rows_per_s,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows} rows ({rows // x_cpu.shape[0]} passes over the {x_cpu.shape[0]} x {D} "
+                  f"workload rows), reference mode, p=2, E4M3, {el:.1f} s",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+              "(rows shard over GPUs with no exchange); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import norm_mx_quantisation_amd as mxq
+    from norm_mx_quantisation_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mxq.lib()
+    w = workloads.WORKLOADS[WORKLOAD]
+    T, D = w.T, w.D
+    dev = torch.device("cuda:0")
+    x0, g = workloads.make_inputs(WORKLOAD, device=dev)
+
+    xs = [x0.clone() for _ in range(ROTATE)]
+    outs = [(torch.empty((T, D), dtype=torch.uint8, device=dev),
+             torch.empty((T, D // 32), dtype=torch.uint8, device=dev),
+             torch.empty((T,), dtype=torch.float32, device=dev)) for _ in range(ROTATE)]
+    ys = [torch.empty((T, D), dtype=torch.bfloat16, device=dev) for _ in range(ROTATE)]
+
+    def fused(p):
+        return lambda i: mxq.mxnorm(xs[i % ROTATE], g, p, "e4m3", "rne", out=outs[i % ROTATE])
+
+    def two_pass(i):
+        k = i % ROTATE
+        mxq.rmsnorm_mxcast(xs[k], g, 1e-5, "e4m3", "rne", out=outs[k], y=ys[k])
+
+    def two_pass_hot(i):
+        mxq.rmsnorm_mxcast(xs[0], g, 1e-5, "e4m3", "rne", out=outs[0], y=ys[0])
+
+    copy_n = fused_bytes(T, D) // 2
+    src = [torch.empty(copy_n, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
+    dst = [torch.empty(copy_n, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
+
+    def copy(i):
+        dst[i % ROTATE].copy_(src[i % ROTATE])
+
+    K, W = args.steps, args.warmup
+    main_t = time_launches(torch, fused(2.0), K, W)        # the headline: p = 2
+    p1_t = time_launches(torch, fused(1.0), K, W)
+    tp_t = time_launches(torch, two_pass, K, W)
+    tp_hot = time_launches(torch, two_pass_hot, K, W)
+    cp_t = time_launches(torch, copy, K, W)
+
+    nbytes = fused_bytes(T, D)
+    value = nbytes / main_t["s_per_step"] / 1e9
+    achieved = nbytes / main_t["kernel_mean_s"] / 1e9
+    traffic = measured_traffic()
+    line = {
+        "metric": "fused MXNorm+MXFP8 cast GB/s & rows/s at T=8192,D=4096; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(main_t["s_per_step"] * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "T": T, "D": D, "p": 2.0, "elem": "e4m3",
+                   "rounding": "rne", "gamma": True, "block": 32,
+                   "algorithmic_bytes_per_step": nbytes, "rotating_buffer_sets": ROTATE},
+        "rows_per_s": round(T / main_t["s_per_step"], 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "mxnorm_reg_kernel<8, E4M3, RNE, gamma>",
+            "kernel_mean_us": round(main_t["kernel_mean_s"] * 1e6, 3),
+            "kernel_median_us": round(main_t["kernel_median_s"] * 1e6, 3),
+            "kernel_p10_us": round(main_t["kernel_p10_s"] * 1e6, 3),
+            "kernel_p90_us": round(main_t["kernel_p90_s"] * 1e6, 3),
+            "bytes_per_launch": nbytes,
+        },
+        "comparison": {
+            "fused_p1": {"kernel_mean_us": round(p1_t["kernel_mean_s"] * 1e6, 3),
+                         "GB/s": round(nbytes / p1_t["s_per_step"] / 1e9, 2)},
+            "two_pass": {
+                "ms_per_step": round(tp_t["s_per_step"] * 1e3, 6),
+                "kernels_mean_us": round(tp_t["kernel_mean_s"] * 1e6, 3),
+                "GB/s_own_bytes": round(two_pass_bytes(T, D) / tp_t["s_per_step"] / 1e9, 2),
+                "fused_speedup": round(tp_t["s_per_step"] / main_t["s_per_step"], 3),
+                "hot_no_rotation_kernels_mean_us": round(tp_hot["kernel_mean_s"] * 1e6, 3),
+            },
+            "d2d_copy_same_bytes": {"kernel_mean_us": round(cp_t["kernel_mean_s"] * 1e6, 3),
+                                    "GB/s": round(2 * copy_n / cp_t["kernel_mean_s"] / 1e9, 2)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x0.cpu(), g.cpu(), T, D, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

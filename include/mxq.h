@@ -99,7 +99,7 @@ enum {
 
 /* Largest D of the register-resident MXNorm path and of any path. */
 #define MXQ_MAX_D_REG 8192
-#define MXQ_MAX_D 65536
+#define MXQ_MAX_D 32768
 
 /*
  * Fused MXNorm -> MX cast (MXNorm page, §2.1 and §2.3).

@@ -24,7 +24,7 @@ MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_ARG, MXQ_ERR_UNSUPPO
 MXQ_E4M3, MXQ_E2M1 = 0, 1
 MXQ_RNE, MXQ_SR = 0, 1
 MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS = 1, 2
-MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 65536
+MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
 ABI_VERSION = 1
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "mxcast_fwd", "mxq_strerror", "mxq_abi_version")

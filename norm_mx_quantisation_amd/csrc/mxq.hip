@@ -323,14 +323,14 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 // chunk's raw bf16, mbits the quad's block maximum of |x| (bit pattern).
 template <int ELEM, int RND, bool GAMMA>
 __device__ __forceinline__ void mxnorm_chunk_out(const NormArgs& A, int64_t row, int d,
-                                                 const uint4& xb, uint32_t mbits, float inv,
-                                                 int lane) {
+                                                 const uint4& xb, const uint4& gb, uint32_t mbits,
+                                                 float inv, int lane) {
   float v[8];
   unpack8(xb, v);
   float amax;
   if (GAMMA) {
     float g[8];
-    unpack8(load16(A.gamma + d), g);
+    unpack8(gb, g);
     uint32_t mp = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -350,19 +350,34 @@ __device__ __forceinline__ void mxnorm_chunk_out(const NormArgs& A, int64_t row,
   if ((lane & 3) == 0) A.scales[(uint64_t)row * (uint64_t)A.K + (uint64_t)(d >> 5)] = (uint8_t)code;
 }
 
-// Register-resident row: NC chunks of 512 elements held in VGPRs.
+// gamma [D] copied into LDS by the whole workgroup (once per workgroup; the
+// caller's barrier makes it visible). Slot c * 64 + lane holds the 8 gains of
+// chunk c, lane `lane`.
+__device__ __forceinline__ void stage_gamma(const uint16_t* gamma, int D, int nchunks, uint4* g_lds) {
+  for (int i = threadIdx.x; i < nchunks * kWave; i += blockDim.x)
+    g_lds[i] = (i * 8 < D) ? load16(gamma + i * 8) : make_uint4(0, 0, 0, 0);
+}
+
+// Register-resident row: NC chunks of 512 elements held in VGPRs. The
+// workgroup's rows share one LDS copy of gamma.
 template <int NC, int ELEM, int RND, bool GAMMA>
 __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
+  __shared__ uint4 g_lds[GAMMA ? NC * kWave : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= A.T) return;
-  const uint16_t* xr = A.x + row * A.ldx;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : 0) * A.ldx;
   const int dl = lane * 8;
 
   uint4 raw[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
-    raw[c] = (c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
+    raw[c] = (live && c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
+  if (GAMMA) {
+    stage_gamma(A.gamma, A.D, NC, g_lds);  // overlaps the row loads in flight
+    __syncthreads();
+  }
+  if (!live) return;
 
   uint32_t mb[NC];
   uint32_t rmax = 0;
@@ -378,7 +393,9 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int d = c * kChunk + dl;
-    if (d < A.D) mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, raw[c], mb[c], inv, lane);
+    if (d < A.D)
+      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, raw[c], GAMMA ? g_lds[c * kWave + lane] : raw[c],
+                                         mb[c], inv, lane);
   }
 }
 
@@ -388,22 +405,31 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
 // MXQ_MAX_D fit; a lane only ever reads back the 16 bytes it loaded.
 template <int ELEM, int RND, bool GAMMA>
 __global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nchunks) {
-  extern __shared__ uint4 lds_rows[];
+  extern __shared__ uint4 lds_rows[];  // [rows][nchunks * 64] then gamma [nchunks * 64]
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  if (row >= A.T) return;
-  const uint16_t* xr = A.x + row * A.ldx;
+  const int rows = blockDim.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * rows + wave;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : 0) * A.ldx;
   const int dl = lane * 8;
   uint4* slice = lds_rows + (size_t)wave * nchunks * kWave;
+  uint4* g_lds = lds_rows + (size_t)rows * nchunks * kWave;
 
-  for (int c = 0; c < nchunks; ++c) {
-    if (c * kChunk + dl < A.D)
-      __builtin_amdgcn_global_load_lds((const void*)(xr + c * kChunk + dl),
-                                       (lds_void*)(slice + c * kWave), 16, 0, 0);
-    else
-      slice[c * kWave + lane] = make_uint4(0, 0, 0, 0);
+  if (live) {
+    for (int c = 0; c < nchunks; ++c) {
+      if (c * kChunk + dl < A.D)
+        __builtin_amdgcn_global_load_lds((const void*)(xr + c * kChunk + dl),
+                                         (lds_void*)(slice + c * kWave), 16, 0, 0);
+      else
+        slice[c * kWave + lane] = make_uint4(0, 0, 0, 0);
+    }
   }
+  if (GAMMA) {
+    stage_gamma(A.gamma, A.D, nchunks, g_lds);
+    __syncthreads();
+  }
+  if (!live) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   auto mb = [&](int c) { return quad_max_u32(absmax_bits8(slice[c * kWave + lane])); };
@@ -417,7 +443,8 @@ __global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nc
     const int d = c * kChunk + dl;
     if (d < A.D) {
       const uint4 xb = slice[c * kWave + lane];
-      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, xb, GAMMA ? 0u : mb(c), inv, lane);
+      const uint4 gb = GAMMA ? g_lds[c * kWave + lane] : xb;
+      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, xb, gb, GAMMA ? 0u : mb(c), inv, lane);
     }
   }
 }
@@ -600,10 +627,11 @@ constexpr size_t kLdsPerBlockMax = 160 * 1024;  // gfx950 LDS per workgroup
 template <int ELEM, int RND, bool GAMMA>
 mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
   const size_t per_row = (size_t)nc * kWave * sizeof(uint4);
-  int rows = (int)(kLdsPerBlockMax / per_row);
-  if (rows < 1) return MXQ_ERR_UNSUPPORTED;
+  const size_t g_bytes = GAMMA ? per_row : 0;
+  if (per_row + g_bytes > kLdsPerBlockMax) return MXQ_ERR_UNSUPPORTED;
+  int rows = (int)((kLdsPerBlockMax - g_bytes) / per_row);
   if (rows > kRowsPerBlock) rows = kRowsPerBlock;
-  const size_t bytes = per_row * rows;
+  const size_t bytes = per_row * rows + g_bytes;
   auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA>;
   if (bytes > 64 * 1024 &&
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
