@@ -277,8 +277,40 @@ __device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], uint32_t c
   return q;
 }
 
-// Encode and store 8 elements at element offset n_row + d of a contiguous
-// [T, D] code tensor (n_row = t * D).
+// ------------------------------------------------------------------ memory
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// The activation is read exactly once and the codes are written once: both
+// go through non-temporal accesses.
+__device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Chunk c of a row, 16 bytes per lane. A lane whose 8 elements lie past the
+// row end reads the row's last 16 bytes instead, so every load is
+// unconditional and in bounds (a predicated load would make the compiler wait
+// for earlier loads); callers mask such lanes where the data is used.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int c, int dl, int D) {
+  return load16_stream(xr + min(c * kChunk + dl, D - 8));
+}
+
+__device__ __forceinline__ void store8_stream(uint8_t* p, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
+__device__ __forceinline__ void store4_stream(uint8_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
+// Encode and store 8 elements at element offset n of a contiguous code tensor.
 template <int ELEM, int RND>
 __device__ __forceinline__ void encode_store8(uint8_t* codes, uint64_t n, const float y[8],
                                               uint32_t code, const SrStream& rng) {
@@ -286,15 +318,40 @@ __device__ __forceinline__ void encode_store8(uint8_t* codes, uint64_t n, const 
     uint32_t r[8];
     rng.words8(n, r);
     if (ELEM == MXQ_E4M3)
-      *reinterpret_cast<uint2*>(codes + n) = encode8_e4m3_sr(y, code, r);
+      store8_stream(codes + n, encode8_e4m3_sr(y, code, r));
     else
-      *reinterpret_cast<uint32_t*>(codes + (n >> 1)) = encode8_e2m1_sr(y, code, r);
+      store4_stream(codes + (n >> 1), encode8_e2m1_sr(y, code, r));
   } else {
     if (ELEM == MXQ_E4M3)
-      *reinterpret_cast<uint2*>(codes + n) = encode8_e4m3_rne(y, code);
+      store8_stream(codes + n, encode8_e4m3_rne(y, code));
     else
-      *reinterpret_cast<uint32_t*>(codes + (n >> 1)) = encode8_e2m1_rne(y, code);
+      store4_stream(codes + (n >> 1), encode8_e2m1_rne(y, code));
   }
+}
+
+// Make one lane's LDS writes visible to the other lanes of its wavefront.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Scale bytes are gathered per wavefront in LDS (one byte per quad and chunk)
+// and leave in dword stores, one per lane, instead of one byte store per
+// block. vec: dst is 4-byte aligned and nbytes % 4 == 0; else bytes.
+__device__ __forceinline__ void flush_scales(const uint32_t* sc, uint8_t* dst, int nbytes, bool vec,
+                                             int lane) {
+  wave_sync_lds();
+  if (vec) {
+    for (int j = lane; j * 4 < nbytes; j += kWave) reinterpret_cast<uint32_t*>(dst)[j] = sc[j];
+  } else {
+    const uint8_t* b = reinterpret_cast<const uint8_t*>(sc);
+    for (int j = lane; j < nbytes; j += kWave) dst[j] = b[j];
+  }
+}
+
+__device__ __forceinline__ void put_scale(uint32_t* sc, int idx, uint32_t code) {
+  reinterpret_cast<uint8_t*>(sc)[idx] = (uint8_t)code;
 }
 
 // ------------------------------------------------------------------ MXNorm
@@ -312,110 +369,216 @@ struct NormArgs {
   float Kf;
   float p;
   int pmode;
+  int sc_vec;  // scales rows can be written in dwords
   SrStream rng;
 };
 
-__device__ __forceinline__ uint4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+// How the block maximum of |x * gamma| is taken:
+//   G_NONE  no gamma: the block maximum of |x| is reused (rounding is monotone);
+//   G_GAIN  gains: fp32 max with abs modifiers over the products. A NaN
+//           product can only come from a non-finite gain (a non-finite x
+//           already makes the row's normaliser NaN), and the staging of the
+//           gains turns every lane-group of 8 gains holding a NaN or Inf into
+//           8 NaNs, so that group's products are all NaN, the fp32 max is NaN
+//           and the block is flagged non-finite, as it must be.
+enum GMode { G_NONE = 0, G_GAIN = 1 };
+
+// First half of a chunk, needing no normaliser: v = x * gamma (exact: two
+// bf16 factors) and the quad's block maximum of |v| as a bit pattern (for
+// G_NONE, v = x and the maximum is the block maximum of |x|, mbits).
+template <int GM>
+__device__ __forceinline__ uint32_t chunk_products(const uint4& xb, const float g[8], uint32_t mbits,
+                                                   float v[8]) {
+  unpack8(xb, v);
+  if (GM == G_NONE) return mbits << 16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * g[j];
+  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  m = fmaxf(fmaxf(m, fabsf(v[3])), fabsf(v[4]));
+  m = fmaxf(fmaxf(m, fabsf(v[5])), fabsf(v[6]));
+  m = fmaxf(m, fabsf(v[7]));
+  // integer max of non-negative floats: NaN bits exceed every other value
+  return quad_max_u32(__float_as_uint(m));
 }
 
-// Second half of a row: normalise, scale, cast and store one chunk. xb is the
-// chunk's raw bf16, mbits the quad's block maximum of |x| (bit pattern).
-template <int ELEM, int RND, bool GAMMA>
-__device__ __forceinline__ void mxnorm_chunk_out(const NormArgs& A, int64_t row, int d,
-                                                 const uint4& xb, const uint4& gb, uint32_t mbits,
-                                                 float inv, int lane) {
-  float v[8];
-  unpack8(xb, v);
-  float amax;
-  if (GAMMA) {
-    float g[8];
-    unpack8(gb, g);
-    uint32_t mp = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = v[j] * g[j];  // exact: a product of two bf16 values fits fp32
-      mp = max(mp, __float_as_uint(v[j]) & 0x7FFFFFFFu);
-    }
-    // max |y| = RN(max |x*gamma| * inv): rounding is monotone
-    amax = __uint_as_float(quad_max_u32(mp)) * inv;
-  } else {
-    amax = __uint_as_float(mbits << 16) * inv;
-  }
+// Second half: y = RN(v * inv), E8M0 code from max |y| = RN(max |v| * inv)
+// (rounding is monotone), codes stored. Returns the code of the lane's block.
+template <int ELEM, int RND>
+__device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint64_t n, float v[8],
+                                                 uint32_t vmax_bits, float inv) {
+  const float amax = __uint_as_float(vmax_bits) * inv;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
   const uint32_t code = e8m0_code<ELEM>(amax);
-  const uint64_t n = (uint64_t)row * (uint64_t)A.D + (uint64_t)d;
   encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
-  if ((lane & 3) == 0) A.scales[(uint64_t)row * (uint64_t)A.K + (uint64_t)(d >> 5)] = (uint8_t)code;
+  return code;
 }
 
-// gamma [D] copied into LDS by the whole workgroup (once per workgroup; the
-// caller's barrier makes it visible). Slot c * 64 + lane holds the 8 gains of
-// chunk c, lane `lane`.
-__device__ __forceinline__ void stage_gamma(const uint16_t* gamma, int D, int nchunks, uint4* g_lds) {
-  for (int i = threadIdx.x; i < nchunks * kWave; i += blockDim.x)
-    g_lds[i] = (i * 8 < D) ? load16(gamma + i * 8) : make_uint4(0, 0, 0, 0);
+// Both halves of one chunk.
+template <int ELEM, int RND, int GM>
+__device__ __forceinline__ uint32_t mxnorm_chunk(const NormArgs& A, uint64_t n, const uint4& xb,
+                                                 const float g[8], uint32_t mbits, float inv) {
+  float v[8];
+  const uint32_t vm = chunk_products<GM>(xb, g, mbits, v);
+  return chunk_finish<ELEM, RND>(A, n, v, vm, inv);
 }
 
-// Register-resident row: NC chunks of 512 elements held in VGPRs. The
-// workgroup's rows share one LDS copy of gamma.
-template <int NC, int ELEM, int RND, bool GAMMA>
-__global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
-  __shared__ uint4 g_lds[GAMMA ? NC * kWave : 1];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  const bool live = row < A.T;
-  const uint16_t* xr = A.x + (live ? row : 0) * A.ldx;
-  const int dl = lane * 8;
+// 8 bf16 quiet NaNs.
+__device__ __forceinline__ uint4 nan_group() {
+  return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+}
 
-  uint4 raw[NC];
+// Whether any of 8 bf16 values is NaN or Inf (exponent field all ones).
+__device__ __forceinline__ bool nonfinite_bf16x8(const uint4& r) {
+  auto bad = [](uint32_t w) {
+    return ((w & 0x7F80u) == 0x7F80u) || (((w >> 16) & 0x7F80u) == 0x7F80u);
+  };
+  return bad(r.x) || bad(r.y) || bad(r.z) || bad(r.w);
+}
+
+// gamma [D] goes to LDS as fp32, laid out [chunk][half][lane] (float4 each),
+// so each lane reads its 8 gains of a chunk as two conflict-free 16-byte LDS
+// reads. Staging is split in two: the global loads are issued first, ahead of
+// the row loads (the memory counter retires loads in order, so gains loaded
+// after the row could only be used once the whole row had arrived), and
+// written to LDS after the row loads are in flight. Item i = c * 64 + lane;
+// each of the workgroup's NT threads handles items tid, tid + NT, ...
+template <int NC, int NT>
+struct GammaStage {
+  static constexpr int kItems = (NC * kWave + NT - 1) / NT;
+  uint4 r[kItems];
+
+  __device__ __forceinline__ void load(const uint16_t* gamma, int D) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    raw[c] = (live && c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
-  if (GAMMA) {
-    stage_gamma(A.gamma, A.D, NC, g_lds);  // overlaps the row loads in flight
+    for (int k = 0; k < kItems; ++k) {
+      const int i = min((int)threadIdx.x + k * NT, NC * kWave - 1);
+      r[k] = load16(gamma + min(i * 8, D - 8));  // always in bounds; masked in store()
+    }
+  }
+
+  // Writes the gains to LDS (a group of 8 holding a NaN or Inf becomes 8
+  // NaNs, see G_GAIN) and waits for the whole workgroup.
+  __device__ __forceinline__ void store(int D, float4* g_lds) {
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const int i = (int)threadIdx.x + k * NT;
+      if (i < NC * kWave) {
+        const uint4 q = i * 8 < D ? r[k] : make_uint4(0, 0, 0, 0);
+        float v[8];
+        unpack8(nonfinite_bf16x8(q) ? nan_group() : q, v);
+        const int c = i / kWave, l = i % kWave;
+        g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
+        g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
     __syncthreads();
   }
-  if (!live) return;
+};
 
+__device__ __forceinline__ void gains(const float4* g_lds, int c, int lane, float g[8]) {
+  const float4 a = g_lds[(2 * c) * kWave + lane];
+  const float4 b = g_lds[(2 * c + 1) * kWave + lane];
+  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
+  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+}
+
+// The rest of a register-resident row once its chunks are loaded: block
+// maxima and the normaliser, then each chunk's products, scale, cast and
+// stores.
+template <int NC, int ELEM, int RND, int GM>
+__device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[NC],
+                                               const float4* g_lds, int64_t row, int lane,
+                                               uint32_t* sc) {
+  const int dl = lane * 8;
   uint32_t mb[NC];
   uint32_t rmax = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    mb[c] = quad_max_u32(absmax_bits8(raw[c]));
+    mb[c] = quad_max_u32(c * kChunk + dl < A.D ? absmax_bits8(raw[c]) : 0u);
     rmax = max(rmax, mb[c]);
   }
   rmax = max_over_quads(rmax);
   const float inv = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, rmax, A.pmode, A.p, A.Kf);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  // The empty asm claims to rewrite the packed row, so the compiler widens
+  // each chunk to fp32 where it is used below instead of ahead of the row
+  // reduction, where all widened chunks would be live at once.
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
 
+  const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
+  float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int d = c * kChunk + dl;
-    if (d < A.D)
-      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, raw[c], GAMMA ? g_lds[c * kWave + lane] : raw[c],
-                                         mb[c], inv, lane);
+    if (d < A.D) {
+      if (GM != G_NONE) gains(g_lds, c, lane, g);
+      const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, nrow + d, raw[c], g, mb[c], inv);
+      if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
+    }
   }
+  flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K, A.K, A.sc_vec != 0, lane);
+}
+
+// Register-resident row: NC chunks of 512 elements held in VGPRs. The
+// workgroup's rows share one LDS copy of gamma.
+
+template <int NC, int ELEM, int RND, bool GAMMA>
+__global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
+  __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
+  __shared__ uint32_t sc_lds[kRowsPerBlock][NC * 4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
+  const int dl = lane * 8;
+
+  GammaStage<GAMMA ? NC : 1, kThreads> gs;
+  if (GAMMA) gs.load(A.gamma, A.D);
+  __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
+  uint4 raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
+  __builtin_amdgcn_sched_barrier(0);
+  if (GAMMA) gs.store(A.D, g_lds);  // the row loads stay in flight meanwhile
+  if (!live) return;
+  uint32_t* sc = sc_lds[wave];
+  if (!GAMMA)
+    mxnorm_row_reg<NC, ELEM, RND, G_NONE>(A, raw, g_lds, row, lane, sc);
+  else
+    mxnorm_row_reg<NC, ELEM, RND, G_GAIN>(A, raw, g_lds, row, lane, sc);
 }
 
 // LDS-staged row: each wavefront copies its row into its own LDS slice with
 // direct-to-LDS loads (no VGPR staging), then runs the same two halves
 // reading chunks back from LDS. The chunk loop is not unrolled, so rows up to
-// MXQ_MAX_D fit; a lane only ever reads back the 16 bytes it loaded.
+// MXQ_MAX_D fit; a lane only ever reads back the 16 bytes it loaded. gamma
+// stays bf16 in LDS here (it is widened per use, to the same fp32 values).
+// Dynamic LDS: [rows][nchunks * 64] uint4 row slices, gamma [nchunks * 64]
+// uint4, then [rows][nchunks * 4] dwords of scales.
 template <int ELEM, int RND, bool GAMMA>
-__global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nchunks) {
-  extern __shared__ uint4 lds_rows[];  // [rows][nchunks * 64] then gamma [nchunks * 64]
+__global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nchunks, int rows) {
+  extern __shared__ uint4 lds_rows[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int rows = blockDim.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * rows + wave;
   const bool live = row < A.T;
   const uint16_t* xr = A.x + (live ? row : 0) * A.ldx;
   const int dl = lane * 8;
   uint4* slice = lds_rows + (size_t)wave * nchunks * kWave;
   uint4* g_lds = lds_rows + (size_t)rows * nchunks * kWave;
+  uint32_t* sc = reinterpret_cast<uint32_t*>(g_lds + (GAMMA ? nchunks * kWave : 0)) +
+                 (size_t)wave * nchunks * 4;
 
+  // gamma first: the memory counter retires loads in order (see GammaStage)
+  if (GAMMA) {
+    for (int i = threadIdx.x; i < nchunks * kWave; i += rows * kWave) {
+      const uint4 r = (i * 8 < A.D) ? load16(A.gamma + i * 8) : make_uint4(0, 0, 0, 0);
+      g_lds[i] = nonfinite_bf16x8(r) ? nan_group() : r;  // see G_GAIN
+    }
+  }
   if (live) {
     for (int c = 0; c < nchunks; ++c) {
       if (c * kChunk + dl < A.D)
@@ -425,10 +588,7 @@ __global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nc
         slice[c * kWave + lane] = make_uint4(0, 0, 0, 0);
     }
   }
-  if (GAMMA) {
-    stage_gamma(A.gamma, A.D, nchunks, g_lds);
-    __syncthreads();
-  }
+  if (GAMMA) __syncthreads();
   if (!live) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -439,14 +599,23 @@ __global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nc
   const float inv = row_normaliser<0>(nchunks, mb, rmax, A.pmode, A.p, A.Kf);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
 
+  const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
+  float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c = 0; c < nchunks; ++c) {
     const int d = c * kChunk + dl;
     if (d < A.D) {
       const uint4 xb = slice[c * kWave + lane];
-      const uint4 gb = GAMMA ? g_lds[c * kWave + lane] : xb;
-      mxnorm_chunk_out<ELEM, RND, GAMMA>(A, row, d, xb, gb, GAMMA ? 0u : mb(c), inv, lane);
+      uint32_t code;
+      if (!GAMMA) {
+        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, nrow + d, xb, g, mb(c), inv);
+      } else {
+        unpack8(g_lds[c * kWave + lane], g);
+        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, nrow + d, xb, g, 0u, inv);
+      }
+      if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
     }
   }
+  flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K, A.K, A.sc_vec != 0, lane);
 }
 
 // ------------------------------------------------------------------ RMSNorm
@@ -508,11 +677,11 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
   const int dl = lane * 8;
   uint4 raw[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    raw[c] = (c * kChunk + dl < A.D) ? load16(xr + c * kChunk + dl) : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) s = sumsq8(raw[c], s);
+  for (int c = 0; c < NC; ++c)
+    if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
   s = sum_over_wave(s);
   const float inv = 1.0f / sqrtf(s / A.Df + A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
@@ -554,11 +723,13 @@ struct CastArgs {
   uint32_t chunks_per_row;
   int D;
   int K;
+  int sc_vec;  // every chunk holds 16 blocks (D % 512 == 0) and scales take dword stores
   SrStream rng;
 };
 
 template <int ELEM, int RND>
 __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
+  __shared__ uint32_t sc_lds[kRowsPerBlock][kCastChunksPerWave * 4];
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t g0 = (blockIdx.x * kRowsPerBlock + wave) * kCastChunksPerWave;
@@ -568,13 +739,14 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
   int ds[kCastChunksPerWave];
 #pragma unroll
   for (int u = 0; u < kCastChunksPerWave; ++u) {
-    const uint32_t g = g0 + u;
+    const uint32_t g = min(g0 + u, A.total_chunks - 1);  // past the end: re-read the last chunk
     const uint32_t r = g / A.chunks_per_row;
     rows[u] = r;
-    ds[u] = (int)(g - r * A.chunks_per_row) * kChunk + dl;
-    raw[u] = (g < A.total_chunks && ds[u] < A.D)
-                 ? load16(A.x + (int64_t)r * A.ldx + ds[u]) : make_uint4(0, 0, 0, 0);
+    const int c = (int)(g - r * A.chunks_per_row);
+    ds[u] = c * kChunk + dl;
+    raw[u] = load_chunk(A.x + (int64_t)r * A.ldx, c, dl, A.D);
   }
+  uint32_t* sc = sc_lds[wave];
 #pragma unroll
   for (int u = 0; u < kCastChunksPerWave; ++u) {
     if (g0 + u < A.total_chunks && ds[u] < A.D) {
@@ -584,9 +756,18 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
       unpack8(raw[u], v);
       const uint64_t n = (uint64_t)rows[u] * (uint64_t)A.D + (uint64_t)ds[u];
       encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
-      if ((lane & 3) == 0)
-        A.scales[(uint64_t)rows[u] * (uint64_t)A.K + (uint64_t)(ds[u] >> 5)] = (uint8_t)code;
+      if ((lane & 3) == 0) {
+        if (A.sc_vec)
+          put_scale(sc, u * 16 + (lane >> 2), code);
+        else
+          A.scales[(uint64_t)rows[u] * (uint64_t)A.K + (uint64_t)(ds[u] >> 5)] = (uint8_t)code;
+      }
     }
+  }
+  if (A.sc_vec && g0 < A.total_chunks) {
+    // with 16 blocks per chunk, block q of chunk g sits at scale index 16 g + q
+    const uint32_t nvalid = min((uint32_t)kCastChunksPerWave, A.total_chunks - g0);
+    flush_scales(sc, A.scales + (uint64_t)g0 * 16u, (int)(16 * nvalid), true, lane);
   }
 }
 
@@ -626,8 +807,9 @@ constexpr size_t kLdsPerBlockMax = 160 * 1024;  // gfx950 LDS per workgroup
 
 template <int ELEM, int RND, bool GAMMA>
 mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
-  const size_t per_row = (size_t)nc * kWave * sizeof(uint4);
-  const size_t g_bytes = GAMMA ? per_row : 0;
+  // per row: the bf16 row and its scale bytes; per workgroup: bf16 gamma
+  const size_t per_row = (size_t)nc * kWave * sizeof(uint4) + (size_t)nc * 16;
+  const size_t g_bytes = GAMMA ? (size_t)nc * kWave * sizeof(uint4) : 0;
   if (per_row + g_bytes > kLdsPerBlockMax) return MXQ_ERR_UNSUPPORTED;
   int rows = (int)((kLdsPerBlockMax - g_bytes) / per_row);
   if (rows > kRowsPerBlock) rows = kRowsPerBlock;
@@ -638,7 +820,7 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
                           (int)bytes) != hipSuccess)
     return MXQ_ERR_HIP;
   const unsigned grid = (unsigned)((A.T + rows - 1) / rows);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * rows), bytes, s, A, nc);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * rows), bytes, s, A, nc, rows);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
@@ -755,6 +937,7 @@ mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int
   A.Kf = (float)(D / 32);
   A.p = p;
   A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
+  A.sc_vec = (A.K % 4 == 0) && aligned(scales, 4);
   A.rng = make_stream(rng);
   const int nc = (int)((D + kChunk - 1) / kChunk);
   const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
@@ -805,6 +988,7 @@ mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* ga
   C.total_chunks = (uint32_t)(T * nc);
   C.D = (int)D;
   C.K = (int)(D / 32);
+  C.sc_vec = (D % kChunk == 0) && aligned(scales, 4);
   C.rng = make_stream(rng);
   return dispatch_cast(C, elem, rnd, s);
 }
@@ -826,6 +1010,7 @@ mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_
   C.total_chunks = (uint32_t)(T * nc);
   C.D = (int)D;
   C.K = (int)(D / 32);
+  C.sc_vec = (D % kChunk == 0) && aligned(scales, 4);
   C.rng = make_stream(rng);
   return dispatch_cast(C, elem, rnd, (hipStream_t)stream);
 }

@@ -195,6 +195,28 @@ def test_mxnorm_special_rows(p):
     check_mxnorm(xg, g, p, what=f"special gamma p={p}")
 
 
+@pytest.mark.parametrize("flags", [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS])
+def test_mxnorm_nonfinite_gains(flags):
+    # a NaN or Inf gain makes its products non-finite: those blocks get scale
+    # 0xFF and NaN codes in every row; Inf * 0 (zero row) is NaN too
+    D = 1024
+    x = workloads.random_rows(6, D, seed=85).clone()
+    x[2] = 0.0
+    x[3, :] = x[3, :] * 1e30                 # products overflow to Inf with large gains
+    g = workloads.random_gamma(D, seed=86).clone()
+    g[5] = float("nan")
+    g[300] = float("inf")
+    g[301] = float("-inf")
+    g[700] = 3e38                            # finite gain, x * gain overflows in row 3
+    # fp32 products overflow where fp64 ones do not: only the injected-mode
+    # (bit-exact, fp32 operation order) comparison applies here
+    c, s, i = check_mxnorm(x.to(DEV), g.to(DEV), 2.0, flags=flags, what=f"nonfinite gains {flags}",
+                           ref=False)
+    assert s[3, 700 // 32] == 255
+    assert (s[:, 0] == 255).all() and (s[:, 9] == 255).all()
+    assert (c[:, :32] == 0x7F).all()
+
+
 @pytest.mark.parametrize("D", [256, 4096, 8192])
 @pytest.mark.parametrize("gamma", [False, True])
 def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma):
@@ -285,3 +307,44 @@ def test_workload_mxfp4_sampled():
     T = x.shape[0]
     for r0 in (0, T // 3, T - 512):
         check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r0 + 512), what=f"mxfp4 rows {r0}")
+
+
+# ---------------------------------------------------------------- graph capture
+
+def test_graph_replays_match_eager():
+    # the C-ABI calls captured in a HIP graph and replayed several times, with
+    # eager work and synchronisations between replays, reproduce the eager outputs
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV, rows=777)
+    T, D = x.shape
+    eager = mxq.mxnorm(x, g, 2.0)
+    eager_tp = mxq.rmsnorm_mxcast(x, g, 1e-5, "e4m3", "sr", 5, 1)
+    eager_c = mxq.mxcast(x, "e2m1", "sr", 7, 3)
+    torch.cuda.synchronize()
+    out = tuple(torch.empty_like(t) for t in eager)
+    out_tp = tuple(torch.empty_like(t) for t in eager_tp[:3])
+    y_tp = torch.empty_like(eager_tp[3])
+    out_c = (torch.empty_like(eager_c[0]), torch.empty_like(eager_c[1]), None)
+
+    def work():
+        mxq.mxnorm(x, g, 2.0, out=out)
+        mxq.rmsnorm_mxcast(x, g, 1e-5, "e4m3", "sr", 5, 1, out=out_tp, y=y_tp)
+        mxq.mxcast(x, "e2m1", "sr", 7, 3, out=out_c)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        for t in (*out, *out_tp, y_tp, out_c[0], out_c[1]):
+            t.view(torch.uint8).fill_(0xA5 + rep)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert same_outputs(out, eager), rep
+        assert same_outputs(out_tp, eager_tp[:3]) and torch.equal(y_tp, eager_tp[3]), rep
+        assert same_outputs(out_c[:2], eager_c), rep
