@@ -170,18 +170,26 @@ __device__ __forceinline__ uint32_t e8m0_code(float amax) {
 
 // ------------------------------------------------------------------ Philox
 
+// a ^ b ^ k in one VALU instruction (k is the wave-uniform round key).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_xor3_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53
 // and 0xCD9E8D57, key increments 0x9E3779B9 and 0xBB67AE85.
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-    c0 = hi1 ^ c1 ^ k0;
-    c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
-    c3 = lo0;
+    // one 32x32 -> 64-bit multiply each (v_mad_u64_u32 gives both halves)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    c0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    c1 = (uint32_t)p1;
+    c2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+    c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -231,31 +239,31 @@ __device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], uint32_t 
 }
 
 // Stochastic rounding of v (already divided by the scale, |v| < 2^(emax+1)):
-// with M the 24-bit significand and the quantum 2^sh units of it, n = M >> sh
-// and frac32 = floor(frac * 2^32) are the bits below; round up iff r < frac32.
+// with n the magnitude in units of the local quantum, truncated, and frac32 =
+// floor(frac * 2^32) the part below it, round up iff r < frac32; saturating.
+//   normal binades: n and the exponent form the code directly, (a >> sh) - bias,
+//     and the discarded mantissa bits shifted to the top are frac32;
+//   below the smallest normal the quantum is fixed (2^-9, E2M1 2^-1): q = |v| /
+//     quantum is exact, n = trunc(q), and (q - n) * 2^32 is exact as well.
 template <int ELEM>
 __device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
-  // E4M3: normal binades keep 3 of 23 mantissa bits (sh = 20); below 2^-6 the
-  // quantum is 2^-9 (sh = 141 - e). E2M1: sh = 22 and quantum 2^-1 below 1.
-  constexpr int kShNorm = (ELEM == MXQ_E4M3) ? 20 : 22;
-  constexpr int kShBase = (ELEM == MXQ_E4M3) ? 141 : 149;
-  constexpr int kEmin = (ELEM == MXQ_E4M3) ? 121 : 127;  // biased fp32 exponent of min normal
-  constexpr int kMbits = (ELEM == MXQ_E4M3) ? 3 : 1;
+  constexpr int kSh = (ELEM == MXQ_E4M3) ? 20 : 22;                // fp32 mantissa bits dropped
+  constexpr uint32_t kBias = (ELEM == MXQ_E4M3) ? 960u : 252u;     // (120 << 3), (126 << 1)
+  constexpr uint32_t kMinNormal = (ELEM == MXQ_E4M3) ? 0x3C800000u : 0x3F800000u;  // 2^-6, 1
+  constexpr float kInvQuantum = (ELEM == MXQ_E4M3) ? 512.0f : 2.0f;
   constexpr uint32_t kMaxCode = (ELEM == MXQ_E4M3) ? 0x7Eu : 0x7u;
   constexpr int kSignBit = (ELEM == MXQ_E4M3) ? 7 : 3;
   const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 31) << kSignBit;
   const uint32_t a = u & 0x7FFFFFFFu;
-  const int e = (int)(a >> 23);
-  const uint32_t m24 = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-  const int ee = e ? e : 1;
-  const int sh = max(kShBase - ee, kShNorm);
-  const uint32_t n = sh < 32 ? (m24 >> sh) : 0u;
-  const uint32_t frac = (uint32_t)(((uint64_t)m24 << 32) >> min(sh, 63));
-  const uint32_t up = r < frac ? 1u : 0u;
-  uint32_t code = (ee > kEmin ? (uint32_t)(ee - kEmin) << kMbits : 0u) + n + up;
-  code = min(code, kMaxCode);
-  return code | sign;
+  // both forms, then a select per lane (no divergent branch); q < 2^18 always
+  const float q = __uint_as_float(a) * kInvQuantum;
+  const uint32_t n_sub = (uint32_t)q;
+  const uint32_t f_sub = (uint32_t)((q - (float)n_sub) * 4294967296.0f);
+  const bool normal = a >= kMinNormal;
+  uint32_t code = normal ? (a >> kSh) - kBias : n_sub;
+  const uint32_t frac = normal ? a << (32 - kSh) : f_sub;
+  code = min(code + (r < frac ? 1u : 0u), kMaxCode);
+  return code | ((u >> 31) << kSignBit);
 }
 
 __device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], uint32_t code, const uint32_t r[8]) {
@@ -551,6 +559,8 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
     mxnorm_row_reg<NC, ELEM, RND, G_GAIN>(A, raw, g_lds, row, lane, sc);
 }
 
+constexpr int kMaxLdsRows = 16;  // wavefronts (rows) per workgroup of the LDS-staged variant
+
 // LDS-staged row: each wavefront copies its row into its own LDS slice with
 // direct-to-LDS loads (no VGPR staging), then runs the same two halves
 // reading chunks back from LDS. The chunk loop is not unrolled, so rows up to
@@ -559,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
 // Dynamic LDS: [rows][nchunks * 64] uint4 row slices, gamma [nchunks * 64]
 // uint4, then [rows][nchunks * 4] dwords of scales.
 template <int ELEM, int RND, bool GAMMA>
-__global__ __launch_bounds__(kThreads) void mxnorm_lds_kernel(NormArgs A, int nchunks, int rows) {
+__global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArgs A, int nchunks, int rows) {
   extern __shared__ uint4 lds_rows[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -807,12 +817,23 @@ constexpr size_t kLdsPerBlockMax = 160 * 1024;  // gfx950 LDS per workgroup
 
 template <int ELEM, int RND, bool GAMMA>
 mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
-  // per row: the bf16 row and its scale bytes; per workgroup: bf16 gamma
+  // per row: the bf16 row and its scale bytes; per workgroup: bf16 gamma.
+  // Rows per workgroup: the count that keeps the most rows resident per CU
+  // (LDS is the limit), the smaller one on ties.
   const size_t per_row = (size_t)nc * kWave * sizeof(uint4) + (size_t)nc * 16;
   const size_t g_bytes = GAMMA ? (size_t)nc * kWave * sizeof(uint4) : 0;
   if (per_row + g_bytes > kLdsPerBlockMax) return MXQ_ERR_UNSUPPORTED;
-  int rows = (int)((kLdsPerBlockMax - g_bytes) / per_row);
-  if (rows > kRowsPerBlock) rows = kRowsPerBlock;
+  int rows = 1;
+  size_t best = 0;
+  for (int r = 1; r <= kMaxLdsRows; ++r) {
+    const size_t b = per_row * r + g_bytes;
+    if (b > kLdsPerBlockMax) break;
+    const size_t resident = (size_t)r * (kLdsPerBlockMax / b);
+    if (resident > best) {
+      best = resident;
+      rows = r;
+    }
+  }
   const size_t bytes = per_row * rows + g_bytes;
   auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA>;
   if (bytes > 64 * 1024 &&
