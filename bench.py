@@ -6,7 +6,8 @@ HBM. Ten input/output buffer sets (~1 GB) are used round-robin so the 256 MB
 MALL cannot serve a step from cache. Prints one JSON line.
 
 The same line carries, for context: the p = 1 variant, the two-pass
-RMSNorm -> MXCast comparison path (each timed the same way), a plain
+RMSNorm -> MXCast comparison path and the single-pass exact-RMS comparator
+(each timed the same way), a plain
 device-to-device copy of the same byte count, the roofline of the fused
 kernel (per-launch HIP-event durations on the launch stream) and the CPU
 oracle timed on a bounded sample.
@@ -216,6 +217,16 @@ def main():
         if st != mxq.MXQ_OK:
             raise mxq.MxqError(st, "rmsnorm_mxcast_fwd")
 
+    rs_args = [(vp(xs[k].data_ptr()), D, vp(g.data_ptr()), T, D, ctypes.c_float(1e-5),
+                mxq.MXQ_E4M3, mxq.MXQ_RNE, None, 0, vp(outs[k][0].data_ptr()),
+                vp(outs[k][1].data_ptr()), vp(outs[k][2].data_ptr())) for k in range(ROTATE)]
+
+    def rms_fused_raw(i):
+        st = lib.rmsnorm_mxcast_fused_fwd(*rs_args[i % ROTATE],
+                                          vp(torch.cuda.current_stream().cuda_stream))
+        if st != mxq.MXQ_OK:
+            raise mxq.MxqError(st, "rmsnorm_mxcast_fused_fwd")
+
     def two_pass_hot(i):
         mxq.rmsnorm_mxcast(xs[0], g, 1e-5, "e4m3", "rne", out=outs[0], y=ys[0])
 
@@ -234,6 +245,7 @@ def main():
     tp_t = time_launches(torch, two_pass_raw, K, W)
     tp_step_s, _, _ = time_graph(torch, two_pass_raw, K, W)
     tp_hot = time_launches(torch, two_pass_hot, K, W)
+    rs_step_s, _, _ = time_graph(torch, rms_fused_raw, K, W)
     cp_t = time_launches(torch, copy, K, W)
 
     nbytes = fused_bytes(T, D)
@@ -287,6 +299,12 @@ def main():
                 "GB/s_own_bytes": round(two_pass_bytes(T, D) / tp_step_s / 1e9, 2),
                 "fused_speedup_kernels": round(tp_t["kernel_mean_s"] / main_t["kernel_mean_s"], 3),
                 "hot_no_rotation_kernels_mean_us": round(tp_hot["kernel_mean_s"] * 1e6, 3),
+            },
+            "single_pass_exact_rms": {
+                "ms_per_step": round(rs_step_s * 1e3, 6),
+                "GB/s": round(nbytes / rs_step_s / 1e9, 2),
+                "mxnorm_speedup": round(rs_step_s / step_s, 3),
+                "speedup_over_two_pass": round(tp_step_s / rs_step_s, 3),
             },
             "d2d_copy_same_bytes": {"kernel_mean_us": round(cp_t["kernel_mean_s"] * 1e6, 3),
                                     "GB/s": round(2 * copy_n / cp_t["kernel_mean_s"] / 1e9, 2)},

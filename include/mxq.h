@@ -132,6 +132,22 @@ mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* ga
                               uint8_t* scales, float* inv_rms, void* stream);
 
 /*
+ * Single-pass exact-RMS comparator: RMSNorm's statistic (MXNorm page, §1.1),
+ * inv = 1 / sqrt(sum(x^2) / D + eps) in fp32 summed in the same order as
+ * rmsnorm_mxcast_fwd (so inv_rms is bit-identical to its), applied as in
+ * mxnorm_fwd, y = RN32(RN32(x * gamma) * inv), and cast to MX in the same pass
+ * (§2.1) without rounding y to bf16. It differs from mxnorm_fwd only in the
+ * statistic (D squares instead of K block maxima) and from the two-pass path
+ * only in keeping the row on chip. Arguments, flags and errors as for
+ * mxnorm_fwd with eps (>= 0, finite) in place of p; inv_rms [T] may be NULL.
+ */
+mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                                    int64_t T, int64_t D, float eps, mxq_elem elem,
+                                    mxq_round rnd, const mxq_rng* rng, uint32_t flags,
+                                    uint8_t* codes, uint8_t* scales, float* inv_rms,
+                                    void* stream);
+
+/*
  * MXCast of a bf16 activation (MXNorm page, §1.2 and §2.1): block absmax,
  * E8M0 scale and element cast, with no normalisation.
  */

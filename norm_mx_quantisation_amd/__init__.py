@@ -1,12 +1,13 @@
 """norm_mx_quantisation_amd: MXNorm fused with the MX cast on MI355X (gfx950).
 
 Thin ctypes binding of libmxq.so. The functions named like the C entry points
-(mxnorm_fwd, rmsnorm_mxcast_fwd, mxcast_fwd, mxq_strerror, mxq_abi_version)
-take raw device pointers and sizes and return the status code, exactly as the
-C ABI does. The torch helpers (mxnorm, rmsnorm_mxcast, mxcast) only check
-tensor metadata, allocate the outputs and pass pointers; every step of the
-computation runs in the HIP kernels. There is no CPU fallback: without the
-built library every call raises.
+(mxnorm_fwd, rmsnorm_mxcast_fwd, rmsnorm_mxcast_fused_fwd, mxcast_fwd,
+mxq_strerror, mxq_abi_version) take raw device pointers and sizes and return
+the status code, exactly as the C ABI does. The torch helpers (mxnorm,
+rmsnorm_mxcast, rmsnorm_mxcast_fused, mxcast) only check tensor metadata,
+allocate the outputs and pass pointers; every step of the computation runs in
+the HIP kernels. There is no CPU fallback: without the built library every
+call raises.
 """
 
 from __future__ import annotations
@@ -27,7 +28,8 @@ MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS = 1, 2
 MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
 ABI_VERSION = 1
 
-EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "mxcast_fwd", "mxq_strerror", "mxq_abi_version")
+EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
+           "mxq_strerror", "mxq_abi_version")
 
 
 class mxq_rng(ctypes.Structure):
@@ -62,6 +64,9 @@ def lib():
             L.rmsnorm_mxcast_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, vp, vp, vp,
                                              vp, vp]
             L.rmsnorm_mxcast_fwd.restype = i32
+            L.rmsnorm_mxcast_fused_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, u32,
+                                                   vp, vp, vp, vp]
+            L.rmsnorm_mxcast_fused_fwd.restype = i32
             L.mxcast_fwd.argtypes = [vp, i64, i64, i64, i32, i32, rp, vp, vp, vp]
             L.mxcast_fwd.restype = i32
             L.mxq_strerror.argtypes = [i32]
@@ -95,6 +100,12 @@ def rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, y_workspace, co
                        inv_rms, stream) -> int:
     return lib().rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, _rng(rng), y_workspace,
                                     codes, scales, inv_rms, stream)
+
+
+def rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, codes, scales,
+                             inv_rms, stream) -> int:
+    return lib().rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, _rng(rng), flags,
+                                          codes, scales, inv_rms, stream)
 
 
 def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, codes, scales, stream) -> int:
@@ -177,6 +188,23 @@ def rmsnorm_mxcast(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3", rounding
     if st != MXQ_OK:
         raise MxqError(st, "rmsnorm_mxcast_fwd")
     return codes, scales, inv, y
+
+
+def rmsnorm_mxcast_fused(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3",
+                         rounding: str = "rne", seed: int = 0, offset: int = 0, flags: int = 0,
+                         stream=None, out=None):
+    """Single-pass exact-RMS normalise and MX cast. Returns (codes, scales, inv_rms)."""
+    T, D, ldx = _check_x(x)
+    elem, rnd = _ELEM[fmt], _RND[rounding]
+    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
+    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    st = rmsnorm_mxcast_fused_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(eps), elem, rnd,
+                                  (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(codes),
+                                  _ptr(scales), _ptr(inv), _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "rmsnorm_mxcast_fused_fwd")
+    return codes, scales, inv
 
 
 def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: int = 0,

@@ -41,6 +41,11 @@ constexpr int kCastChunksPerWave = 4; // MXCast chunks per wavefront
 
 enum PMode { P_ONE = 0, P_TWO = 1, P_INF = 2, P_GEN = 3 };
 
+// Row statistic of the single-pass normalise-and-cast kernels: the power mean
+// of the block maxima (MXNorm), or the exact RMS over all D elements (RMSNorm's
+// statistic, the single-pass comparator).
+enum Stat { S_PMEAN = 0, S_RMS = 1 };
+
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -72,35 +77,81 @@ __device__ __forceinline__ uint32_t absmax_bits8(const uint4& r) {
   return max(mm & 0xFFFFu, mm >> 16);
 }
 
+// Cross-lane moves that stay in the VALU (no LDS round trip): DPP within a
+// quad and within a row of 16 lanes; across rows, lane reads into scalar
+// registers (over_quads below).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowMirror = 0x140;    // lane i <-> 15 - i within a row of 16
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within 8 lanes
+
 // Max over the 4 lanes of a quad (one MX block); exact, so any order is fine.
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false)); // [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false)); // [2,3,0,1]
+  v = max(v, dpp<kDppQuadSwap1>(v));
+  v = max(v, dpp<kDppQuadSwap2>(v));
   return v;
 }
 
-// Sum of a value held identically by the 4 lanes of each quad, over the 16
-// quads. XOR butterflies make every lane compute the same bits.
+__device__ __forceinline__ uint32_t f32_add_bits(uint32_t a, uint32_t b) {
+  return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+}
+
+// Butterfly over the 16 quads of a wave for a value each quad holds in all 4
+// lanes, with a commutative op: quad q meets q ^ 1 (half mirror), then pairs
+// meet pairs (row mirror), so every lane of a row of 16 holds its row's
+// value; the four row values are read into scalar registers and combined as
+// (row0 op row1) op (row2 op row3). The result is wave-uniform, and the
+// combining tree is the one an XOR butterfly over lane distances 4, 8, 16, 32
+// builds.
+template <class Op>
+__device__ __forceinline__ uint32_t over_quads(uint32_t v, Op op) {
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppRowMirror>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)op(op(r0, r1), op(r2, r3)));
+}
+
+// Sum over the 16 quads of a value held identically by each quad's 4 lanes.
 __device__ __forceinline__ float sum_over_quads(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  return __uint_as_float(over_quads(__float_as_uint(v), f32_add_bits));
 }
 
 __device__ __forceinline__ uint32_t max_over_quads(uint32_t v) {
-  v = max(v, (uint32_t)__shfl_xor((int)v, 4));
-  v = max(v, (uint32_t)__shfl_xor((int)v, 8));
-  v = max(v, (uint32_t)__shfl_xor((int)v, 16));
-  v = max(v, (uint32_t)__shfl_xor((int)v, 32));
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+  return over_quads(v, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 
+// Sum over all 64 lanes: lane pairs, then pairs of pairs within each quad,
+// then over the quads.
 __device__ __forceinline__ float sum_over_wave(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  return sum_over_quads(v);
+  uint32_t u = __float_as_uint(v);
+  u = f32_add_bits(u, dpp<kDppQuadSwap1>(u));
+  u = f32_add_bits(u, dpp<kDppQuadSwap2>(u));
+  return sum_over_quads(__uint_as_float(u));
+}
+
+// Adds the squares of 8 bf16 values to s, in element order.
+__device__ __forceinline__ float sumsq8(const uint4& r, float s) {
+  float v[8];
+  unpack8(r, v);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = __builtin_fmaf(v[j], v[j], s);
+  return s;
+}
+
+// RMSNorm's normaliser 1 / sqrt(S / D + eps) from a lane's partial sum of
+// squares: the lanes' sums are added by the wave butterfly. Every RMS path
+// (two-pass and single-pass, register and LDS rows) sums in this order: each
+// lane its chunks in chunk order, then the butterfly, so all give the same bits.
+__device__ __forceinline__ float rms_normaliser(float lane_sum, float Df, float eps) {
+  const float s = sum_over_wave(lane_sum);
+  return 1.0f / sqrtf(s / Df + eps);
 }
 
 // ------------------------------------------------------------------ p-mean
@@ -136,23 +187,29 @@ __device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift,
 }
 
 // Normaliser 1/G of a row from its block maxima (bf16 bit patterns, one per
-// chunk for this lane's quad, zero for blocks past the row end). rmax is the
-// row maximum of the patterns. Terms are added chunk by chunk in each lane,
-// then over the quads; every variant uses exactly this order.
-template <int NCT, class BlockMax>
-__device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, uint32_t rmax, int pmode,
-                                                float p, float K) {
+// chunk for this lane's quad, zero for blocks past the row end). lane_max()
+// gives this lane's maximum of the patterns. Terms are added chunk by chunk in
+// each lane, then over the quads; every variant uses exactly this order.
+// A sum inside [2^-96, 2^96] is finite and nonzero, so the row holds no NaN
+// or Inf (either would make the sum non-finite) and is not all zero: the row
+// maximum is only needed outside that range, and for p = inf.
+template <int NCT, class BlockMax, class LaneMax>
+__device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, LaneMax lane_max,
+                                                int pmode, float p, float K) {
+  if (pmode != P_INF) {
+    const float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, 0, pmode, p));
+    if (s >= 0x1p-96f && s <= 0x1p96f) return 1.0f / pmean_finish(s, pmode, p, K);
+  }
+  const uint32_t rmax = max_over_quads(lane_max());
   if (rmax >= 0x7F80u) return __builtin_nanf("");  // the row holds NaN or Inf
   if (rmax == 0u) return 0.0f;                      // all-zero row
   if (pmode == P_INF) return 1.0f / __uint_as_float(rmax << 16);
-  float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, 0, pmode, p));
-  if (s >= 0x1p-96f && s <= 0x1p96f) return 1.0f / pmean_finish(s, pmode, p, K);
   // The p-th powers left the range where fp32 holds them accurately (an
   // underflowing or overflowing sum): rescale the maxima by 2^-E, E the
   // exponent of the row maximum, and undo it on G.
   int E = (int)((rmax >> 7) & 0xFFu) - 127;
   if (E < -126) E = -126;
-  s = sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p));
+  const float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p));
   return 1.0f / ldexpf(pmean_finish(s, pmode, p, K), E);
 }
 
@@ -170,11 +227,10 @@ __device__ __forceinline__ uint32_t e8m0_code(float amax) {
 
 // ------------------------------------------------------------------ Philox
 
-// a ^ b ^ k in one VALU instruction (k is the wave-uniform round key).
-__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_xor3_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+// a ^ b ^ c as one gfx950 three-input bitwise operation (0x96 is the truth
+// table of the three-way parity, the same for any order of the inputs).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53
@@ -319,22 +375,33 @@ __device__ __forceinline__ void store4_stream(uint8_t* p, uint32_t v) {
 }
 
 // Encode and store 8 elements at element offset n of a contiguous code tensor.
+// Encodes the 8 elements at column d of a row and stores them. codes_row is
+// the row's first code byte (uniform across the wave, so the store takes a
+// scalar base and a 32-bit lane offset); n = row * D + d is the logical
+// element index that keys the stochastic-rounding stream.
 template <int ELEM, int RND>
-__device__ __forceinline__ void encode_store8(uint8_t* codes, uint64_t n, const float y[8],
-                                              uint32_t code, const SrStream& rng) {
+__device__ __forceinline__ void encode_store8(uint8_t* codes_row, uint32_t d, uint64_t n,
+                                              const float y[8], uint32_t code,
+                                              const SrStream& rng) {
   if (RND == MXQ_SR) {
     uint32_t r[8];
     rng.words8(n, r);
     if (ELEM == MXQ_E4M3)
-      store8_stream(codes + n, encode8_e4m3_sr(y, code, r));
+      store8_stream(codes_row + d, encode8_e4m3_sr(y, code, r));
     else
-      store4_stream(codes + (n >> 1), encode8_e2m1_sr(y, code, r));
+      store4_stream(codes_row + (d >> 1), encode8_e2m1_sr(y, code, r));
   } else {
     if (ELEM == MXQ_E4M3)
-      store8_stream(codes + n, encode8_e4m3_rne(y, code));
+      store8_stream(codes_row + d, encode8_e4m3_rne(y, code));
     else
-      store4_stream(codes + (n >> 1), encode8_e2m1_rne(y, code));
+      store4_stream(codes_row + (d >> 1), encode8_e2m1_rne(y, code));
   }
+}
+
+// First code byte of row t (E2M1 packs two codes per byte; D is even).
+template <int ELEM>
+__device__ __forceinline__ uint8_t* code_row(uint8_t* codes, uint64_t nrow) {
+  return codes + (ELEM == MXQ_E4M3 ? nrow : nrow >> 1);
 }
 
 // Make one lane's LDS writes visible to the other lanes of its wavefront.
@@ -377,6 +444,8 @@ struct NormArgs {
   float Kf;
   float p;
   int pmode;
+  float Df;    // D, for the RMS statistic
+  float eps;   // RMS statistic only
   int sc_vec;  // scales rows can be written in dwords
   SrStream rng;
 };
@@ -412,23 +481,25 @@ __device__ __forceinline__ uint32_t chunk_products(const uint4& xb, const float 
 // Second half: y = RN(v * inv), E8M0 code from max |y| = RN(max |v| * inv)
 // (rounding is monotone), codes stored. Returns the code of the lane's block.
 template <int ELEM, int RND>
-__device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint64_t n, float v[8],
+__device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* codes_row,
+                                                 uint64_t nrow, uint32_t d, float v[8],
                                                  uint32_t vmax_bits, float inv) {
   const float amax = __uint_as_float(vmax_bits) * inv;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
   const uint32_t code = e8m0_code<ELEM>(amax);
-  encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
+  encode_store8<ELEM, RND>(codes_row, d, nrow + d, v, code, A.rng);
   return code;
 }
 
-// Both halves of one chunk.
+// Both halves of the chunk at column d of row nrow / D.
 template <int ELEM, int RND, int GM>
-__device__ __forceinline__ uint32_t mxnorm_chunk(const NormArgs& A, uint64_t n, const uint4& xb,
+__device__ __forceinline__ uint32_t mxnorm_chunk(const NormArgs& A, uint8_t* codes_row,
+                                                 uint64_t nrow, uint32_t d, const uint4& xb,
                                                  const float g[8], uint32_t mbits, float inv) {
   float v[8];
   const uint32_t vm = chunk_products<GM>(xb, g, mbits, v);
-  return chunk_finish<ELEM, RND>(A, n, v, vm, inv);
+  return chunk_finish<ELEM, RND>(A, codes_row, nrow, d, v, vm, inv);
 }
 
 // 8 bf16 quiet NaNs.
@@ -493,20 +564,30 @@ __device__ __forceinline__ void gains(const float4* g_lds, int c, int lane, floa
 // The rest of a register-resident row once its chunks are loaded: block
 // maxima and the normaliser, then each chunk's products, scale, cast and
 // stores.
-template <int NC, int ELEM, int RND, int GM>
+template <int NC, int ELEM, int RND, int GM, int STAT>
 __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[NC],
                                                const float4* g_lds, int64_t row, int lane,
                                                uint32_t* sc) {
   const int dl = lane * 8;
   uint32_t mb[NC];
-  uint32_t rmax = 0;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    mb[c] = quad_max_u32(c * kChunk + dl < A.D ? absmax_bits8(raw[c]) : 0u);
-    rmax = max(rmax, mb[c]);
+  for (int c = 0; c < NC; ++c) mb[c] = quad_max_u32(c * kChunk + dl < A.D ? absmax_bits8(raw[c]) : 0u);
+  float inv;
+  if constexpr (STAT == S_RMS) {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
+    inv = rms_normaliser(s, A.Df, A.eps);
+  } else {
+    auto lane_max = [&]() {
+      uint32_t m = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) m = max(m, mb[c]);
+      return m;
+    };
+    inv = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, lane_max, A.pmode, A.p, A.Kf);
   }
-  rmax = max_over_quads(rmax);
-  const float inv = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, rmax, A.pmode, A.p, A.Kf);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
   // The empty asm claims to rewrite the packed row, so the compiler widens
   // each chunk to fp32 where it is used below instead of ahead of the row
@@ -516,13 +597,14 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
     asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
 
   const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
+  uint8_t* crow = code_row<ELEM>(A.codes, nrow);
   float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int d = c * kChunk + dl;
     if (d < A.D) {
       if (GM != G_NONE) gains(g_lds, c, lane, g);
-      const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, nrow + d, raw[c], g, mb[c], inv);
+      const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, crow, nrow, d, raw[c], g, mb[c], inv);
       if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
     }
   }
@@ -532,12 +614,12 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
 // Register-resident row: NC chunks of 512 elements held in VGPRs. The
 // workgroup's rows share one LDS copy of gamma.
 
-template <int NC, int ELEM, int RND, bool GAMMA>
+template <int NC, int ELEM, int RND, bool GAMMA, int STAT>
 __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
   __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
   __shared__ uint32_t sc_lds[kRowsPerBlock][NC * 4];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
   const bool live = row < A.T;
   const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
@@ -554,9 +636,9 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
   if (!live) return;
   uint32_t* sc = sc_lds[wave];
   if (!GAMMA)
-    mxnorm_row_reg<NC, ELEM, RND, G_NONE>(A, raw, g_lds, row, lane, sc);
+    mxnorm_row_reg<NC, ELEM, RND, G_NONE, STAT>(A, raw, g_lds, row, lane, sc);
   else
-    mxnorm_row_reg<NC, ELEM, RND, G_GAIN>(A, raw, g_lds, row, lane, sc);
+    mxnorm_row_reg<NC, ELEM, RND, G_GAIN, STAT>(A, raw, g_lds, row, lane, sc);
 }
 
 constexpr int kMaxLdsRows = 16;  // wavefronts (rows) per workgroup of the LDS-staged variant
@@ -568,11 +650,11 @@ constexpr int kMaxLdsRows = 16;  // wavefronts (rows) per workgroup of the LDS-s
 // stays bf16 in LDS here (it is widened per use, to the same fp32 values).
 // Dynamic LDS: [rows][nchunks * 64] uint4 row slices, gamma [nchunks * 64]
 // uint4, then [rows][nchunks * 4] dwords of scales.
-template <int ELEM, int RND, bool GAMMA>
+template <int ELEM, int RND, bool GAMMA, int STAT>
 __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArgs A, int nchunks, int rows) {
   extern __shared__ uint4 lds_rows[];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   const int64_t row = (int64_t)blockIdx.x * rows + wave;
   const bool live = row < A.T;
   const uint16_t* xr = A.x + (live ? row : 0) * A.ldx;
@@ -603,13 +685,24 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   auto mb = [&](int c) { return quad_max_u32(absmax_bits8(slice[c * kWave + lane])); };
-  uint32_t rmax = 0;
-  for (int c = 0; c < nchunks; ++c) rmax = max(rmax, mb(c));
-  rmax = max_over_quads(rmax);
-  const float inv = row_normaliser<0>(nchunks, mb, rmax, A.pmode, A.p, A.Kf);
+  float inv;
+  if constexpr (STAT == S_RMS) {
+    float s = 0.0f;
+    for (int c = 0; c < nchunks; ++c)
+      if (c * kChunk + dl < A.D) s = sumsq8(slice[c * kWave + lane], s);
+    inv = rms_normaliser(s, A.Df, A.eps);
+  } else {
+    auto lane_max = [&]() {
+      uint32_t m = 0;
+      for (int c = 0; c < nchunks; ++c) m = max(m, mb(c));
+      return m;
+    };
+    inv = row_normaliser<0>(nchunks, mb, lane_max, A.pmode, A.p, A.Kf);
+  }
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
 
   const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
+  uint8_t* crow = code_row<ELEM>(A.codes, nrow);
   float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c = 0; c < nchunks; ++c) {
     const int d = c * kChunk + dl;
@@ -617,10 +710,10 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
       const uint4 xb = slice[c * kWave + lane];
       uint32_t code;
       if (!GAMMA) {
-        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, nrow + d, xb, g, mb(c), inv);
+        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, xb, g, mb(c), inv);
       } else {
         unpack8(g_lds[c * kWave + lane], g);
-        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, nrow + d, xb, g, 0u, inv);
+        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, xb, g, 0u, inv);
       }
       if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
     }
@@ -669,14 +762,6 @@ __device__ __forceinline__ void rms_chunk_out(const RmsArgs& A, int64_t row, int
   *reinterpret_cast<uint4*>(A.y + (uint64_t)row * (uint64_t)A.D + (uint64_t)d) = o;
 }
 
-__device__ __forceinline__ float sumsq8(const uint4& r, float s) {
-  float v[8];
-  unpack8(r, v);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s = __builtin_fmaf(v[j], v[j], s);
-  return s;
-}
-
 // Row in registers (D <= NC * 512).
 template <int NC, bool GAMMA>
 __global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
@@ -692,8 +777,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
 #pragma unroll
   for (int c = 0; c < NC; ++c)
     if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
-  s = sum_over_wave(s);
-  const float inv = 1.0f / sqrtf(s / A.Df + A.eps);
+  const float inv = rms_normaliser(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -713,8 +797,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_wide_kernel(RmsArgs A, int n
   float s = 0.0f;
   for (int c = 0; c < nchunks; ++c)
     if (c * kChunk + dl < A.D) s = sumsq8(load16(xr + c * kChunk + dl), s);
-  s = sum_over_wave(s);
-  const float inv = 1.0f / sqrtf(s / A.Df + A.eps);
+  const float inv = rms_normaliser(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
   for (int c = 0; c < nchunks; ++c) {
     const int d = c * kChunk + dl;
@@ -764,8 +847,9 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
       const uint32_t code = e8m0_code<ELEM>(__uint_as_float(mbits << 16));
       float v[8];
       unpack8(raw[u], v);
-      const uint64_t n = (uint64_t)rows[u] * (uint64_t)A.D + (uint64_t)ds[u];
-      encode_store8<ELEM, RND>(A.codes, n, v, code, A.rng);
+      const uint64_t nrow = (uint64_t)rows[u] * (uint64_t)A.D;
+      encode_store8<ELEM, RND>(code_row<ELEM>(A.codes, nrow), (uint32_t)ds[u], nrow + ds[u], v,
+                               code, A.rng);
       if ((lane & 3) == 0) {
         if (A.sc_vec)
           put_scale(sc, u * 16 + (lane >> 2), code);
@@ -790,20 +874,20 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
     if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP; \
   } while (0)
 
-template <int NC, int ELEM, int RND, bool GAMMA>
+template <int NC, int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_reg(const NormArgs& A, hipStream_t s) {
   const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL((mxnorm_reg_kernel<NC, ELEM, RND, GAMMA>), dim3(grid), dim3(kThreads), 0, s, A);
+  hipLaunchKernelGGL((mxnorm_reg_kernel<NC, ELEM, RND, GAMMA, STAT>), dim3(grid), dim3(kThreads), 0, s, A);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
 
-template <int ELEM, int RND, bool GAMMA>
+template <int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status dispatch_mxnorm_reg(const NormArgs& A, int nc, hipStream_t s) {
   switch (nc) {
 #define MXQ_CASE(N) \
   case N:           \
-    return launch_mxnorm_reg<N, ELEM, RND, GAMMA>(A, s);
+    return launch_mxnorm_reg<N, ELEM, RND, GAMMA, STAT>(A, s);
     MXQ_CASE(1) MXQ_CASE(2) MXQ_CASE(3) MXQ_CASE(4) MXQ_CASE(5) MXQ_CASE(6) MXQ_CASE(7)
     MXQ_CASE(8) MXQ_CASE(9) MXQ_CASE(10) MXQ_CASE(11) MXQ_CASE(12) MXQ_CASE(13) MXQ_CASE(14)
     MXQ_CASE(15) MXQ_CASE(16)
@@ -815,7 +899,7 @@ mxq_status dispatch_mxnorm_reg(const NormArgs& A, int nc, hipStream_t s) {
 
 constexpr size_t kLdsPerBlockMax = 160 * 1024;  // gfx950 LDS per workgroup
 
-template <int ELEM, int RND, bool GAMMA>
+template <int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
   // per row: the bf16 row and its scale bytes; per workgroup: bf16 gamma.
   // Rows per workgroup: the count that keeps the most rows resident per CU
@@ -835,7 +919,7 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
     }
   }
   const size_t bytes = per_row * rows + g_bytes;
-  auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA>;
+  auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA, STAT>;
   if (bytes > 64 * 1024 &&
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)bytes) != hipSuccess)
@@ -846,13 +930,23 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
   return MXQ_OK;
 }
 
-template <int ELEM, int RND>
+template <int ELEM, int RND, int STAT>
 mxq_status dispatch_mxnorm(const NormArgs& A, bool gamma, bool lds, int nc, hipStream_t s) {
   if (lds)
-    return gamma ? launch_mxnorm_lds<ELEM, RND, true>(A, nc, s)
-                 : launch_mxnorm_lds<ELEM, RND, false>(A, nc, s);
-  return gamma ? dispatch_mxnorm_reg<ELEM, RND, true>(A, nc, s)
-               : dispatch_mxnorm_reg<ELEM, RND, false>(A, nc, s);
+    return gamma ? launch_mxnorm_lds<ELEM, RND, true, STAT>(A, nc, s)
+                 : launch_mxnorm_lds<ELEM, RND, false, STAT>(A, nc, s);
+  return gamma ? dispatch_mxnorm_reg<ELEM, RND, true, STAT>(A, nc, s)
+               : dispatch_mxnorm_reg<ELEM, RND, false, STAT>(A, nc, s);
+}
+
+template <int STAT>
+mxq_status dispatch_norm_cast(const NormArgs& A, mxq_elem elem, mxq_round rnd, bool gamma,
+                              bool lds, int nc, hipStream_t s) {
+  if (elem == MXQ_E4M3)
+    return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E4M3, MXQ_SR, STAT>(A, gamma, lds, nc, s)
+                         : dispatch_mxnorm<MXQ_E4M3, MXQ_RNE, STAT>(A, gamma, lds, nc, s);
+  return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E2M1, MXQ_SR, STAT>(A, gamma, lds, nc, s)
+                       : dispatch_mxnorm<MXQ_E2M1, MXQ_RNE, STAT>(A, gamma, lds, nc, s);
 }
 
 template <int NC, bool GAMMA>
@@ -924,6 +1018,43 @@ SrStream make_stream(const mxq_rng* rng) {
   return s;
 }
 
+// Validation and launch shared by the single-pass normalise-and-cast entry
+// points; the statistic's own argument (p or eps) is checked by the caller.
+template <int STAT>
+mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T, int64_t D,
+                     float p, float eps, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
+                     uint32_t flags, uint8_t* codes, uint8_t* scales, float* inv_out,
+                     void* stream) {
+  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  if ((flags & MXQ_FLAG_FORCE_REG) && (flags & MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
+  if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
+  if (T == 0) return MXQ_OK;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
+  if (inv_out != nullptr && !aligned(inv_out, 4)) return MXQ_ERR_ALIGN;
+
+  NormArgs A;
+  A.x = x;
+  A.gamma = gamma;
+  A.codes = codes;
+  A.scales = scales;
+  A.inv_out = inv_out;
+  A.ldx = ldx;
+  A.T = T;
+  A.D = (int)D;
+  A.K = (int)(D / 32);
+  A.Kf = (float)(D / 32);
+  A.p = p;
+  A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
+  A.Df = (float)D;
+  A.eps = eps;
+  A.sc_vec = (A.K % 4 == 0) && aligned(scales, 4);
+  A.rng = make_stream(rng);
+  const int nc = (int)((D + kChunk - 1) / kChunk);
+  const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
+  return dispatch_norm_cast<STAT>(A, elem, rnd, gamma != nullptr, lds, nc, (hipStream_t)stream);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI
@@ -937,38 +1068,20 @@ mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int
   mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
   if (st != MXQ_OK) return st;
   if (!(p > 0.0f)) return MXQ_ERR_ARG;  // also rejects NaN
-  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
-  if ((flags & MXQ_FLAG_FORCE_REG) && (flags & MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
-  if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
-  if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
-  if (T == 0) return MXQ_OK;
-  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
-  if (inv_norm != nullptr && !aligned(inv_norm, 4)) return MXQ_ERR_ALIGN;
+  return norm_cast<S_PMEAN>(x, ldx, gamma, T, D, p, 0.0f, elem, rnd, rng, flags, codes, scales,
+                            inv_norm, stream);
+}
 
-  NormArgs A;
-  A.x = x;
-  A.gamma = gamma;
-  A.codes = codes;
-  A.scales = scales;
-  A.inv_out = inv_norm;
-  A.ldx = ldx;
-  A.T = T;
-  A.D = (int)D;
-  A.K = (int)(D / 32);
-  A.Kf = (float)(D / 32);
-  A.p = p;
-  A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
-  A.sc_vec = (A.K % 4 == 0) && aligned(scales, 4);
-  A.rng = make_stream(rng);
-  const int nc = (int)((D + kChunk - 1) / kChunk);
-  const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
-  hipStream_t s = (hipStream_t)stream;
-  const bool g = gamma != nullptr;
-  if (elem == MXQ_E4M3)
-    return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E4M3, MXQ_SR>(A, g, lds, nc, s)
-                         : dispatch_mxnorm<MXQ_E4M3, MXQ_RNE>(A, g, lds, nc, s);
-  return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E2M1, MXQ_SR>(A, g, lds, nc, s)
-                       : dispatch_mxnorm<MXQ_E2M1, MXQ_RNE>(A, g, lds, nc, s);
+mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                                    int64_t T, int64_t D, float eps, mxq_elem elem,
+                                    mxq_round rnd, const mxq_rng* rng, uint32_t flags,
+                                    uint8_t* codes, uint8_t* scales, float* inv_rms,
+                                    void* stream) {
+  mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
+  if (st != MXQ_OK) return st;
+  if (!(eps >= 0.0f) || isinf(eps)) return MXQ_ERR_ARG;
+  return norm_cast<S_RMS>(x, ldx, gamma, T, D, 2.0f, eps, elem, rnd, rng, flags, codes, scales,
+                          inv_rms, stream);
 }
 
 mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,

@@ -88,6 +88,9 @@ def lib():
             L.orc_rmsnorm_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64, u64,
                                              i64, vp, vp, vp, vp, vp]
             L.orc_rmsnorm_mxcast.restype = i32
+            L.orc_rmsnorm_fused_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64,
+                                                   u64, i64, vp, vp, vp, vp]
+            L.orc_rmsnorm_fused_mxcast.restype = i32
             _lib = L
     return _lib
 
@@ -145,7 +148,7 @@ def code_bytes(elem: int, D: int) -> int:
 
 
 # --------------------------------------------------------------------------
-# the three operations
+# the operations
 # --------------------------------------------------------------------------
 
 def mxcast(x, elem="e4m3", rnd="rne", seed=0, offset=0, row_base=0, threads=1):
@@ -211,6 +214,30 @@ def rmsnorm_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offs
             _ptr(y[r0:]), _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return y, codes, scales, inv
+
+
+def rmsnorm_fused_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offset=0,
+                         inv_inject=None, row_base=0, threads=1):
+    """Single-pass exact-RMS normalise and MX cast (y not rounded to bf16).
+    Returns (codes, scales, inv float64 [T])."""
+    L = lib()
+    e, r = ELEM[elem], RND[rnd]
+    x, T, D, ldx = _rows_view(as_bf16_bits(x))
+    g = None if gamma is None else np.ascontiguousarray(as_bf16_bits(gamma).reshape(-1))
+    inj = None if inv_inject is None else np.ascontiguousarray(
+        np.asarray(inv_inject, dtype=np.float32).reshape(-1))
+    codes = np.zeros((T, code_bytes(e, D)), np.uint8)
+    scales = np.zeros((T, D // 32), np.uint8)
+    inv = np.zeros(T, np.float64)
+    xb = x.ctypes.data
+
+    def job(r0, r1):
+        return lambda: L.orc_rmsnorm_fused_mxcast(
+            ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(eps), e, r,
+            seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
+            _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
+    _run([job(a, b) for a, b in _split(T, threads)], threads)
+    return codes, scales, inv
 
 
 # --------------------------------------------------------------------------

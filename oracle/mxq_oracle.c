@@ -1,6 +1,6 @@
 /*
  * mxq_oracle.c - plain, slow, scalar CPU oracle for MXNorm, RMSNorm -> MXCast
- * and MXCast.
+ * (two-pass, and the single-pass exact-RMS comparator) and MXCast.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this. It shares no code, header, table or constant
@@ -47,7 +47,8 @@
  *    G == 0 gives a zero normaliser; a row holding a NaN or Inf gives a NaN
  *    normaliser.
  *  - RMSNorm: y = gamma * x / sqrt(mean(x^2) + eps), rounded once to bf16 (the
- *    separate normalisation op emits a bf16 tensor).
+ *    separate normalisation op emits a bf16 tensor). The single-pass
+ *    comparator uses the same statistic but casts y without the bf16 step.
  *
  * Two modes for the normalising ops:
  *  (R) reference: statistic and normaliser in fp64, y in fp64, cast directly.
@@ -444,6 +445,49 @@ int orc_rmsnorm_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, in
       uint16_t b = orc_bf16_rne(yd);
       ybf[t * D + d] = b;
       y[d] = orc_bf16_to_f64(b);
+    }
+    mxcast_row_f64(y, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * K);
+    store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));
+  }
+  free(y);
+  free(cu);
+  return 0;
+}
+
+/* Single-pass exact-RMS comparator: RMSNorm's statistic over all D elements
+ * (MXNorm page, §1.1) in place of MXNorm's power mean, with y cast straight to
+ * MX in the same pass as MXNorm does (§2.1), so y is never rounded to bf16.
+ * (R): inv = 1/sqrt(mean(x^2) + eps) and y = x*gamma*inv in fp64. (I): the
+ * injected fp32 inv and y = RN32(RN32(x*gamma)*inv). Outputs as orc_mxnorm. */
+int orc_rmsnorm_fused_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                             int64_t D, double eps, int elem, int rnd, uint64_t seed,
+                             uint64_t offset, int64_t row_base, const float* inv_inject,
+                             uint8_t* codes, uint8_t* scales, double* inv_out) {
+  int rc = check_args(T, D, elem, rnd, row_base);
+  if (rc) return rc;
+  if (!(eps >= 0)) return 5;
+  const int64_t K = D / 32;
+  double* y = (double*)malloc(sizeof(double) * (size_t)D);
+  uint8_t* cu = (uint8_t*)malloc((size_t)D);
+  if (!y || !cu) { free(y); free(cu); return 6; }
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ldx;
+    double inv;
+    if (inv_inject) {
+      inv = (double)inv_inject[t];
+    } else {
+      double s = 0;
+      for (int64_t d = 0; d < D; ++d) {
+        double xi = orc_bf16_to_f64(xr[d]);
+        s += xi * xi;
+      }
+      inv = 1.0 / sqrt(s / (double)D + eps);
+    }
+    if (inv_out) inv_out[t] = inv;
+    for (int64_t d = 0; d < D; ++d) {
+      double xi = orc_bf16_to_f64(xr[d]);
+      double gi = gamma ? orc_bf16_to_f64(gamma[d]) : 1.0;
+      y[d] = inv_inject ? (double)rn32((double)rn32(xi * gi) * inv) : xi * gi * inv;
     }
     mxcast_row_f64(y, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * K);
     store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));

@@ -65,6 +65,15 @@ def rms(**kw):
                                   a["stream"])
 
 
+def rms_fused(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, T=8, D=4096, eps=1e-5, elem=0, rnd=0, rng=None,
+             flags=0, codes=A16, scales=A16, inv=None, stream=None)
+    a.update(kw)
+    return mxq.rmsnorm_mxcast_fused_fwd(a["x"], a["ldx"], a["gamma"], a["T"], a["D"], a["eps"],
+                                        a["elem"], a["rnd"], a["rng"], a["flags"], a["codes"],
+                                        a["scales"], a["inv"], a["stream"])
+
+
 def cast(**kw):
     a = dict(x=A16, ldx=4096, T=8, D=4096, elem=0, rnd=0, rng=None, codes=A16, scales=A16, stream=None)
     a.update(kw)
@@ -72,7 +81,7 @@ def cast(**kw):
                           a["codes"], a["scales"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [norm, rms, cast])
+@pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])
 def test_shape_errors(call):
     assert call(D=0) == mxq.MXQ_ERR_SHAPE
     assert call(D=-32) == mxq.MXQ_ERR_SHAPE
@@ -81,7 +90,7 @@ def test_shape_errors(call):
     assert call(ldx=2048) == mxq.MXQ_ERR_SHAPE          # ldx < D
 
 
-@pytest.mark.parametrize("call", [norm, rms, cast])
+@pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])
 def test_null_and_alignment_errors(call):
     assert call(x=None) == mxq.MXQ_ERR_NULL
     assert call(codes=None) == mxq.MXQ_ERR_NULL
@@ -91,7 +100,7 @@ def test_null_and_alignment_errors(call):
     assert call(ldx=4100) == mxq.MXQ_ERR_ALIGN          # rows not 16-byte aligned
 
 
-@pytest.mark.parametrize("call", [norm, rms, cast])
+@pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])
 def test_format_rounding_rng_errors(call):
     assert call(elem=2) == mxq.MXQ_ERR_ARG
     assert call(rnd=5) == mxq.MXQ_ERR_ARG
@@ -110,6 +119,17 @@ def test_mxnorm_argument_errors():
     assert norm(inv_norm=A16 + 2) == mxq.MXQ_ERR_ALIGN
 
 
+def test_rms_fused_argument_errors():
+    assert rms_fused(eps=-1e-6) == mxq.MXQ_ERR_ARG
+    assert rms_fused(eps=float("nan")) == mxq.MXQ_ERR_ARG
+    assert rms_fused(eps=float("inf")) == mxq.MXQ_ERR_ARG
+    assert rms_fused(flags=3) == mxq.MXQ_ERR_ARG
+    assert rms_fused(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
+    assert rms_fused(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
+    assert rms_fused(gamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert rms_fused(inv=A16 + 2) == mxq.MXQ_ERR_ALIGN
+
+
 def test_rmsnorm_argument_errors():
     assert rms(eps=-1e-6) == mxq.MXQ_ERR_ARG
     assert rms(eps=float("nan")) == mxq.MXQ_ERR_ARG
@@ -119,7 +139,7 @@ def test_rmsnorm_argument_errors():
     assert rms(gamma=A8) == mxq.MXQ_ERR_ALIGN
 
 
-@pytest.mark.parametrize("call", [norm, rms, cast])
+@pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])
 def test_empty_input_is_a_no_op(call):
     # T == 0 returns before any pointer is read or kernel launched
     assert call(T=0, x=None, codes=None, scales=None) == mxq.MXQ_OK

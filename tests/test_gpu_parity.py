@@ -88,6 +88,25 @@ def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what=""):
     compare_reference(np_(codes[r0:r1]), np_(scales[r0:r1]), rc, rs, elem, what)
 
 
+def check_rms_fused(x, g, eps=1e-5, elem="e4m3", rnd="rne", flags=0, rows=None, what="",
+                    ref=True):
+    codes, scales, inv = mxq.rmsnorm_mxcast_fused(x, g, eps, elem, rnd, SEED, OFFSET, flags)
+    torch.cuda.synchronize()
+    r0, r1 = (0, x.shape[0]) if rows is None else rows
+    xs, gs = host(x[r0:r1]), host(g)
+    c, s, i = np_(codes[r0:r1]), np_(scales[r0:r1]), np_(inv[r0:r1])
+    oc, os_, _ = oracle.rmsnorm_fused_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, inv_inject=i,
+                                             row_base=r0, threads=THREADS)
+    assert_bits(s, os_, f"{what} scales (I)")
+    assert_bits(c, oc, f"{what} codes (I)")
+    if ref:
+        rc, rs, rinv = oracle.rmsnorm_fused_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET,
+                                                   row_base=r0, threads=THREADS)
+        check_normaliser(i, rinv, what)
+        compare_reference(c, s, rc, rs, elem, what)
+    return c, s, i
+
+
 # ---------------------------------------------------------------- MXCast codec
 
 def _all_bf16_rows(width):
@@ -252,6 +271,60 @@ def test_two_pass_formats(elem, rnd):
                    what=f"two-pass {elem} {rnd}")
 
 
+# ---------------------------------------------------------------- single-pass exact-RMS comparator
+
+@pytest.mark.parametrize("D", [32, 96, 4096, 8192, 8224, 14336])
+@pytest.mark.parametrize("gamma", [False, True])
+def test_rms_fused_shapes(D, gamma):
+    x = workloads.random_rows(5, D, seed=91 + D, device=DEV)
+    x[2, : min(D, 64)] *= 30.0
+    g = workloads.random_gamma(D, seed=92, device=DEV) if gamma else None
+    check_rms_fused(x, g, what=f"rms-fused D={D}")
+
+
+@pytest.mark.parametrize("elem,rnd", [("e4m3", "sr"), ("e2m1", "rne"), ("e2m1", "sr")])
+@pytest.mark.parametrize("T", [1, 7, 64])
+def test_rms_fused_formats(elem, rnd, T):
+    x = workloads.random_rows(T, 1024, seed=93 + T, device=DEV)
+    check_rms_fused(x, workloads.random_gamma(1024, seed=94, device=DEV), elem=elem, rnd=rnd,
+                    what=f"rms-fused {elem} {rnd} T={T}")
+
+
+@pytest.mark.parametrize("D", [256, 4096, 8192])
+def test_rms_fused_register_and_lds_variants_are_bit_identical(D):
+    x = workloads.random_rows(37, D, seed=95 + D, device=DEV)
+    g = workloads.random_gamma(D, seed=96, device=DEV)
+    a = mxq.rmsnorm_mxcast_fused(x, g, flags=mxq.MXQ_FLAG_FORCE_REG)
+    b = mxq.rmsnorm_mxcast_fused(x, g, flags=mxq.MXQ_FLAG_FORCE_LDS)
+    torch.cuda.synchronize()
+    assert same_outputs(a, b)
+
+
+def test_rms_fused_special_rows():
+    x = workloads.random_rows(6, 512, seed=97).clone()
+    x[0] = 0.0
+    x[1, 17] = float("nan")
+    x[2, 100] = float("inf")
+    x[3] = x[3] * 1e-30              # tiny row: eps dominates
+    x[4, :32] = 0.0
+    c, s, i = check_rms_fused(x.to(DEV), None, what="rms-fused special")
+    assert math.isnan(i[1]) and (s[1] == 255).all()
+    assert i[2] == 0 and s[2, 3] == 255 and (s[2, :3] == 0).all()
+    check_rms_fused(x.to(DEV), workloads.random_gamma(512, seed=98, device=DEV),
+                    what="rms-fused special gamma")
+
+
+def test_rms_fused_statistic_matches_two_pass_bitwise():
+    # both RMS paths sum the squares in the same order: identical inv_rms
+    for D in (4096, 8224):
+        x = workloads.random_rows(64, D, seed=99 + D, device=DEV)
+        g = workloads.random_gamma(D, seed=100, device=DEV)
+        _, _, inv_f = mxq.rmsnorm_mxcast_fused(x, g)
+        _, _, inv_t, _ = mxq.rmsnorm_mxcast(x, g)
+        torch.cuda.synchronize()
+        assert torch.equal(inv_f, inv_t), D
+
+
 # ---------------------------------------------------------------- the five workloads
 
 def test_workload_llama3_8b_full():
@@ -259,6 +332,7 @@ def test_workload_llama3_8b_full():
     for p in (1.0, 2.0):
         check_mxnorm(x, g, p, what=f"llama3-8b p={p}")
     check_two_pass(x, g, what="llama3-8b two-pass")
+    check_rms_fused(x, g, what="llama3-8b rms-fused")
 
 
 def test_workload_longseq_sampled_and_variants_identical():

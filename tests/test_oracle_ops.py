@@ -233,3 +233,80 @@ def test_two_pass_and_fused_agree_on_constant_rows(orc):
     a = orc.mxnorm(x, g, 2.0)
     b = orc.rmsnorm_mxcast(x, g, eps=0.0)
     assert np.array_equal(a[0], b[1]) and np.array_equal(a[1], b[2])
+
+
+# ---------------------------------------------------------------- single-pass exact-RMS comparator
+
+def test_rms_fused_reference_mode_matches_torch(orc):
+    # y = RMSNorm(x) in fp64 (torch), cast straight to MX with no bf16 step
+    x, g = workloads.make_inputs("llama3_8b_preattn", rows=48)
+    eps = 1e-5
+    codes, scales, inv = orc.rmsnorm_fused_mxcast(x, g, eps)
+    ref = torch.nn.functional.rms_norm(x.double(), (x.shape[1],), weight=g.double(), eps=eps)
+    want_c, want_s = mx_reference(ref.numpy(), "e4m3")
+    assert (codes == want_c).all() and (scales == want_s).all()
+    rms = np.sqrt((bf16_to_f64(x) ** 2).mean(1) + eps)
+    assert np.allclose(inv, 1 / rms, rtol=1e-14)
+    # same statistic as the two-pass path
+    _, _, _, inv_tp = orc.rmsnorm_mxcast(x, g, eps)
+    assert np.array_equal(inv, inv_tp)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_rms_fused_injected_mode_follows_fp32_order(orc, elem):
+    x, g = workloads.make_inputs("llama3_8b_preattn", rows=16)
+    _, _, inv64 = orc.rmsnorm_fused_mxcast(x, g, 1e-5)
+    inv32 = (inv64 * (1 - 5e-7)).astype(np.float32)    # a perturbed fp32 normaliser
+    codes, scales, used = orc.rmsnorm_fused_mxcast(x, g, 1e-5, elem, inv_inject=inv32)
+    assert (used == inv32.astype(np.float64)).all()
+    y32 = (x.float() * g.float()[None, :]) * torch.from_numpy(inv32)[:, None]
+    want_c, want_s = mx_reference(y32.double().numpy(), elem)
+    got_c = unpack_e2m1(codes) if elem == "e2m1" else codes
+    assert (got_c == want_c).all() and (scales == want_s).all()
+
+
+def test_rms_fused_equals_mxnorm_on_constant_rows(orc):
+    # |x_i| = a for every i: RMS = a = G for every p, so with eps = 0 the
+    # comparator and MXNorm quantise the same y = +-gamma
+    rng = np.random.default_rng(53)
+    x = torch.from_numpy(np.where(rng.random((6, 512)) < 0.5, -1.25, 1.25)).to(torch.bfloat16)
+    g = workloads.random_gamma(512, seed=54)
+    for p in (1.0, 2.0, math.inf):
+        a = orc.mxnorm(x, g, p)
+        b = orc.rmsnorm_fused_mxcast(x, g, eps=0.0)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
+
+
+def test_rms_fused_differs_from_two_pass_only_by_the_bf16_step(orc):
+    # the two-pass path rounds y to bf16 before the cast; the comparator does
+    # not: the dequantised outputs differ by at most one element ulp, on few
+    # elements, and agree wherever y is already a bf16 value
+    x, g = workloads.make_inputs("llama3_8b_preattn", rows=32)
+    c1, s1, inv1 = orc.rmsnorm_fused_mxcast(x, g, 1e-5)
+    _, c2, s2, inv2 = orc.rmsnorm_mxcast(x, g, 1e-5)
+    assert np.array_equal(inv1, inv2)
+    tab = torch_e4m3_table()
+    dq = lambda c, s: tab[c] * np.ldexp(1.0, s.astype(np.int64).repeat(32, axis=1) - 127)
+    a, b = dq(c1, s1), dq(c2, s2)
+    diff = a != b
+    # double rounding (8 then 3 mantissa bits) moves about 2^-5 of the elements
+    assert 0.01 < diff.mean() < 0.05
+    big = np.maximum(np.abs(a), np.abs(b))[diff]
+    s = np.maximum(s1, s2).astype(np.int64).repeat(32, axis=1)[diff] - 127
+    ulp = np.maximum(np.ldexp(1.0, np.floor(np.log2(big)).astype(np.int64) - 3),
+                     np.ldexp(1.0, s - 9))                  # E4M3 ulp, subnormal floor
+    assert (np.abs(a - b)[diff] <= ulp).all()
+
+
+def test_rms_fused_special_rows(orc):
+    x = workloads.random_rows(4, 128, seed=55).clone()
+    x[0] = 0.0
+    x[1, 17] = float("nan")
+    x[2, 100] = float("inf")          # sum of squares Inf: inv = 0, Inf * 0 is NaN
+    codes, scales, inv = orc.rmsnorm_fused_mxcast(x, None, eps=1e-5)
+    assert inv[0] == 1 / math.sqrt(1e-5) and (scales[0] == 0).all() and (codes[0] == 0).all()
+    assert math.isnan(inv[1]) and (scales[1] == 255).all() and (codes[1] == 0x7F).all()
+    assert inv[2] == 0 and scales[2, 3] == 255 and (codes[2, 96:] == 0x7F).all()
+    assert (scales[2, :3] == 0).all() and (codes[2, :96] & 0x7F == 0).all()
+    assert np.isfinite(inv[3])
