@@ -173,17 +173,25 @@ __device__ __forceinline__ float pmean_finish(float s, int pmode, float p, float
 // Sum of the power-mean terms of this lane's chunks, in chunk order, of the
 // block maxima scaled by 2^shift. NCT > 0 gives a compile-time (unrolled)
 // chunk count, NCT == 0 the runtime count.
-template <int NCT, class BlockMax>
-__device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift, int pmode, float p) {
+template <int NCT, int PM, class BlockMax>
+__device__ __forceinline__ float lane_terms_p(int nchunks, BlockMax mb, int shift, float p) {
   float s = 0.0f;
   if constexpr (NCT > 0) {
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), pmode, p);
+    for (int c = 0; c < NCT; ++c) s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), PM, p);
   } else {
     for (int c = 0; c < nchunks; ++c)
-      s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), pmode, p);
+      s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), PM, p);
   }
   return s;
+}
+
+// The power mode is tested once, outside the term loop.
+template <int NCT, class BlockMax>
+__device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift, int pmode, float p) {
+  if (pmode == P_TWO) return lane_terms_p<NCT, P_TWO>(nchunks, mb, shift, p);
+  if (pmode == P_ONE) return lane_terms_p<NCT, P_ONE>(nchunks, mb, shift, p);
+  return lane_terms_p<NCT, P_GEN>(nchunks, mb, shift, p);
 }
 
 // Normaliser 1/G of a row from its block maxima (bf16 bit patterns, one per
@@ -267,31 +275,39 @@ struct SrStream {
 // ------------------------------------------------------------------ encode
 
 // 8 values y (not yet divided by the scale) -> 8 E4M3 codes, RNE, saturating.
-__device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], uint32_t code) {
-  if (code == 0xFFu) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+// A non-finite block (code 0xFF) is encoded with a harmless stand-in scale
+// and then replaced by NaN codes with a select, so the common path has no
+// branch.
+__device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], uint32_t code_in) {
+  const bool bad = code_in == 0xFFu;
+  const uint32_t code = bad ? 127u : code_in;
   const float scale = __uint_as_float(code << 23);                  // 2^(code-127)
   const float lim = __uint_as_float(((code + 8u) << 23) | 0x00600000u); // 448 * 2^(code-127)
   float w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) w[j] = __builtin_amdgcn_fmed3f(y[j], -lim, lim);
-  short2_t a = {0, 0}, b = {0, 0};
+  // each convert writes one half of its destination and keeps the other, so
+  // the starting value is irrelevant (both halves are written): reuse w bits
+  short2_t a = __builtin_bit_cast(short2_t, w[0]), b = __builtin_bit_cast(short2_t, w[4]);
   a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, w[0], w[1], scale, false);
   a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, w[2], w[3], scale, true);
   b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[4], w[5], scale, false);
   b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[6], w[7], scale, true);
-  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+  const uint32_t lo = __builtin_bit_cast(uint32_t, a), hi = __builtin_bit_cast(uint32_t, b);
+  return make_uint2(bad ? 0x7F7F7F7Fu : lo, bad ? 0x7F7F7F7Fu : hi);
 }
 
 // 8 values -> 8 E2M1 codes packed in one word (element 2j in the low nibble).
-__device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], uint32_t code) {
-  if (code == 0xFFu) return 0x77777777u;
+__device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], uint32_t code_in) {
+  const bool bad = code_in == 0xFFu;  // as for E4M3: select, no branch
+  const uint32_t code = bad ? 127u : code_in;
   const float scale = __uint_as_float(code << 23);
-  uint32_t q = 0;
+  uint32_t q = __float_as_uint(y[0]);  // all four bytes are written below
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[0], y[1], scale, 0);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[2], y[3], scale, 1);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[4], y[5], scale, 2);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[6], y[7], scale, 3);
-  return q;
+  return bad ? 0x77777777u : q;
 }
 
 // Stochastic rounding of v (already divided by the scale, |v| < 2^(emax+1)):
@@ -512,7 +528,7 @@ __device__ __forceinline__ bool nonfinite_bf16x8(const uint4& r) {
   auto bad = [](uint32_t w) {
     return ((w & 0x7F80u) == 0x7F80u) || (((w >> 16) & 0x7F80u) == 0x7F80u);
   };
-  return bad(r.x) || bad(r.y) || bad(r.z) || bad(r.w);
+  return bad(r.x) | bad(r.y) | bad(r.z) | bad(r.w);  // no short-circuit branches
 }
 
 // gamma [D] goes to LDS as fp32, laid out [chunk][half][lane] (float4 each),
@@ -571,7 +587,11 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
   const int dl = lane * 8;
   uint32_t mb[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) mb[c] = quad_max_u32(c * kChunk + dl < A.D ? absmax_bits8(raw[c]) : 0u);
+  for (int c = 0; c < NC; ++c) {
+    // every lane computes (the loads are clamped in bounds), then masks: no branch
+    const uint32_t valid = 0u - (uint32_t)(c * kChunk + dl < A.D);
+    mb[c] = quad_max_u32(absmax_bits8(raw[c]) & valid);
+  }
   float inv;
   if constexpr (STAT == S_RMS) {
     float s = 0.0f;
