@@ -1,0 +1,129 @@
+"""Time every workload's hot-path call through the C ABI on one GPU.
+
+    python -m norm_mx_quantisation_amd.timing [--steps K] [--only NAME[,NAME]]
+
+For each case: inputs resident in HBM, R rotating buffer sets of at least
+1 GB in total (so the 256 MB MALL cannot serve a call), W warm-up launches,
+then K launches bracketed by HIP events on the launch stream. Prints one line
+per case with the mean time per launch and the algorithmic bandwidth (bytes
+the operation must move: read x, write codes and scales; the two-pass path
+also writes and reads its bf16 intermediate). Run it under
+`rocprofv3 --kernel-trace --stats` for per-kernel durations.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import sys
+
+import norm_mx_quantisation_amd as mxq
+from norm_mx_quantisation_amd import workloads
+
+HBM_PEAK_GBS = 8000.0
+
+# (case, workload, operation, options)
+CASES = (
+    ("llama3_8b_preattn mxnorm p=2", "llama3_8b_preattn", "mxnorm", {"p": 2.0}),
+    ("llama3_8b_preattn mxnorm p=1", "llama3_8b_preattn", "mxnorm", {"p": 1.0}),
+    ("llama3_8b_preattn mxnorm p=2 gamma folded", "llama3_8b_preattn", "mxnorm",
+     {"p": 2.0, "gamma": False}),
+    ("llama3_8b_preattn rms single-pass", "llama3_8b_preattn", "rms_fused", {}),
+    ("llama3_8b_preattn two-pass", "llama3_8b_preattn", "two_pass", {}),
+    ("longseq_t3 mxnorm register rows", "longseq_t3", "mxnorm",
+     {"flags": mxq.MXQ_FLAG_FORCE_REG}),
+    ("longseq_t3 mxnorm LDS rows", "longseq_t3", "mxnorm", {"flags": mxq.MXQ_FLAG_FORCE_LDS}),
+    ("swiglu_downproj mxcast rne", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_RNE}),
+    ("swiglu_downproj mxcast sr", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_SR}),
+    ("mxfp4 mxnorm e2m1", "mxfp4", "mxnorm", {"elem": mxq.MXQ_E2M1}),
+)
+
+
+def algorithmic_bytes(op, T, D, elem):
+    code = D // 2 if elem == mxq.MXQ_E2M1 else D
+    if op == "two_pass":
+        return T * (2 * D + 2 * D + 2 * D + code + D // 32)
+    return T * (2 * D + code + D // 32)
+
+
+def run_case(torch, name, wl, op, opt, steps, warmup):
+    w = workloads.WORKLOADS[wl]
+    x0, g = workloads.make_inputs(wl, device="cuda")
+    T, D = x0.shape
+    if not opt.get("gamma", True):
+        g = None
+    elem = opt.get("elem", mxq.MXQ_E4M3)
+    rnd = opt.get("rnd", mxq.MXQ_RNE)
+    rng = mxq.mxq_rng(workloads.SR_SEED, workloads.SR_OFFSET)
+    x_bytes = x0.numel() * 2
+    R = max(2, min(10, -(-(1 << 30) // x_bytes)))      # >= 1 GB of inputs in rotation
+    cb = D // 2 if elem == mxq.MXQ_E2M1 else D
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    codes = [torch.empty((T, cb), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    scales = [torch.empty((T, D // 32), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    invs = [torch.empty((T,), dtype=torch.float32, device="cuda") for _ in range(R)]
+    ys = ([torch.empty((T, D), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+          if op == "two_pass" else None)
+    L = mxq.lib()
+    vp = ctypes.c_void_p
+    gp = vp(g.data_ptr()) if g is not None else None
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    rngp = ctypes.pointer(rng) if rnd == mxq.MXQ_SR else None
+
+    def launch(i):
+        k = i % R
+        xp, cp, sp, ip = (vp(xs[k].data_ptr()), vp(codes[k].data_ptr()),
+                          vp(scales[k].data_ptr()), vp(invs[k].data_ptr()))
+        if op == "mxnorm":
+            st = L.mxnorm_fwd(xp, D, gp, T, D, ctypes.c_float(opt.get("p", 2.0)), elem, rnd, rngp,
+                              opt.get("flags", 0), cp, sp, ip, stream)
+        elif op == "rms_fused":
+            st = L.rmsnorm_mxcast_fused_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
+                                            0, cp, sp, ip, stream)
+        elif op == "two_pass":
+            st = L.rmsnorm_mxcast_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
+                                      vp(ys[k].data_ptr()), cp, sp, ip, stream)
+        else:
+            st = L.mxcast_fwd(xp, D, T, D, elem, rnd, rngp, cp, sp, stream)
+        if st != mxq.MXQ_OK:
+            raise mxq.MxqError(st, name)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        launch(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    nbytes = algorithmic_bytes(op, T, D, elem)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(f"{name:44s} T={T:6d} D={D:6d} {us:9.2f} us/launch (events, back-to-back)  "
+          f"{nbytes:>13,d} B  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of HBM peak",
+          flush=True)
+    del xs, codes, scales, invs, ys
+    torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="")
+    args = ap.parse_args()
+    import torch
+    if not torch.cuda.is_available():
+        print("timing needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sel = [s for s in args.only.split(",") if s]
+    for name, wl, op, opt in CASES:
+        if sel and not any(s in name for s in sel):
+            continue
+        run_case(torch, name, wl, op, opt, args.steps, args.warmup)
+
+
+if __name__ == "__main__":
+    main()
