@@ -91,6 +91,10 @@ def lib():
             L.orc_rmsnorm_fused_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64,
                                                    u64, i64, vp, vp, vp, vp]
             L.orc_rmsnorm_fused_mxcast.restype = i32
+            L.orc_mxnorm_bwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp]
+            L.orc_mxnorm_bwd.restype = i32
+            L.orc_mxnorm_bwd_dgamma.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp]
+            L.orc_mxnorm_bwd_dgamma.restype = i32
             _lib = L
     return _lib
 
@@ -238,6 +242,44 @@ def rmsnorm_fused_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0
             _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return codes, scales, inv
+
+
+def mxnorm_bwd(x, gamma, dy, inv, s_inject=None, threads=1):
+    """Straight-through backward: returns (dx uint16 bf16 bits [T, D], s float64 [T]).
+    s_inject=None: mode (R); else mode (I) with the given fp32 row dots."""
+    L = lib()
+    x, T, D, ldx = _rows_view(as_bf16_bits(x))
+    d, T2, D2, lddy = _rows_view(as_bf16_bits(dy))
+    assert (T2, D2) == (T, D)
+    g = None if gamma is None else np.ascontiguousarray(as_bf16_bits(gamma).reshape(-1))
+    iv = np.ascontiguousarray(np.asarray(inv, dtype=np.float32).reshape(-1))
+    inj = None if s_inject is None else np.ascontiguousarray(
+        np.asarray(s_inject, dtype=np.float32).reshape(-1))
+    dx = np.zeros((T, D), np.uint16)
+    s = np.zeros(T, np.float64)
+    xb, db = x.ctypes.data, d.ctypes.data
+
+    def job(r0, r1):
+        return lambda: L.orc_mxnorm_bwd(
+            ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), ctypes.c_void_p(db + 2 * r0 * lddy),
+            lddy, _ptr(iv[r0:]), r1 - r0, D, None if inj is None else _ptr(inj[r0:]),
+            _ptr(dx[r0:]), _ptr(s[r0:]))
+    _run([job(a, b) for a, b in _split(T, threads)], threads)
+    return dx, s
+
+
+def mxnorm_bwd_dgamma(x, dy, inv):
+    """dgamma [D] float64 and the matching sum of |terms| per column."""
+    L = lib()
+    x, T, D, ldx = _rows_view(as_bf16_bits(x))
+    d, _, _, lddy = _rows_view(as_bf16_bits(dy))
+    iv = np.ascontiguousarray(np.asarray(inv, dtype=np.float32).reshape(-1))
+    out = np.zeros(D, np.float64)
+    ab = np.zeros(D, np.float64)
+    rc = L.orc_mxnorm_bwd_dgamma(_ptr(x), ldx, _ptr(d), lddy, _ptr(iv), T, D, _ptr(out), _ptr(ab))
+    if rc:
+        raise ValueError(f"oracle returned error {rc}")
+    return out, ab
 
 
 # --------------------------------------------------------------------------

@@ -1,6 +1,7 @@
 /*
  * mxq_oracle.c - plain, slow, scalar CPU oracle for MXNorm, RMSNorm -> MXCast
- * (two-pass, and the single-pass exact-RMS comparator) and MXCast.
+ * (two-pass, and the single-pass exact-RMS comparator), MXCast, and the
+ * straight-through backward of the normalisation.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this. It shares no code, header, table or constant
@@ -494,5 +495,76 @@ int orc_rmsnorm_fused_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gam
   }
   free(y);
   free(cu);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward (straight-through)                                         */
+/* ------------------------------------------------------------------ */
+
+/* Backward of the normalisation with the cast taken as the identity (MXNorm
+ * page, §2.3, gradient paragraph: RMSNorm's gradient computation is reused as a
+ * straight-through estimator), with the forward's normaliser inv_t = 1/G_t in
+ * the place of RMSNorm's 1/rms. Per row t, with g_i = gamma_i * dy_i:
+ *   s_t  = sum_i g_i * x_i
+ *   dx_i = inv_t * g_i - inv_t^3 * (s_t / D) * x_i
+ * which is d/dx of gamma * x * r(x) for r = (mean(x^2))^(-1/2), with r's value
+ * replaced by inv_t. (R): everything in fp64, dx rounded once to bf16.
+ * (I): s_inject[t] is the kernel's fp32 row dot and the fp32 order is
+ *   k = RN(RN(inv*inv)*inv); c = RN(k * RN(s/D)); dx = bf16(RN(RN(inv*g) - RN(c*x))).
+ * s_out (nullable) receives the s used. dx is contiguous [T, D]. */
+int orc_mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
+                   int64_t lddy, const float* inv, int64_t T, int64_t D, const float* s_inject,
+                   uint16_t* dx, double* s_out) {
+  if (T < 0 || D <= 0) return 2;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ldx;
+    const uint16_t* dr = dy + t * lddy;
+    double s;
+    if (s_inject) {
+      s = (double)s_inject[t];
+    } else {
+      s = 0;
+      for (int64_t d = 0; d < D; ++d) {
+        double gi = gamma ? orc_bf16_to_f64(gamma[d]) : 1.0;
+        s += gi * orc_bf16_to_f64(dr[d]) * orc_bf16_to_f64(xr[d]);
+      }
+    }
+    if (s_out) s_out[t] = s;
+    const double a = (double)inv[t];
+    for (int64_t d = 0; d < D; ++d) {
+      double gi = gamma ? orc_bf16_to_f64(gamma[d]) : 1.0;
+      double g = gi * orc_bf16_to_f64(dr[d]); /* exact in fp32 and fp64 */
+      double xi = orc_bf16_to_f64(xr[d]);
+      double v;
+      if (s_inject) {
+        float k = rn32((double)rn32(a * a) * a);
+        float c = rn32((double)k * (double)rn32(s / (double)D));
+        v = (double)rn32((double)rn32(a * g) - (double)rn32((double)c * xi));
+      } else {
+        v = a * g - a * a * a * (s / (double)D) * xi;
+      }
+      dx[t * D + d] = orc_bf16_rne(v);
+    }
+  }
+  return 0;
+}
+
+/* Gradient of the gain: dgamma_i = sum_t dy_ti * x_ti * inv_t, in fp64, rows in
+ * order (MXNorm page, §2.3: the gain of the normalisation). */
+int orc_mxnorm_bwd_dgamma(const uint16_t* x, int64_t ldx, const uint16_t* dy, int64_t lddy,
+                          const float* inv, int64_t T, int64_t D, double* dgamma,
+                          double* abs_sum) {
+  if (T < 0 || D <= 0) return 2;
+  for (int64_t d = 0; d < D; ++d) {
+    dgamma[d] = 0;
+    if (abs_sum) abs_sum[d] = 0;
+  }
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t d = 0; d < D; ++d) {
+      double v = orc_bf16_to_f64(dy[t * lddy + d]) * orc_bf16_to_f64(x[t * ldx + d]) * (double)inv[t];
+      dgamma[d] += v;
+      if (abs_sum) abs_sum[d] += fabs(v);
+    }
   return 0;
 }
