@@ -63,6 +63,7 @@
 #ifndef MXQ_H
 #define MXQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -154,6 +155,38 @@ mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16
 mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
                       mxq_round rnd, const mxq_rng* rng, uint8_t* codes, uint8_t* scales,
                       void* stream);
+
+/*
+ * Straight-through backward of the normalisation (MXNorm page, §2.3, gradient
+ * paragraph: RMSNorm's gradient computation is reused as a straight-through
+ * estimator). The cast counts as the identity, and the forward's exported
+ * normaliser inv_norm (1/G from mxnorm_fwd, or any per-row normaliser) stands
+ * where RMSNorm has 1/rms. Per row t, with g = gamma * dy:
+ *   s_t      = sum_i g_i * x_i
+ *   dx_ti    = inv_t * g_i - inv_t^3 * (s_t / D) * x_ti      (rounded to bf16)
+ *   dgamma_i = sum_t dy_ti * x_ti * inv_t                      (fp32)
+ * fp32 order: g and dy * x are exact; s sums each lane's chunks in order and
+ * then the wave, as the RMS paths do; k = (inv*inv)*inv, c = k * (s/D),
+ * dx = bf16(inv*g - c*x). dgamma sums rows in a fixed order (bit-reproducible
+ * from run to run).
+ *   x [T, D] bf16, row stride ldx; dy [T, D] bf16, row stride lddy.
+ *   gamma [D] bf16 or NULL (gamma == 1).  inv_norm [T] fp32.
+ *   dx [T, D] bf16 contiguous output.  row_dot [T] fp32 output (s), may be NULL.
+ *   dgamma [D] fp32 output (16-byte aligned), may be NULL; it then needs a
+ *   caller-owned workspace of at least mxnorm_bwd_workspace_size(T, D) bytes
+ *   (16-byte aligned), which the call overwrites. For T == 0, dgamma is zeroed.
+ * Errors: SHAPE (T < 0, D <= 0, D % 32, ldx or lddy < D), UNSUPPORTED
+ * (D > MXQ_MAX_D_REG), NULL (x, dy, inv_norm, dx; workspace with dgamma), ARG
+ * (workspace too small), ALIGN (16-byte x, dy, dx, gamma, dgamma, workspace;
+ * ldx, lddy % 8), HIP.
+ */
+mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
+                      int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
+                      float* row_dot, float* dgamma, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Workspace bytes mxnorm_bwd needs to produce dgamma (0 for a bad shape). */
+size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D);
 
 /* Static message for a status code (never NULL). */
 const char* mxq_strerror(mxq_status status);

@@ -29,7 +29,7 @@ MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
 ABI_VERSION = 1
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
-           "mxq_strerror", "mxq_abi_version")
+           "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mxq_strerror", "mxq_abi_version")
 
 
 class mxq_rng(ctypes.Structure):
@@ -69,6 +69,11 @@ def lib():
             L.rmsnorm_mxcast_fused_fwd.restype = i32
             L.mxcast_fwd.argtypes = [vp, i64, i64, i64, i32, i32, rp, vp, vp, vp]
             L.mxcast_fwd.restype = i32
+            L.mxnorm_bwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+            L.mxnorm_bwd.restype = i32
+            L.mxnorm_bwd_workspace_size.argtypes = [i64, i64]
+            L.mxnorm_bwd_workspace_size.restype = ctypes.c_size_t
             L.mxq_strerror.argtypes = [i32]
             L.mxq_strerror.restype = ctypes.c_char_p
             L.mxq_abi_version.argtypes = []
@@ -110,6 +115,16 @@ def rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, co
 
 def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, codes, scales, stream) -> int:
     return lib().mxcast_fwd(x, ldx, T, D, elem, rnd, _rng(rng), codes, scales, stream)
+
+
+def mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, workspace,
+               workspace_bytes, stream) -> int:
+    return lib().mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma,
+                            workspace, workspace_bytes, stream)
+
+
+def mxnorm_bwd_workspace_size(T, D) -> int:
+    return lib().mxnorm_bwd_workspace_size(T, D)
 
 
 def mxq_strerror(status: int) -> str:
@@ -218,6 +233,34 @@ def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: i
     if st != MXQ_OK:
         raise MxqError(st, "mxcast_fwd")
     return codes, scales
+
+
+def mxnorm_backward(x, gamma, dy, inv_norm, want_dgamma: bool = True, stream=None, out=None):
+    """Straight-through backward. Returns (dx bf16, row_dot fp32, dgamma fp32 or None).
+    out = (dx, row_dot, dgamma, workspace) reuses caller buffers."""
+    import torch
+    T, D, ldx = _check_x(x)
+    Td, Dd, lddy = _check_x(dy)
+    if (Td, Dd) != (T, D):
+        raise ValueError("dy must have the shape of x")
+    if inv_norm.dtype != torch.float32 or inv_norm.numel() != T or not inv_norm.is_contiguous():
+        raise ValueError("inv_norm must be a contiguous fp32 tensor of T elements")
+    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
+        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    if out is not None:
+        dx, row_dot, dgamma, ws = out
+    else:
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        row_dot = torch.empty((T,), dtype=torch.float32, device=x.device)
+        dgamma = torch.empty((D,), dtype=torch.float32, device=x.device) if want_dgamma else None
+        nb = mxnorm_bwd_workspace_size(T, D) if want_dgamma else 0
+        ws = torch.empty((max(nb, 16) // 4,), dtype=torch.float32, device=x.device) if want_dgamma else None
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = mxnorm_bwd(_ptr(x), ldx, _ptr(gamma), _ptr(dy), lddy, _ptr(inv_norm), T, D, _ptr(dx),
+                    _ptr(row_dot), _ptr(dgamma), _ptr(ws), nbytes, _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "mxnorm_bwd")
+    return dx, row_dot, dgamma
 
 
 def as_torch_mx(codes, scales, fmt: str = "e4m3"):

@@ -36,11 +36,18 @@ CASES = (
     ("swiglu_downproj mxcast rne", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_RNE}),
     ("swiglu_downproj mxcast sr", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_SR}),
     ("mxfp4 mxnorm e2m1", "mxfp4", "mxnorm", {"elem": mxq.MXQ_E2M1}),
+    ("llama3_8b_preattn backward dx+dgamma", "llama3_8b_preattn", "backward", {}),
+    ("llama3_8b_preattn backward dx only", "llama3_8b_preattn", "backward", {"dgamma": False}),
+    ("mxfp4 backward dx+dgamma", "mxfp4", "backward", {}),
 )
 
 
 def algorithmic_bytes(op, T, D, elem):
     code = D // 2 if elem == mxq.MXQ_E2M1 else D
+    if op == "backward":
+        # read x and dy, write dx (bf16), read the normaliser; the dgamma
+        # partials are workspace traffic and not counted
+        return T * (2 * D + 2 * D + 2 * D + 4)
     if op == "two_pass":
         return T * (2 * D + 2 * D + 2 * D + code + D // 32)
     return T * (2 * D + code + D // 32)
@@ -63,7 +70,18 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
     scales = [torch.empty((T, D // 32), dtype=torch.uint8, device="cuda") for _ in range(R)]
     invs = [torch.empty((T,), dtype=torch.float32, device="cuda") for _ in range(R)]
     ys = ([torch.empty((T, D), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-          if op == "two_pass" else None)
+          if op in ("two_pass", "backward") else None)
+    if op == "backward":
+        R = max(2, min(10, -(-(1 << 30) // (3 * x_bytes))))
+        xs, ys = xs[:R], ys[:R]
+        dys = [workloads.random_rows(T, D, seed=7 + k, device="cuda") for k in range(R)]
+        for k in range(R):
+            mxq.mxnorm(xs[k], g, 2.0, out=(codes[k], scales[k], invs[k]))
+        want_dg = opt.get("dgamma", True)
+        dgam = torch.empty((D,), dtype=torch.float32, device="cuda")
+        wsb = mxq.mxnorm_bwd_workspace_size(T, D)
+        ws = torch.empty((wsb // 4,), dtype=torch.float32, device="cuda")
+        rows = torch.empty((T,), dtype=torch.float32, device="cuda")
     L = mxq.lib()
     vp = ctypes.c_void_p
     gp = vp(g.data_ptr()) if g is not None else None
@@ -80,6 +98,11 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
         elif op == "rms_fused":
             st = L.rmsnorm_mxcast_fused_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
                                             0, cp, sp, ip, stream)
+        elif op == "backward":
+            st = L.mxnorm_bwd(xp, D, gp, vp(dys[k].data_ptr()), D, ip, T, D, vp(ys[k].data_ptr()),
+                              vp(rows.data_ptr()), vp(dgam.data_ptr()) if want_dg else None,
+                              vp(ws.data_ptr()) if want_dg else None, wsb if want_dg else 0,
+                              stream)
         elif op == "two_pass":
             st = L.rmsnorm_mxcast_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
                                       vp(ys[k].data_ptr()), cp, sp, ip, stream)

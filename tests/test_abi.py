@@ -162,3 +162,47 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
+
+
+def bwd(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, dy=A16, lddy=4096, inv=A16, T=8, D=4096, dx=A16,
+             row_dot=None, dgamma=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return mxq.mxnorm_bwd(a["x"], a["ldx"], a["gamma"], a["dy"], a["lddy"], a["inv"], a["T"],
+                          a["D"], a["dx"], a["row_dot"], a["dgamma"], a["ws"], a["wsb"],
+                          a["stream"])
+
+
+def test_backward_argument_errors():
+    assert bwd(D=0) == mxq.MXQ_ERR_SHAPE
+    assert bwd(D=4000 + 16) == mxq.MXQ_ERR_SHAPE
+    assert bwd(T=-1) == mxq.MXQ_ERR_SHAPE
+    assert bwd(ldx=2048) == mxq.MXQ_ERR_SHAPE
+    assert bwd(lddy=2048) == mxq.MXQ_ERR_SHAPE
+    assert bwd(D=8224, ldx=8224, lddy=8224) == mxq.MXQ_ERR_UNSUPPORTED
+    assert bwd(x=None) == mxq.MXQ_ERR_NULL
+    assert bwd(dy=None) == mxq.MXQ_ERR_NULL
+    assert bwd(inv=None) == mxq.MXQ_ERR_NULL
+    assert bwd(dx=None) == mxq.MXQ_ERR_NULL
+    assert bwd(x=A8) == mxq.MXQ_ERR_ALIGN
+    assert bwd(dy=A8) == mxq.MXQ_ERR_ALIGN
+    assert bwd(dx=A8) == mxq.MXQ_ERR_ALIGN
+    assert bwd(gamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert bwd(lddy=4100) == mxq.MXQ_ERR_ALIGN
+    need = mxq.mxnorm_bwd_workspace_size(8, 4096)
+    assert need >= 4096 * 4 * 2
+    assert bwd(dgamma=A16, ws=None) == mxq.MXQ_ERR_NULL
+    assert bwd(dgamma=A16, ws=A16, wsb=need - 1) == mxq.MXQ_ERR_ARG
+    assert bwd(dgamma=A8, ws=A16, wsb=need) == mxq.MXQ_ERR_ALIGN
+    assert bwd(dgamma=A16, ws=A8, wsb=need) == mxq.MXQ_ERR_ALIGN
+    assert mxq.mxnorm_bwd_workspace_size(8, 100) == 0
+    # empty input without dgamma launches nothing and reads no pointer
+    assert bwd(T=0, x=None, dy=None, inv=None, dx=None) == mxq.MXQ_OK
+
+
+def test_backward_workspace_grows_slowly_with_rows():
+    # at most 512 partial rows of D floats plus their segment sums
+    D = 4096
+    small = mxq.mxnorm_bwd_workspace_size(64, D)
+    big = mxq.mxnorm_bwd_workspace_size(1 << 20, D)
+    assert small < big <= (512 + 32) * D * 4

@@ -325,6 +325,106 @@ def test_rms_fused_statistic_matches_two_pass_bitwise():
         assert torch.equal(inv_f, inv_t), D
 
 
+# ---------------------------------------------------------------- straight-through backward
+
+U24 = 2.0 ** -24
+
+
+def check_backward(x, g, dy, inv, what="", dgamma=True):
+    """Kernel backward against the oracle: dx bit-exact in mode (I) (the
+    kernel's own row dot), the row dot and dx within the fp32 rounding bounds
+    of mode (R), dgamma within the bound of its fixed summation order."""
+    T, D = x.shape
+    dx, row_dot, dg = mxq.mxnorm_backward(x, g, dy, inv, want_dgamma=dgamma)
+    torch.cuda.synchronize()
+    xs, gs, dys, iv = host(x), host(g), host(dy), np_(inv)
+    s_k = np_(row_dot)
+    ox, _ = oracle.mxnorm_bwd(xs, gs, dys, iv, s_inject=s_k, threads=THREADS)
+    assert_bits(np_(dx.view(torch.int16)).view(np.uint16), ox, f"{what} dx (I)")
+    rx, s64 = oracle.mxnorm_bwd(xs, gs, dys, iv, threads=THREADS)
+    gd = np.ones(D) if g is None else gs.double().numpy()
+    terms = np.abs(gd[None, :] * dys.double().numpy() * xs.double().numpy())
+    sabs = terms.sum(1)
+    nc = -(-D // 512)
+    # s: each lane adds 8 * nc terms in order, then 6 butterfly levels
+    assert (np.abs(s_k - s64) <= (8 * nc + 8) * U24 * sabs).all(), what
+    # dx against (R): one bf16 ulp of the result plus the fp32 error of the
+    # two terms (the row dot's bound scaled by inv^3 |x| / D, and 4 roundings)
+    a = iv.astype(np.float64)[:, None]
+    xd = xs.double().numpy()
+    t1 = np.abs(a * gd[None, :] * dys.double().numpy())
+    t2 = np.abs(a ** 3 * s64[:, None] / D * xd)
+    ref = torch.from_numpy(rx.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = torch.from_numpy(np_(dx.view(torch.int16))).view(torch.bfloat16).double().numpy()
+    want64 = a * gd[None, :] * dys.double().numpy() - a ** 3 * (s64[:, None] / D) * xd
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(want64), 1e-38))).astype(np.int64) - 7)
+    bound = ulp + 4 * U24 * (t1 + t2) + a ** 3 * np.abs(xd) / D * (8 * nc + 8) * U24 * sabs[:, None]
+    assert (np.abs(got - want64) <= bound).all(), what
+    assert (np.abs(got - ref) <= 2 * ulp + bound).all(), what
+    if dgamma:
+        dg64, absum = oracle.mxnorm_bwd_dgamma(xs, dys, iv)
+        # per column: each term rounds twice, each wave adds its rows in order,
+        # then 2 combine levels, then up to 16 + 32 sequential partial sums
+        per_wave = -(-T // 4)
+        n = min(per_wave, 64) + 2 + 16 + 32 + 2
+        assert (np.abs(np_(dg) - dg64) <= n * U24 * absum + 1e-30).all(), what
+    return dx, row_dot, dg
+
+
+@pytest.mark.parametrize("D", [32, 96, 512, 1056, 4096, 8192])
+@pytest.mark.parametrize("gamma", [False, True])
+def test_backward_shapes(D, gamma):
+    T = 13
+    x = workloads.random_rows(T, D, seed=301 + D, device=DEV)
+    x[3, : min(D, 64)] *= 30.0
+    dy = workloads.random_rows(T, D, seed=302 + D, device=DEV)
+    g = workloads.random_gamma(D, seed=303, device=DEV) if gamma else None
+    _, _, inv = mxq.mxnorm(x, g, 2.0)
+    check_backward(x, g, dy, inv, what=f"bwd D={D} gamma={gamma}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 5, 64, 700, 3000])
+def test_backward_row_counts(T):
+    # ragged row blocks per workgroup, and more rows than partial groups
+    D = 512
+    x = workloads.random_rows(T, D, seed=304 + T, device=DEV)
+    dy = workloads.random_rows(T, D, seed=305 + T, device=DEV)
+    g = workloads.random_gamma(D, seed=306, device=DEV)
+    _, _, inv = mxq.mxnorm(x, g, 2.0)
+    check_backward(x, g, dy, inv, what=f"bwd T={T}")
+
+
+def test_backward_strided_and_no_dgamma():
+    x = workloads.random_rows(9, 1024, seed=307, device=DEV, ldx=1056)
+    dy = workloads.random_rows(9, 1024, seed=308, device=DEV, ldx=1088)
+    g = workloads.random_gamma(1024, seed=309, device=DEV)
+    _, _, inv = mxq.mxnorm(x, g, 1.0)
+    a = check_backward(x, g, dy, inv, what="bwd strided")
+    b = check_backward(x.contiguous(), g, dy.contiguous(), inv, what="bwd strided", dgamma=False)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and b[2] is None
+
+
+def test_backward_is_deterministic_and_empty():
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV, rows=1000)
+    dy = workloads.random_rows(1000, 4096, seed=310, device=DEV)
+    _, _, inv = mxq.mxnorm(x, g, 2.0)
+    a = mxq.mxnorm_backward(x, g, dy, inv)
+    b = mxq.mxnorm_backward(x, g, dy, inv)
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+    e = torch.empty(0, 4096, dtype=torch.bfloat16, device=DEV)
+    dx, rd, dg = mxq.mxnorm_backward(e, g, e, torch.empty(0, device=DEV))
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 4096) and (dg == 0).all()
+
+
+def test_backward_llama3_workload():
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV)
+    dy = workloads.random_rows(x.shape[0], x.shape[1], seed=311, device=DEV)
+    _, _, inv = mxq.mxnorm(x, g, 2.0)
+    check_backward(x, g, dy, inv, what="bwd llama3-8b")
+
+
 # ---------------------------------------------------------------- the five workloads
 
 def test_workload_llama3_8b_full():
