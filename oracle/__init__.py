@@ -95,6 +95,9 @@ def lib():
             L.orc_mxnorm_bwd.restype = i32
             L.orc_mxnorm_bwd_dgamma.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp, vp]
             L.orc_mxnorm_bwd_dgamma.restype = i32
+            L.orc_mx_gemm.argtypes = [vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i64, i64,
+                                      i64, vp, vp]
+            L.orc_mx_gemm.restype = i32
             _lib = L
     return _lib
 
@@ -280,6 +283,30 @@ def mxnorm_bwd_dgamma(x, dy, inv):
     if rc:
         raise ValueError(f"oracle returned error {rc}")
     return out, ab
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales, K, elem_a="e4m3", elem_b="e4m3",
+            threads=1):
+    """C = A B^T over MX operands (codes [rows, K or K/2] uint8, scales [rows, K/32]).
+    Returns (C float64 [M, N], sum |a b| float64 [M, N])."""
+    L = lib()
+    A = np.ascontiguousarray(np.asarray(a_codes, dtype=np.uint8))
+    SA = np.ascontiguousarray(np.asarray(a_scales, dtype=np.uint8))
+    B = np.ascontiguousarray(np.asarray(b_codes, dtype=np.uint8))
+    SB = np.ascontiguousarray(np.asarray(b_scales, dtype=np.uint8))
+    M, N = A.shape[0], B.shape[0]
+    c = np.zeros((M, N), np.float64)
+    ab = np.zeros((M, N), np.float64)
+    ea, eb = ELEM[elem_a], ELEM[elem_b]
+
+    def job(r0, r1):
+        return lambda: L.orc_mx_gemm(
+            ctypes.c_void_p(A.ctypes.data + r0 * A.shape[1]), A.shape[1],
+            ctypes.c_void_p(SA.ctypes.data + r0 * SA.shape[1]), SA.shape[1], ea,
+            _ptr(B), B.shape[1], _ptr(SB), SB.shape[1], eb, r1 - r0, N, K,
+            _ptr(c[r0:]), _ptr(ab[r0:]))
+    _run([job(x, y) for x, y in _split(M, threads)], threads)
+    return c, ab
 
 
 # --------------------------------------------------------------------------

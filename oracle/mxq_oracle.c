@@ -1,7 +1,8 @@
 /*
  * mxq_oracle.c - plain, slow, scalar CPU oracle for MXNorm, RMSNorm -> MXCast
- * (two-pass, and the single-pass exact-RMS comparator), MXCast, and the
- * straight-through backward of the normalisation.
+ * (two-pass, and the single-pass exact-RMS comparator), MXCast, the
+ * straight-through backward of the normalisation, and the MX GEMM that
+ * consumes the MX output.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this. It shares no code, header, table or constant
@@ -566,5 +567,51 @@ int orc_mxnorm_bwd_dgamma(const uint16_t* x, int64_t ldx, const uint16_t* dy, in
       dgamma[d] += v;
       if (abs_sum) abs_sum[d] += fabs(v);
     }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MX GEMM (the consumer of the MX output)                             */
+/* ------------------------------------------------------------------ */
+
+/* Decoded value of element k of an MX row: code (unpacked from the E2M1 byte
+ * pair when elem is E2M1) times the block's scale 2^(s - 127); a 0xFF scale
+ * is NaN. */
+static double mx_value(const uint8_t* codes_row, const uint8_t* scales_row, int elem, int64_t k) {
+  uint8_t c;
+  if (elem == ORC_E2M1) c = (uint8_t)((codes_row[k / 2] >> (4 * (k & 1))) & 0xF);
+  else c = codes_row[k];
+  uint8_t s = scales_row[k / 32];
+  if (s == 0xFF) return NAN;
+  double v = elem == ORC_E2M1 ? orc_e2m1_decode(c) : orc_e4m3_decode(c);
+  return v * ldexp(1.0, (int)s - 127);
+}
+
+/* C[m][n] = sum_k A[m][k] * B[n][k] over MX operands: A is [M, K] with its
+ * scales [M, K/32] (the MX cast of the activation, MXNorm page §2.1), B is
+ * [N, K] with scales [N, K/32] (the next linear layer's weight, gain folded and
+ * MX-cast along K, §2.3). fp64, k in order. abs_out (nullable) receives
+ * sum_k |A[m][k] B[n][k]|. lda / ldb are code bytes per row, ldsa / ldsb scale
+ * bytes per row. */
+int orc_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t ldsa, int elem_a,
+                const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ldsb, int elem_b,
+                int64_t M, int64_t N, int64_t K, double* c, double* abs_out) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return 2;
+  double* av = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!av) return 6;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t k = 0; k < K; ++k) av[k] = mx_value(a + m * lda, sa + m * ldsa, elem_a, k);
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0, ab = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        double p = av[k] * mx_value(b + n * ldb, sb + n * ldsb, elem_b, k);
+        acc += p;
+        ab += fabs(p);
+      }
+      c[m * N + n] = acc;
+      if (abs_out) abs_out[m * N + n] = ab;
+    }
+  }
+  free(av);
   return 0;
 }
