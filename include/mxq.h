@@ -188,6 +188,33 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
 /* Workspace bytes mxnorm_bwd needs to produce dgamma (0 for a bad shape). */
 size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D);
 
+/* Element type of a GEMM result. */
+typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;
+
+/*
+ * MX GEMM, the consumer of the MX output (MXNorm page, §2.3: the gain is
+ * folded into the next linear layer's weight, which is MX-cast; §3.2 times the
+ * layer around it):
+ *   C[m][n] = sum_k A[m][k] * B[n][k],
+ * with A[m][k] = dec(a[m][k]) * 2^(a_scales[m][k/32] - 127) (the MX output of
+ * mxnorm_fwd / mxcast_fwd, [M, K]) and B likewise from the weight [N, K] MX-cast
+ * along K (mxcast_fwd of W). The products run on the gfx950 block-scaled matrix
+ * cores with fp32 accumulation (order not specified); C is fp32 or bf16
+ * (round to nearest even) [M, N] with row stride ldc elements. A NaN code or a
+ * 0xFF scale makes the outputs it reaches NaN.
+ *   a, b       codes, lda / ldb bytes per row (>= K), 16-byte aligned rows.
+ *   a_scales, b_scales  E8M0 bytes, ldsa / ldsb per row (>= K/32, % 4 == 0),
+ *              4-byte aligned.
+ *   elem_a, elem_b  MXQ_E4M3 (MXQ_E2M1 is reserved: UNSUPPORTED).
+ * Errors: SHAPE (M, N < 0, K <= 0, K % 32, a leading dimension too small), ARG
+ * (unknown element or output type), UNSUPPORTED (E2M1, K % 128 != 0, sizes of
+ * 2^31 or more), NULL, ALIGN, HIP. M == 0 or N == 0 is a no-op.
+ */
+mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_scales, int64_t ldsa,
+                   const uint8_t* b, int64_t ldb, const uint8_t* b_scales, int64_t ldsb,
+                   int64_t M, int64_t N, int64_t K, mxq_elem elem_a, mxq_elem elem_b, void* c,
+                   int64_t ldc, mxq_out_type c_type, void* stream);
+
 /* Static message for a status code (never NULL). */
 const char* mxq_strerror(mxq_status status);
 

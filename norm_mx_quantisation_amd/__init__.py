@@ -25,11 +25,13 @@ MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_ARG, MXQ_ERR_UNSUPPO
 MXQ_E4M3, MXQ_E2M1 = 0, 1
 MXQ_RNE, MXQ_SR = 0, 1
 MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS = 1, 2
+MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
 ABI_VERSION = 1
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
-           "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mxq_strerror", "mxq_abi_version")
+           "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mx_gemm", "mxq_strerror",
+           "mxq_abi_version")
 
 
 class mxq_rng(ctypes.Structure):
@@ -74,6 +76,9 @@ def lib():
             L.mxnorm_bwd.restype = i32
             L.mxnorm_bwd_workspace_size.argtypes = [i64, i64]
             L.mxnorm_bwd_workspace_size.restype = ctypes.c_size_t
+            L.mx_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, i32, vp,
+                                  i64, i32, vp]
+            L.mx_gemm.restype = i32
             L.mxq_strerror.argtypes = [i32]
             L.mxq_strerror.restype = ctypes.c_char_p
             L.mxq_abi_version.argtypes = []
@@ -125,6 +130,12 @@ def mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, wor
 
 def mxnorm_bwd_workspace_size(T, D) -> int:
     return lib().mxnorm_bwd_workspace_size(T, D)
+
+
+def mx_gemm(a, lda, a_scales, ldsa, b, ldb, b_scales, ldsb, M, N, K, elem_a, elem_b, c, ldc,
+            c_type, stream) -> int:
+    return lib().mx_gemm(a, lda, a_scales, ldsa, b, ldb, b_scales, ldsb, M, N, K, elem_a, elem_b,
+                         c, ldc, c_type, stream)
 
 
 def mxq_strerror(status: int) -> str:
@@ -261,6 +272,31 @@ def mxnorm_backward(x, gamma, dy, inv_norm, want_dgamma: bool = True, stream=Non
     if st != MXQ_OK:
         raise MxqError(st, "mxnorm_bwd")
     return dx, row_dot, dgamma
+
+
+def mx_matmul(a_codes, a_scales, b_codes, b_scales, out_dtype=None, stream=None, out=None):
+    """C = A B^T for MX operands (uint8 codes [M, K] / [N, K], E8M0 scales [M, K/32] /
+    [N, K/32], E4M3). out_dtype torch.float32 (default) or torch.bfloat16."""
+    import torch
+    for t in (a_codes, a_scales, b_codes, b_scales):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 2 or not t.is_cuda:
+            raise TypeError("MX operands must be 2-D uint8 GPU tensors")
+        if t.stride(1) != 1:
+            raise ValueError("MX operands need unit column stride")
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    if b_codes.shape[1] != K or a_scales.shape != (M, K // 32) or b_scales.shape != (N, K // 32):
+        raise ValueError("MX operand shapes do not match")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    ct = {torch.float32: MXQ_OUT_F32, torch.bfloat16: MXQ_OUT_BF16}[out_dtype]
+    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    ld = lambda t: t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    st = mx_gemm(_ptr(a_codes), ld(a_codes), _ptr(a_scales), ld(a_scales), _ptr(b_codes),
+                 ld(b_codes), _ptr(b_scales), ld(b_scales), M, N, K, MXQ_E4M3, MXQ_E4M3, _ptr(c),
+                 ld(c) if M > 1 else N, ct, _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "mx_gemm")
+    return c
 
 
 def as_torch_mx(codes, scales, fmt: str = "e4m3"):

@@ -3,16 +3,17 @@
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mxq.hip")
+SRCS = [os.path.join(PKG, "csrc", "mxq.hip"), os.path.join(PKG, "csrc", "mx_gemm.hip")]
 HDR = os.path.join(ROOT, "include", "mxq.h")
 LIB = os.path.join(PKG, "libmxq.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # the arithmetic order is the one written in the source: no contraction
     "-ffp-contract=off",
     # packed-fp32 VALU ops stay off
@@ -22,15 +23,32 @@ FLAGS = [
 
 def build(force: bool = True, verbose: bool = False) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
-            os.path.getmtime(SRC), os.path.getmtime(HDR)):
+            os.path.getmtime(p) for p in SRCS + [HDR]):
         return LIB
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    res = subprocess.run(cmd, cwd="/tmp", capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    with tempfile.TemporaryDirectory() as tmpdir:
+        objs, procs = [], []
+        for src in SRCS:   # each source compiles in its own process, in parallel
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), file=sys.stderr)
+            procs.append(subprocess.Popen(cmd, cwd=tmpdir, stdout=subprocess.PIPE,
+                                          stderr=subprocess.PIPE, text=True))
+            objs.append(obj)
+        errors = []
+        for p in procs:
+            out, err = p.communicate()
+            if p.returncode != 0:
+                errors.append(out + err)
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        res = subprocess.run(cmd, cwd=tmpdir, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
     return LIB
 

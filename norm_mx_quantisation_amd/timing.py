@@ -39,7 +39,14 @@ CASES = (
     ("llama3_8b_preattn backward dx+dgamma", "llama3_8b_preattn", "backward", {}),
     ("llama3_8b_preattn backward dx only", "llama3_8b_preattn", "backward", {"dgamma": False}),
     ("mxfp4 backward dx+dgamma", "mxfp4", "backward", {}),
+    # MXNormLinear: the MX output of llama3_8b_preattn [8192, 4096] times a
+    # gain-folded, MX-cast weight: the QKV projection (4096 + 1024 + 1024 rows)
+    # and the feed-forward up projection (14336 rows)
+    ("llama3_8b_preattn mx_gemm qkv N=6144", "llama3_8b_preattn", "gemm", {"N": 6144}),
+    ("llama3_8b_preattn mx_gemm ffn-up N=14336", "llama3_8b_preattn", "gemm", {"N": 14336}),
 )
+
+PEAK_MXFP8_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
 
 
 def algorithmic_bytes(op, T, D, elem):
@@ -53,7 +60,48 @@ def algorithmic_bytes(op, T, D, elem):
     return T * (2 * D + code + D // 32)
 
 
+def run_gemm(torch, name, wl, opt, steps, warmup):
+    x0, g = workloads.make_inputs(wl, device="cuda")
+    M, K = x0.shape
+    N = opt["N"]
+    A, SA, _ = mxq.mxnorm(x0, None, 2.0)
+    w = workloads.random_rows(N, K, seed=11, device="cuda", scale=0.02)
+    B, SB = mxq.mxcast((w.float() * g.float()[None, :]).to(torch.bfloat16))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    L = mxq.lib()
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    args = (vp(A.data_ptr()), K, vp(SA.data_ptr()), K // 32, vp(B.data_ptr()), K, vp(SB.data_ptr()),
+            K // 32, M, N, K, mxq.MXQ_E4M3, mxq.MXQ_E4M3, vp(C.data_ptr()), N, mxq.MXQ_OUT_BF16,
+            stream)
+
+    def launch(i):
+        st = L.mx_gemm(*args)
+        if st != mxq.MXQ_OK:
+            raise mxq.MxqError(st, name)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        launch(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    print(f"{name:44s} M={M:6d} N={N:6d} K={K:5d} {us:9.2f} us/launch (events, back-to-back)  "
+          f"{tflops:8.1f} TFLOP/s  {100 * tflops / PEAK_MXFP8_TFLOPS:5.1f}% of MXFP8 peak",
+          flush=True)
+    del A, SA, B, SB, C
+    torch.cuda.empty_cache()
+
+
 def run_case(torch, name, wl, op, opt, steps, warmup):
+    if op == "gemm":
+        return run_gemm(torch, name, wl, opt, steps, warmup)
     w = workloads.WORKLOADS[wl]
     x0, g = workloads.make_inputs(wl, device="cuda")
     T, D = x0.shape

@@ -206,3 +206,31 @@ def test_backward_workspace_grows_slowly_with_rows():
     small = mxq.mxnorm_bwd_workspace_size(64, D)
     big = mxq.mxnorm_bwd_workspace_size(1 << 20, D)
     assert small < big <= (512 + 32) * D * 4
+
+
+def gemm(**kw):
+    a = dict(a=A16, lda=4096, sa=A16, ldsa=128, b=A16, ldb=4096, sb=A16, ldsb=128, M=256, N=256,
+             K=4096, ea=0, eb=0, c=A16, ldc=256, ct=0, stream=None)
+    a.update(kw)
+    return mxq.mx_gemm(a["a"], a["lda"], a["sa"], a["ldsa"], a["b"], a["ldb"], a["sb"], a["ldsb"],
+                       a["M"], a["N"], a["K"], a["ea"], a["eb"], a["c"], a["ldc"], a["ct"],
+                       a["stream"])
+
+
+def test_gemm_argument_errors():
+    assert gemm(K=0) == mxq.MXQ_ERR_SHAPE
+    assert gemm(K=100) == mxq.MXQ_ERR_SHAPE
+    assert gemm(M=-1) == mxq.MXQ_ERR_SHAPE
+    assert gemm(lda=2048) == mxq.MXQ_ERR_SHAPE
+    assert gemm(ldsb=64) == mxq.MXQ_ERR_SHAPE
+    assert gemm(ldc=100) == mxq.MXQ_ERR_SHAPE
+    assert gemm(ea=3) == mxq.MXQ_ERR_ARG
+    assert gemm(ct=2) == mxq.MXQ_ERR_ARG
+    assert gemm(ea=1) == mxq.MXQ_ERR_UNSUPPORTED           # E2M1 operands are reserved
+    assert gemm(K=160, lda=160, ldb=160, ldsa=8, ldsb=8) == mxq.MXQ_ERR_UNSUPPORTED  # K % 128
+    assert gemm(a=None) == mxq.MXQ_ERR_NULL
+    assert gemm(c=None) == mxq.MXQ_ERR_NULL
+    assert gemm(a=A8) == mxq.MXQ_ERR_ALIGN
+    assert gemm(lda=4104) == mxq.MXQ_ERR_ALIGN
+    assert gemm(ldsa=130) == mxq.MXQ_ERR_ALIGN
+    assert gemm(M=0, a=None, sa=None, b=None, sb=None, c=None) == mxq.MXQ_OK
