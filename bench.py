@@ -30,7 +30,9 @@ WORKLOAD = "llama3_8b_preattn"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE = 10
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_mxnorm_fwd_llama3_8b.json")
-KERNEL_SRC = os.path.join(ROOT, "norm_mx_quantisation_amd", "csrc", "mxq.hip")
+# the sources the fused forward kernel is built from
+KERNEL_SRCS = [os.path.join(ROOT, "norm_mx_quantisation_amd", "csrc", f)
+               for f in ("mxq.hip", "mxq_device.h")]
 
 
 def fused_bytes(T, D, elem="e4m3"):
@@ -45,8 +47,11 @@ def two_pass_bytes(T, D):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():

@@ -7,7 +7,8 @@ import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "mxq.hip"), os.path.join(PKG, "csrc", "mx_gemm.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("mxq.hip", "mxq_bwd.hip", "mx_gemm.hip")]
+DEV_HDR = os.path.join(PKG, "csrc", "mxq_device.h")
 HDR = os.path.join(ROOT, "include", "mxq.h")
 LIB = os.path.join(PKG, "libmxq.so")
 
@@ -23,7 +24,7 @@ FLAGS = [
 
 def build(force: bool = True, verbose: bool = False) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
-            os.path.getmtime(p) for p in SRCS + [HDR]):
+            os.path.getmtime(p) for p in SRCS + [HDR, DEV_HDR]):
         return LIB
     with tempfile.TemporaryDirectory() as tmpdir:
         objs, procs = [], []

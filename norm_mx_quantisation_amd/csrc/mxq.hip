@@ -33,10 +33,8 @@
 
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kChunk = 512;           // elements per wave-wide chunk
-constexpr int kRowsPerBlock = 4;      // wavefronts (rows) per workgroup
-constexpr int kThreads = kWave * kRowsPerBlock;
+#include "mxq_device.h"
+
 constexpr int kCastChunksPerWave = 4; // MXCast chunks per wavefront
 
 enum PMode { P_ONE = 0, P_TWO = 1, P_INF = 2, P_GEN = 3 };
@@ -47,112 +45,6 @@ enum PMode { P_ONE = 0, P_TWO = 1, P_INF = 2, P_GEN = 3 };
 enum Stat { S_PMEAN = 0, S_RMS = 1 };
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// ------------------------------------------------------------------ bf16
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ void unpack8(const uint4& r, float v[8]) {
-  v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
-  v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
-  v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
-  v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
-}
-
-// Largest |x| of 8 bf16 values as a bit pattern with the sign cleared. For
-// non-negative bf16 the integer order is the magnitude order, with +Inf
-// (0x7F80) below every NaN, so a non-finite element always surfaces.
-__device__ __forceinline__ uint32_t absmax_bits8(const uint4& r) {
-  const uint32_t k = 0x7FFF7FFFu;
-  u16x2 a = __builtin_bit_cast(u16x2, r.x & k);
-  u16x2 b = __builtin_bit_cast(u16x2, r.y & k);
-  u16x2 c = __builtin_bit_cast(u16x2, r.z & k);
-  u16x2 d = __builtin_bit_cast(u16x2, r.w & k);
-  u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                      __builtin_elementwise_max(c, d));
-  uint32_t mm = __builtin_bit_cast(uint32_t, m);
-  return max(mm & 0xFFFFu, mm >> 16);
-}
-
-// Cross-lane moves that stay in the VALU (no LDS round trip): DPP within a
-// quad and within a row of 16 lanes; across rows, lane reads into scalar
-// registers (over_quads below).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
-constexpr int kDppRowMirror = 0x140;    // lane i <-> 15 - i within a row of 16
-constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within 8 lanes
-
-// Max over the 4 lanes of a quad (one MX block); exact, so any order is fine.
-__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  v = max(v, dpp<kDppQuadSwap1>(v));
-  v = max(v, dpp<kDppQuadSwap2>(v));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t f32_add_bits(uint32_t a, uint32_t b) {
-  return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
-}
-
-// Butterfly over the 16 quads of a wave for a value each quad holds in all 4
-// lanes, with a commutative op: quad q meets q ^ 1 (half mirror), then pairs
-// meet pairs (row mirror), so every lane of a row of 16 holds its row's
-// value; the four row values are read into scalar registers and combined as
-// (row0 op row1) op (row2 op row3). The result is wave-uniform, and the
-// combining tree is the one an XOR butterfly over lane distances 4, 8, 16, 32
-// builds.
-template <class Op>
-__device__ __forceinline__ uint32_t over_quads(uint32_t v, Op op) {
-  v = op(v, dpp<kDppHalfMirror>(v));
-  v = op(v, dpp<kDppRowMirror>(v));
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)op(op(r0, r1), op(r2, r3)));
-}
-
-// Sum over the 16 quads of a value held identically by each quad's 4 lanes.
-__device__ __forceinline__ float sum_over_quads(float v) {
-  return __uint_as_float(over_quads(__float_as_uint(v), f32_add_bits));
-}
-
-__device__ __forceinline__ uint32_t max_over_quads(uint32_t v) {
-  return over_quads(v, [](uint32_t a, uint32_t b) { return max(a, b); });
-}
-
-// Sum over all 64 lanes: lane pairs, then pairs of pairs within each quad,
-// then over the quads.
-__device__ __forceinline__ float sum_over_wave(float v) {
-  uint32_t u = __float_as_uint(v);
-  u = f32_add_bits(u, dpp<kDppQuadSwap1>(u));
-  u = f32_add_bits(u, dpp<kDppQuadSwap2>(u));
-  return sum_over_quads(__uint_as_float(u));
-}
-
-// Adds the squares of 8 bf16 values to s, in element order.
-__device__ __forceinline__ float sumsq8(const uint4& r, float s) {
-  float v[8];
-  unpack8(r, v);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s = __builtin_fmaf(v[j], v[j], s);
-  return s;
-}
-
-// RMSNorm's normaliser 1 / sqrt(S / D + eps) from a lane's partial sum of
-// squares: the lanes' sums are added by the wave butterfly. Every RMS path
-// (two-pass and single-pass, register and LDS rows) sums in this order: each
-// lane its chunks in chunk order, then the butterfly, so all give the same bits.
-__device__ __forceinline__ float rms_normaliser(float lane_sum, float Df, float eps) {
-  const float s = sum_over_wave(lane_sum);
-  return 1.0f / sqrtf(s / Df + eps);
-}
 
 // ------------------------------------------------------------------ p-mean
 
@@ -359,28 +251,6 @@ __device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], uint32_t c
 
 // ------------------------------------------------------------------ memory
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-// The activation is read exactly once and the codes are written once: both
-// go through non-temporal accesses.
-__device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Chunk c of a row, 16 bytes per lane. A lane whose 8 elements lie past the
-// row end reads the row's last 16 bytes instead, so every load is
-// unconditional and in bounds (a predicated load would make the compiler wait
-// for earlier loads); callers mask such lanes where the data is used.
-__device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int c, int dl, int D) {
-  return load16_stream(xr + min(c * kChunk + dl, D - 8));
-}
-
 __device__ __forceinline__ void store8_stream(uint8_t* p, uint2 v) {
   const u32x2 w = {v.x, v.y};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
@@ -390,7 +260,6 @@ __device__ __forceinline__ void store4_stream(uint8_t* p, uint32_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
 
-// Encode and store 8 elements at element offset n of a contiguous code tensor.
 // Encodes the 8 elements at column d of a row and stores them. codes_row is
 // the row's first code byte (uniform across the wave, so the store takes a
 // scalar base and a 32-bit lane offset); n = row * D + d is the logical
@@ -570,12 +439,6 @@ struct GammaStage {
   }
 };
 
-__device__ __forceinline__ void gains(const float4* g_lds, int c, int lane, float g[8]) {
-  const float4 a = g_lds[(2 * c) * kWave + lane];
-  const float4 b = g_lds[(2 * c + 1) * kWave + lane];
-  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
-}
 
 // The rest of a register-resident row once its chunks are loaded: block
 // maxima and the normaliser, then each chunk's products, scale, cast and
@@ -755,11 +618,6 @@ struct RmsArgs {
   float eps;
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)a);  // round to nearest even
-  const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
-}
 
 template <bool GAMMA>
 __device__ __forceinline__ void rms_chunk_out(const RmsArgs& A, int64_t row, int d, const uint4& xb,
@@ -885,247 +743,9 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
   }
 }
 
-// ------------------------------------------------------------------ backward
-
-// Straight-through backward (MXNorm page, §2.3, gradient paragraph): the cast
-// counts as the identity and RMSNorm's gradient is taken with the forward's
-// normaliser inv = 1/G:  g = gamma * dy,  s = sum_i g_i x_i,
-// dx_i = inv * g_i - inv^3 * (s / D) * x_i,  dgamma_i = sum_t dy_ti x_ti inv_t.
-// fp32 order: g and dy * x are exact products of two bf16 values; s sums in
-// chunk order per lane, then over the wave as every RMS path does;
-// k = (inv * inv) * inv, c = k * (s / D), dx = bf16(inv * g - c * x).
-struct BwdArgs {
-  const uint16_t* x;
-  const uint16_t* dy;
-  const uint16_t* gamma;
-  const float* inv;
-  uint16_t* dx;
-  float* row_dot;
-  float* partial;   // [groups][D] fp32 dgamma partials, or null
-  int64_t ldx;
-  int64_t lddy;
-  int64_t T;
-  int D;
-  float Df;
-  int rows_per_group;  // rows per workgroup, a multiple of kRowsPerBlock
-};
-
-// One workgroup of 4 waves takes rows [g R, g R + R); wave w takes rows
-// g R + w, g R + w + 4, ... in order and keeps its dgamma sums in registers
-// (chunk c, element j of lane l is column 512 c + 8 l + j). The 4 waves'
-// sums are combined as (w0 + w2) + (w1 + w3) through LDS into the group's
-// partial row. KEEP holds the row's x and dy in registers between the two
-// passes (D <= 4096); otherwise the second pass loads them again (from L2).
-template <int NC, bool GAMMA, bool DGAMMA, bool KEEP>
-__global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
-  __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
-  __shared__ float red[DGAMMA ? 2 * NC * 8 * kWave : 1];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int dl = lane * 8;
-  const int64_t row0 = (int64_t)blockIdx.x * A.rows_per_group;
-  const int64_t row_end = min(A.T, row0 + A.rows_per_group);
-
-  if (GAMMA) {
-    for (int i = threadIdx.x; i < NC * kWave; i += kThreads) {
-      float v[8];
-      unpack8(i * 8 < A.D ? load16(A.gamma + i * 8) : make_uint4(0, 0, 0, 0), v);
-      const int c = i / kWave, l = i % kWave;
-      g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
-      g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
-    }
-    __syncthreads();
-  }
-
-  float acc[DGAMMA ? NC : 1][8];
-  if (DGAMMA) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[c][j] = 0.0f;
-  }
-
-  // KEEP: the row's packed x and dy in registers. With dgamma a wave walks
-  // several rows, and its next row is prefetched into xn / dn while this one
-  // is processed; without, each wave has one row.
-  constexpr bool PREFETCH = KEEP && DGAMMA;
-  uint4 xk[KEEP ? NC : 1], dk[KEEP ? NC : 1], xn[PREFETCH ? NC : 1], dn[PREFETCH ? NC : 1];
-  if (PREFETCH && row0 + wave < row_end) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      xn[c] = load_chunk(A.x + (row0 + wave) * A.ldx, c, dl, A.D);
-      dn[c] = load_chunk(A.dy + (row0 + wave) * A.lddy, c, dl, A.D);
-    }
-  }
-  for (int64_t row = row0 + wave; row < row_end; row += kRowsPerBlock) {
-    const uint16_t* xr = A.x + row * A.ldx;
-    const uint16_t* dr = A.dy + row * A.lddy;
-    float s = 0.0f;
-    float g[8] = {1, 1, 1, 1, 1, 1, 1, 1};
-    if (KEEP && !PREFETCH) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        xk[c] = load_chunk(xr, c, dl, A.D);
-        dk[c] = load_chunk(dr, c, dl, A.D);
-      }
-    }
-    if (PREFETCH) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        xk[c] = xn[c];
-        dk[c] = dn[c];
-      }
-      const int64_t next = row + kRowsPerBlock;
-      if (next < row_end) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          xn[c] = load_chunk(A.x + next * A.ldx, c, dl, A.D);
-          dn[c] = load_chunk(A.dy + next * A.lddy, c, dl, A.D);
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c * kChunk + dl < A.D) {
-        float xv[8], dv[8];
-        unpack8(KEEP ? xk[c] : load16(xr + c * kChunk + dl), xv);
-        unpack8(KEEP ? dk[c] : load16(dr + c * kChunk + dl), dv);
-        if (GAMMA) gains(g_lds, c, lane, g);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s = __builtin_fmaf(g[j] * dv[j], xv[j], s);
-      }
-    }
-    if (KEEP) {
-      // keep the packed row: widen again in the second pass rather than hold
-      // both passes' fp32 copies (see mxnorm_row_reg)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        asm volatile("" : "+v"(xk[c].x), "+v"(xk[c].y), "+v"(xk[c].z), "+v"(xk[c].w));
-        asm volatile("" : "+v"(dk[c].x), "+v"(dk[c].y), "+v"(dk[c].z), "+v"(dk[c].w));
-      }
-    }
-    s = sum_over_wave(s);
-    const float a = A.inv[row];
-    if (lane == 0 && A.row_dot) A.row_dot[row] = s;
-    const float k = (a * a) * a;
-    const float cf = k * (s / A.Df);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int d = c * kChunk + dl;
-      if (d < A.D) {
-        float xv[8], dv[8], o[8];
-        unpack8(KEEP ? xk[c] : load16(xr + d), xv);
-        unpack8(KEEP ? dk[c] : load16(dr + d), dv);
-        if (GAMMA) gains(g_lds, c, lane, g);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = a * (g[j] * dv[j]) - cf * xv[j];
-        uint4 w;
-        w.x = pack_bf16x2(o[0], o[1]);
-        w.y = pack_bf16x2(o[2], o[3]);
-        w.z = pack_bf16x2(o[4], o[5]);
-        w.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(A.dx + (uint64_t)row * (uint64_t)A.D + (uint64_t)d) = w;
-        if (DGAMMA) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[c][j] += (dv[j] * xv[j]) * a;
-        }
-      }
-    }
-  }
-
-  if (DGAMMA) {
-    // red: two slots of [chunk][element][lane] floats
-    auto slot = [&](int sl, int c, int j) -> float& { return red[((sl * NC + c) * 8 + j) * kWave + lane]; };
-    if (wave >= 2) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) slot(wave - 2, c, j) = acc[c][j];
-    }
-    __syncthreads();
-    if (wave < 2) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[c][j] += slot(wave, c, j);
-    }
-    __syncthreads();
-    if (wave == 1) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) slot(0, c, j) = acc[c][j];
-    }
-    __syncthreads();
-    if (wave == 0) {
-      float* out = A.partial + (uint64_t)blockIdx.x * (uint64_t)A.D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int d = c * kChunk + dl;
-        if (d < A.D) {
-          float r[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) r[j] = acc[c][j] + slot(0, c, j);
-          *reinterpret_cast<float4*>(out + d) = make_float4(r[0], r[1], r[2], r[3]);
-          *reinterpret_cast<float4*>(out + d + 4) = make_float4(r[4], r[5], r[6], r[7]);
-        }
-      }
-    }
-  }
-}
-
-// out[s][d] = sum of in[r][d] over the rows r of segment s ([s * seg,
-// s * seg + seg) clipped to rows). A workgroup covers 64 float4 columns of one
-// segment; wave w adds rows [w * q, w * q + q) of the segment in row order
-// (q = ceil(seg / 4); loads batched 8 deep), and the four wave sums combine as
-// (w0 + w1) + (w2 + w3). With rows == 0 it writes zeros.
-__global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int rows, int D4, int seg,
-                                                           float* out) {
-  __shared__ float4 part[3][kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int q = blockIdx.x * kWave + lane;
-  const int qc = min(q, D4 - 1);  // lanes past the last column stay in bounds, store nothing
-  const int per = (seg + 3) / 4;
-  const int r0 = blockIdx.y * seg + wave * per;
-  const int r1 = min(min(rows, blockIdx.y * seg + seg), r0 + per);
-  const float4* src = reinterpret_cast<const float4*>(in);
-  float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  int r = r0;
-  for (; r + 8 <= r1; r += 8) {  // 8 loads in flight, then added in row order
-    float4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(r + u) * D4 + qc];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
-    }
-  }
-  for (; r < r1; ++r) {
-    const float4 v = src[(size_t)r * D4 + qc];
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-  }
-  if (wave > 0) part[wave - 1][lane] = a;
-  __syncthreads();
-  if (wave == 0 && q < D4) {
-    const float4 b = part[0][lane], c = part[1][lane], d = part[2][lane];
-    float4 o;
-    o.x = (a.x + b.x) + (c.x + d.x);
-    o.y = (a.y + b.y) + (c.y + d.y);
-    o.z = (a.z + b.z) + (c.z + d.z);
-    o.w = (a.w + b.w) + (c.w + d.w);
-    reinterpret_cast<float4*>(out)[(size_t)blockIdx.y * D4 + q] = o;
-  }
-}
-
 // ------------------------------------------------------------------ launch helpers
 
-inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-#define MXQ_LAUNCH_CHECK()                                   \
-  do {                                                       \
-    if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP; \
-  } while (0)
 
 template <int NC, int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_reg(const NormArgs& A, hipStream_t s) {
@@ -1244,61 +864,6 @@ mxq_status dispatch_cast(const CastArgs& A, mxq_elem elem, mxq_round rnd, hipStr
   return rnd == MXQ_SR ? launch_cast<MXQ_E2M1, MXQ_SR>(A, s) : launch_cast<MXQ_E2M1, MXQ_RNE>(A, s);
 }
 
-
-// Backward launch geometry: rows per workgroup, a multiple of 4, so that at
-// most kBwdMaxGroups partial rows are written; the partials are then summed
-// in segments of kBwdSegment rows, then the segments.
-constexpr int64_t kBwdMaxGroups = 512;
-constexpr int kBwdSegment = 16;
-
-struct BwdPlan {
-  int64_t rows_per_group, groups, segments;
-  size_t workspace_bytes;
-};
-
-BwdPlan bwd_plan(int64_t T, int64_t D, bool dgamma = true) {
-  BwdPlan p;
-  // without dgamma there are no partials: one row per wave, as in the forward
-  int64_t r = dgamma ? (T + kBwdMaxGroups - 1) / kBwdMaxGroups : kRowsPerBlock;
-  r = ((r + kRowsPerBlock - 1) / kRowsPerBlock) * kRowsPerBlock;
-  p.rows_per_group = r < kRowsPerBlock ? kRowsPerBlock : r;
-  p.groups = (T + p.rows_per_group - 1) / p.rows_per_group;
-  p.segments = (p.groups + kBwdSegment - 1) / kBwdSegment;
-  p.workspace_bytes = (size_t)(p.groups + p.segments) * (size_t)D * sizeof(float);
-  return p;
-}
-
-template <int NC, bool GAMMA, bool DGAMMA>
-mxq_status launch_bwd(const BwdArgs& A, unsigned groups, hipStream_t s) {
-  hipLaunchKernelGGL((mxnorm_bwd_kernel<NC, GAMMA, DGAMMA, (NC <= 8)>), dim3(groups), dim3(kThreads), 0,
-                     s, A);
-  MXQ_LAUNCH_CHECK();
-  return MXQ_OK;
-}
-
-template <bool GAMMA, bool DGAMMA>
-mxq_status dispatch_bwd(const BwdArgs& A, int nc, unsigned groups, hipStream_t s) {
-  switch (nc) {
-#define MXQ_CASE(N) \
-  case N:           \
-    return launch_bwd<N, GAMMA, DGAMMA>(A, groups, s);
-    MXQ_CASE(1) MXQ_CASE(2) MXQ_CASE(3) MXQ_CASE(4) MXQ_CASE(5) MXQ_CASE(6) MXQ_CASE(7)
-    MXQ_CASE(8) MXQ_CASE(9) MXQ_CASE(10) MXQ_CASE(11) MXQ_CASE(12) MXQ_CASE(13) MXQ_CASE(14)
-    MXQ_CASE(15) MXQ_CASE(16)
-#undef MXQ_CASE
-    default:
-      return MXQ_ERR_UNSUPPORTED;
-  }
-}
-
-mxq_status launch_col_sum(const float* in, int rows, int D, int seg, int nseg, float* out,
-                          hipStream_t s) {
-  const int D4 = D / 4;
-  hipLaunchKernelGGL(col_sum_kernel, dim3((D4 + kWave - 1) / kWave, nseg), dim3(kThreads), 0, s,
-                     in, rows, D4, seg, out);
-  MXQ_LAUNCH_CHECK();
-  return MXQ_OK;
-}
 
 // ------------------------------------------------------------------ validation
 
@@ -1456,65 +1021,6 @@ mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_
   C.sc_vec = (D % kChunk == 0) && aligned(scales, 4);
   C.rng = make_stream(rng);
   return dispatch_cast(C, elem, rnd, (hipStream_t)stream);
-}
-
-size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D) {
-  if (T < 0 || D <= 0 || D % 32 != 0) return 0;
-  return bwd_plan(T, D).workspace_bytes;
-}
-
-mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
-                      int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
-                      float* row_dot, float* dgamma, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  if (T < 0 || D <= 0 || D % 32 != 0 || ldx < D || lddy < D) return MXQ_ERR_SHAPE;
-  if (D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
-  if ((uint64_t)T * (uint64_t)D >= (1ull << 40)) return MXQ_ERR_UNSUPPORTED;
-  const BwdPlan plan = bwd_plan(T, D, dgamma != nullptr);
-  if (dgamma != nullptr) {
-    if (workspace == nullptr) return MXQ_ERR_NULL;
-    if (workspace_bytes < plan.workspace_bytes) return MXQ_ERR_ARG;
-    if (!aligned(dgamma, 16) || !aligned(workspace, 16)) return MXQ_ERR_ALIGN;
-  }
-  hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {
-    // nothing to read; the gain's gradient of an empty batch is zero
-    return dgamma ? launch_col_sum(nullptr, 0, (int)D, 1, 1, dgamma, s) : MXQ_OK;
-  }
-  if (x == nullptr || dy == nullptr || inv_norm == nullptr || dx == nullptr) return MXQ_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || ldx % 8 != 0 || lddy % 8 != 0)
-    return MXQ_ERR_ALIGN;
-  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
-  if (!aligned(inv_norm, 4) || (row_dot != nullptr && !aligned(row_dot, 4))) return MXQ_ERR_ALIGN;
-
-  BwdArgs A;
-  A.x = x;
-  A.dy = dy;
-  A.gamma = gamma;
-  A.inv = inv_norm;
-  A.dx = dx;
-  A.row_dot = row_dot;
-  A.partial = dgamma ? static_cast<float*>(workspace) : nullptr;
-  A.ldx = ldx;
-  A.lddy = lddy;
-  A.T = T;
-  A.D = (int)D;
-  A.Df = (float)D;
-  A.rows_per_group = (int)plan.rows_per_group;
-  const int nc = (int)((D + kChunk - 1) / kChunk);
-  const unsigned groups = (unsigned)plan.groups;
-  const bool g = gamma != nullptr;
-  mxq_status st;
-  if (dgamma)
-    st = g ? dispatch_bwd<true, true>(A, nc, groups, s) : dispatch_bwd<false, true>(A, nc, groups, s);
-  else
-    st = g ? dispatch_bwd<true, false>(A, nc, groups, s) : dispatch_bwd<false, false>(A, nc, groups, s);
-  if (st != MXQ_OK || dgamma == nullptr) return st;
-  // partials [groups][D] -> segment sums [segments][D] -> dgamma [D]
-  float* seg = static_cast<float*>(workspace) + (size_t)plan.groups * (size_t)D;
-  st = launch_col_sum(A.partial, (int)plan.groups, (int)D, kBwdSegment, (int)plan.segments, seg, s);
-  if (st != MXQ_OK) return st;
-  return launch_col_sum(seg, (int)plan.segments, (int)D, (int)plan.segments, 1, dgamma, s);
 }
 
 const char* mxq_strerror(mxq_status status) {
