@@ -206,6 +206,8 @@ typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;
  *   a_scales, b_scales  E8M0 bytes, ldsa / ldsb per row (>= K/32, % 4 == 0),
  *              4-byte aligned.
  *   elem_a, elem_b  MXQ_E4M3 (MXQ_E2M1 is reserved: UNSUPPORTED).
+ *   c          aligned to its element; 16-byte (fp32) or 8-byte (bf16) aligned
+ *              rows with ldc % 4 == 0 take vector stores.
  * Errors: SHAPE (M, N < 0, K <= 0, K % 32, a leading dimension too small), ARG
  * (unknown element or output type), UNSUPPORTED (E2M1, K % 128 != 0, sizes of
  * 2^31 or more), NULL, ALIGN, HIP. M == 0 or N == 0 is a no-op.

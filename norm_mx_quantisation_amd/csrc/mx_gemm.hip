@@ -14,9 +14,13 @@
 // K block b (32 columns) of row r is the low byte of lane r + 16 b's scale
 // register, whose other bytes must be zero. The result's
 // lane l holds column l % 16, rows 4 (l / 16) + i in its 4 registers.
+// Here the instruction takes B as its row operand and A as its column
+// operand, so each lane's 4 registers are 4 consecutive columns of C.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "mxq.h"
 
@@ -42,6 +46,7 @@ struct GemmArgs {
   int64_t lda, ldsa, ldb, ldsb, ldc;  // code bytes, scale bytes, C elements per row
   int M, N, K;
   int tiles_m, tiles_n;
+  int vec;  // C rows allow 4-element vector stores (aligned base, ldc % 4 == 0)
 };
 
 // One K step of both operands in LDS. Code rows hold 8 chunks of 16 bytes;
@@ -105,25 +110,38 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mx_gemm_e4m3_kernel(GemmArgs G) {
-  __shared__ Stage S;
+  __shared__ Stage S[2];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;   // wave's 128 x 128 quarter of the tile
 
-  // Tile order: the 8 XCDs take workgroup ids round robin, so id i is first
-  // mapped to slot (i % 8) * (n / 8) + i / 8, giving each XCD (and its L2) a
-  // contiguous run of the sequence; the sequence walks groups of 4 tile rows
-  // column by column, so neighbours share A rows or B rows.
+  // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = grid
+  // size, a multiple of 8), walked as one flattened sequence of (tile, K
+  // step) pairs, so the next tile's first DMA streams during this tile's last
+  // step and the epilogue's stores drain while the next tile computes.
   const int nb = G.tiles_m * G.tiles_n;
-  int pid = blockIdx.x;
-  if (nb % 8 == 0) pid = (pid % 8) * (nb / 8) + pid / 8;
-  constexpr int kGroup = 4;
-  const int group = pid / (kGroup * G.tiles_n);
-  const int first = group * kGroup;
-  const int gsz = min(G.tiles_m - first, kGroup);
-  const int in_group = pid % (kGroup * G.tiles_n);
-  const int m0 = (first + in_group % gsz) * kBM;
-  const int n0 = (in_group / gsz) * kBN;
+  const int nk = G.K / kBK;
+  const int my_tiles = (nb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int total = my_tiles * nk;
+  const int g = lane >> 4;
+  const int rl = lane & 15;
+
+  // Tile order: the 8 XCDs take workgroup ids round robin, so tile t is first
+  // mapped to slot (t % 8) * (n / 8) + t / 8, giving each XCD (and its L2) a
+  // contiguous run of the sequence (tiles b + j G stay on b's XCD); the
+  // sequence walks groups of 4 tile rows column by column, so neighbours
+  // share A rows or B rows.
+  auto tile_origin = [&](int t, int& m0, int& n0) {
+    int pid = t;
+    if (nb % 8 == 0) pid = (pid % 8) * (nb / 8) + pid / 8;
+    constexpr int kGroup = 4;
+    const int group = pid / (kGroup * G.tiles_n);
+    const int first = group * kGroup;
+    const int gsz = min(G.tiles_m - first, kGroup);
+    const int in_group = pid % (kGroup * G.tiles_n);
+    m0 = (first + in_group % gsz) * kBM;
+    n0 = (in_group / gsz) * kBN;
+  };
 
   v4f acc[8][8];
 #pragma unroll
@@ -131,63 +149,105 @@ void mx_gemm_e4m3_kernel(GemmArgs G) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = G.K / kBK;
-  const int g = lane >> 4;
-  const int rl = lane & 15;
-
-  // Per step: wait for the step's DMA, read every operand and scale this
-  // wave needs into registers, release the buffer, start the next step's DMA
-  // into it, and run the 64 MFMAs while that is in flight. The compiler's own
-  // wait before LDS reads (any read may alias an LDS DMA) falls where the
-  // step needs its data anyway.
-  load_stage(G, S, m0, n0, 0, wave, lane);
+  // Two LDS stages. Per step: wait for the step's DMA (the only memory
+  // loads in flight), barrier, issue every LDS read of the step's operands
+  // and scales, then the next step's DMA into the other stage, then the 64
+  // MFMAs, which consume the reads as they land. No LDS read follows a DMA in
+  // program order within the step, so the compiler's wait before LDS reads
+  // (any read may alias an LDS DMA in flight) never fires; the DMA overlaps
+  // the MFMAs and the reads overlap the first MFMAs. The barrier also orders
+  // the refill of a stage after every wave's reads of it, two steps earlier.
+  int m0, n0;
+  tile_origin(blockIdx.x, m0, n0);
+  if (total > 0) load_stage(G, S[0], m0, n0, 0, wave, lane);
+  for (int jt = 0; jt < my_tiles; ++jt) {
   for (int ks = 0; ks < nk; ++ks) {
+    const int step = jt * nk + ks;
+    Stage& cur = S[step & 1];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();  // every wave's share of this step is in LDS
     v8i ao[8], bo[8];
     int sav[8], sbv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int ra = wm * 128 + i * 16 + rl;
-      ao[i] = operand(S.a, ra, g);
-      sav[i] = (int)((S.sa[ra] >> (8 * g)) & 0xFFu);  // the other bytes must be zero
       const int rb = wn * 128 + i * 16 + rl;
-      bo[i] = operand(S.b, rb, g);
-      sbv[i] = (int)((S.sb[rb] >> (8 * g)) & 0xFFu);
+      bo[i] = operand(cur.b, rb, g);
+      sbv[i] = (int)((cur.sb[rb] >> (8 * g)) & 0xFFu);  // the other bytes must be zero
+      const int ra = wm * 128 + i * 16 + rl;
+      ao[i] = operand(cur.a, ra, g);
+      sav[i] = (int)((cur.sa[ra] >> (8 * g)) & 0xFFu);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier();  // every wave holds its operands: the buffer may be refilled
-    if (ks + 1 < nk) load_stage(G, S, m0, n0, ks + 1, wave, lane);
+    if (step + 1 < total) {
+      int nm0 = m0, nn0 = n0;
+      if (ks + 1 == nk) tile_origin(blockIdx.x + (jt + 1) * gridDim.x, nm0, nn0);
+      load_stage(G, S[(step + 1) & 1], nm0, nn0, ks + 1 == nk ? 0 : ks + 1, wave, lane);
+    }
+    // the instruction computes B A^T here (B as its row operand), so that each
+    // lane ends with 4 consecutive columns of C for the epilogue
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ao[i], bo[j], acc[i][j], 0, 0, 0,
-                                                                     sav[i], 0, sbv[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bo[j], ao[i], acc[i][j], 0, 0, 0,
+                                                                     sbv[j], 0, sav[i]);
   }
 
-  // lane holds column rl of each 16 x 16 block, rows 4 g .. 4 g + 3; a tile
-  // wholly inside C stores without per-element checks
-  const bool full = m0 + kBM <= G.M && n0 + kBN <= G.N;
+    // Epilogue of the tile. acc[i][j] holds (B A^T) for B rows j*16 + 4g .. +3
+    // and A row i*16 + rl: lane (rl, g) has C[row i*16 + rl][columns
+    // j*16 + 4g .. +3], stored as one 8-byte (bf16) or 16-byte (fp32) store; a
+    // tile wholly inside C stores without per-element checks.
+    const bool full = G.vec && m0 + kBM <= G.M && n0 + kBN <= G.N;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int row = m0 + wm * 128 + i * 16 + rl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = n0 + wn * 128 + j * 16 + rl;
+      for (int j = 0; j < 8; ++j) {
+        const int col = n0 + wn * 128 + j * 16 + 4 * g;
+        const v4f v = acc[i][j];
+        acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if (full || (G.vec && row < G.M && col + 3 < G.N)) {
+          if (OUT_BF16) {
+            const uint2 w = make_uint2((uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
+                                       (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16));
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(G.c) + (int64_t)row * G.ldc + col) = w;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(G.c) + (int64_t)row * G.ldc + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else if (row < G.M) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 128 + i * 16 + 4 * g + e;
-        if (full || (row < G.M && col < G.N)) {
-          if (OUT_BF16)
-            static_cast<uint16_t*>(G.c)[(int64_t)row * G.ldc + col] = bf16_rne(acc[i][j][e]);
-          else
-            static_cast<float*>(G.c)[(int64_t)row * G.ldc + col] = acc[i][j][e];
+          for (int e = 0; e < 4; ++e) {
+            if (col + e < G.N) {
+              if (OUT_BF16)
+                static_cast<uint16_t*>(G.c)[(int64_t)row * G.ldc + col + e] = bf16_rne(v[e]);
+              else
+                static_cast<float*>(G.c)[(int64_t)row * G.ldc + col + e] = v[e];
+            }
+          }
         }
       }
     }
+    if (jt + 1 < my_tiles) tile_origin(blockIdx.x + (jt + 1) * gridDim.x, m0, n0);
+  }
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Compute units of the current device, cached per device (one workgroup per
+// CU: the kernel's registers and LDS allow no more).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 }  // namespace
 
@@ -206,7 +266,8 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   if (M == 0 || N == 0) return MXQ_OK;
   if (!a || !a_scales || !b || !b_scales || !c) return MXQ_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 || ldb % 16 || !aligned(a_scales, 4) ||
-      !aligned(b_scales, 4) || ldsa % 4 || ldsb % 4 || !aligned(c, 4))
+      !aligned(b_scales, 4) || ldsa % 4 || ldsb % 4 ||
+      !aligned(c, c_type == MXQ_OUT_BF16 ? 2 : 4))
     return MXQ_ERR_ALIGN;
   GemmArgs G;
   G.a = a;
@@ -224,7 +285,15 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   G.K = (int)K;
   G.tiles_m = (int)((M + kBM - 1) / kBM);
   G.tiles_n = (int)((N + kBN - 1) / kBN);
-  const unsigned grid = (unsigned)(G.tiles_m * G.tiles_n);
+  G.vec = (ldc % 4 == 0) && aligned(c, c_type == MXQ_OUT_BF16 ? 8 : 16);
+  // persistent grid: one workgroup per CU, a multiple of 8 (one per XCD
+  // round-robin slot), at most one per tile
+  const int nb = G.tiles_m * G.tiles_n;
+  const int cus = cu_count();
+  if (cus <= 0) return MXQ_ERR_HIP;
+  int grid_i = nb < cus ? nb : cus;
+  if (grid_i >= 8) grid_i -= grid_i % 8;
+  const unsigned grid = (unsigned)grid_i;
   hipStream_t s = (hipStream_t)stream;
   if (c_type == MXQ_OUT_BF16)
     hipLaunchKernelGGL(mx_gemm_e4m3_kernel<true>, dim3(grid), dim3(kThreads), 0, s, G);

@@ -233,4 +233,5 @@ def test_gemm_argument_errors():
     assert gemm(a=A8) == mxq.MXQ_ERR_ALIGN
     assert gemm(lda=4104) == mxq.MXQ_ERR_ALIGN
     assert gemm(ldsa=130) == mxq.MXQ_ERR_ALIGN
+    assert gemm(c=A16 + 2) == mxq.MXQ_ERR_ALIGN            # fp32 output needs 4-byte alignment
     assert gemm(M=0, a=None, sa=None, b=None, sb=None, c=None) == mxq.MXQ_OK
