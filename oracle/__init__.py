@@ -28,6 +28,7 @@ E4M3, E2M1 = 0, 1
 RNE, SR = 0, 1
 ELEM = {"e4m3": E4M3, "e2m1": E2M1}
 RND = {"rne": RNE, "sr": SR}
+RULE = {"floor": 0, "ceil": 1}
 
 _lock = threading.Lock()
 _lib = None
@@ -68,6 +69,8 @@ def lib():
             L.orc_encode_array.restype = None
             L.orc_e8m0_scale.argtypes = [i32, dbl]
             L.orc_e8m0_scale.restype = ctypes.c_uint8
+            L.orc_e8m0_scale_rule.argtypes = [i32, dbl, i32]
+            L.orc_e8m0_scale_rule.restype = ctypes.c_uint8
             L.orc_philox4x32_10.argtypes = [vp, vp, vp]
             L.orc_philox4x32_10.restype = None
             L.orc_philox4x64_10.argtypes = [vp, vp, vp]
@@ -78,17 +81,17 @@ def lib():
             L.orc_sr_words.restype = None
             L.orc_pmean.argtypes = [vp, i64, dbl]
             L.orc_pmean.restype = dbl
-            L.orc_mxcast_f64.argtypes = [vp, i64, i64, i32, i32, u64, u64, vp, vp]
+            L.orc_mxcast_f64.argtypes = [vp, i64, i64, i32, i32, i32, u64, u64, vp, vp]
             L.orc_mxcast_f64.restype = i32
-            L.orc_mxcast.argtypes = [vp, i64, i64, i64, i32, i32, u64, u64, i64, vp, vp]
+            L.orc_mxcast.argtypes = [vp, i64, i64, i64, i32, i32, i32, u64, u64, i64, vp, vp]
             L.orc_mxcast.restype = i32
-            L.orc_mxnorm.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64, u64, i64,
+            L.orc_mxnorm.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, i32, u64, u64, i64,
                                      vp, vp, vp, vp]
             L.orc_mxnorm.restype = i32
-            L.orc_rmsnorm_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64, u64,
+            L.orc_rmsnorm_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, i32, u64, u64,
                                              i64, vp, vp, vp, vp, vp]
             L.orc_rmsnorm_mxcast.restype = i32
-            L.orc_rmsnorm_fused_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, u64,
+            L.orc_rmsnorm_fused_mxcast.argtypes = [vp, i64, vp, i64, i64, dbl, i32, i32, i32, u64,
                                                    u64, i64, vp, vp, vp, vp]
             L.orc_rmsnorm_fused_mxcast.restype = i32
             L.orc_mxnorm_bwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp]
@@ -158,10 +161,10 @@ def code_bytes(elem: int, D: int) -> int:
 # the operations
 # --------------------------------------------------------------------------
 
-def mxcast(x, elem="e4m3", rnd="rne", seed=0, offset=0, row_base=0, threads=1):
+def mxcast(x, elem="e4m3", rnd="rne", seed=0, offset=0, row_base=0, threads=1, rule="floor"):
     """MXCast (R mode is the only mode: the result is unique). Returns (codes, scales)."""
     L = lib()
-    e, r = ELEM[elem], RND[rnd]
+    e, r, ru = ELEM[elem], RND[rnd], RULE[rule]
     x, T, D, ldx = _rows_view(as_bf16_bits(x))
     codes = np.zeros((T, code_bytes(e, D)), np.uint8)
     scales = np.zeros((T, D // 32), np.uint8)
@@ -169,14 +172,14 @@ def mxcast(x, elem="e4m3", rnd="rne", seed=0, offset=0, row_base=0, threads=1):
 
     def job(r0, r1):
         return lambda: L.orc_mxcast(ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, r1 - r0, D, e, r,
-                                    seed, offset, row_base + r0, _ptr(codes[r0:]),
+                                    ru, seed, offset, row_base + r0, _ptr(codes[r0:]),
                                     _ptr(scales[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return codes, scales
 
 
 def mxnorm(x, gamma=None, p=2.0, elem="e4m3", rnd="rne", seed=0, offset=0,
-           inv_inject=None, row_base=0, threads=1):
+           inv_inject=None, row_base=0, threads=1, rule="floor"):
     """Fused MXNorm -> MX cast. inv_inject=None: mode (R); else mode (I) with the
     given fp32 per-row normalisers. Returns (codes, scales, inv float64 [T])."""
     L = lib()
@@ -192,15 +195,15 @@ def mxnorm(x, gamma=None, p=2.0, elem="e4m3", rnd="rne", seed=0, offset=0,
 
     def job(r0, r1):
         return lambda: L.orc_mxnorm(
-            ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(p), e, r, seed,
-            offset, row_base + r0, None if inj is None else _ptr(inj[r0:]), _ptr(codes[r0:]),
-            _ptr(scales[r0:]), _ptr(inv[r0:]))
+            ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(p), e, r,
+            RULE[rule], seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
+            _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return codes, scales, inv
 
 
 def rmsnorm_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offset=0,
-                   inv_inject=None, row_base=0, threads=1):
+                   inv_inject=None, row_base=0, threads=1, rule="floor"):
     """Two-pass RMSNorm (bf16 y) -> MXCast(y). Returns (y uint16, codes, scales, inv)."""
     L = lib()
     e, r = ELEM[elem], RND[rnd]
@@ -217,14 +220,14 @@ def rmsnorm_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offs
     def job(r0, r1):
         return lambda: L.orc_rmsnorm_mxcast(
             ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(eps), e, r,
-            seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
+            RULE[rule], seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
             _ptr(y[r0:]), _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return y, codes, scales, inv
 
 
 def rmsnorm_fused_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offset=0,
-                         inv_inject=None, row_base=0, threads=1):
+                         inv_inject=None, row_base=0, threads=1, rule="floor"):
     """Single-pass exact-RMS normalise and MX cast (y not rounded to bf16).
     Returns (codes, scales, inv float64 [T])."""
     L = lib()
@@ -241,7 +244,7 @@ def rmsnorm_fused_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0
     def job(r0, r1):
         return lambda: L.orc_rmsnorm_fused_mxcast(
             ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(eps), e, r,
-            seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
+            RULE[rule], seed, offset, row_base + r0, None if inj is None else _ptr(inj[r0:]),
             _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return codes, scales, inv
@@ -331,8 +334,10 @@ def encode_array(elem, rnd, v, r=None) -> np.ndarray:
     return out
 
 
-def e8m0_scale(elem, amax: float) -> int:
-    return lib().orc_e8m0_scale(ELEM.get(elem, elem), float(amax))
+def e8m0_scale(elem, amax: float, rule="floor") -> int:
+    if rule == "floor":
+        return lib().orc_e8m0_scale(ELEM.get(elem, elem), float(amax))
+    return lib().orc_e8m0_scale_rule(ELEM.get(elem, elem), float(amax), RULE[rule])
 
 
 def pmean(m, p: float) -> float:
@@ -370,14 +375,14 @@ def sr_words(seed: int, offset: int, n0: int, count: int) -> np.ndarray:
     return out
 
 
-def mxcast_f64(v, elem="e4m3", rnd="rne", seed=0, offset=0, t=0):
+def mxcast_f64(v, elem="e4m3", rnd="rne", seed=0, offset=0, t=0, rule="floor"):
     """MXCast of one row of doubles; returns (unpacked codes [D], scales [D/32])."""
     a = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(-1))
     D = a.size
     codes = np.zeros(D, np.uint8)
     scales = np.zeros(D // 32, np.uint8)
-    rc = lib().orc_mxcast_f64(_ptr(a), D, t, ELEM[elem], RND[rnd], seed, offset, _ptr(codes),
-                              _ptr(scales))
+    rc = lib().orc_mxcast_f64(_ptr(a), D, t, ELEM[elem], RND[rnd], RULE[rule], seed, offset,
+                              _ptr(codes), _ptr(scales))
     if rc:
         raise ValueError(f"oracle returned error {rc}")
     return codes, scales

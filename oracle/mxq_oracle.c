@@ -69,6 +69,8 @@
 #define ORC_E2M1 1
 #define ORC_RNE 0
 #define ORC_SR 1
+#define ORC_SCALE_FLOOR 0
+#define ORC_SCALE_CEIL 1
 
 /* ------------------------------------------------------------------ */
 /* Plain helpers                                                       */
@@ -199,14 +201,29 @@ void orc_encode_array(int elem, int rnd, const double* v, const uint32_t* r, int
 }
 
 /* E8M0 block scale from the block absmax. */
-uint8_t orc_e8m0_scale(int elem, double amax) {
+/* E8M0 scale of a block with absmax amax under one of two rules:
+ *   floor (the OCP MX rule): s = floor(log2 amax) - emax;
+ *   ceil  (round the scale up): the smallest s with amax <= maxval * 2^s, so
+ *         no element of the block saturates (the pages' MXFP8 recipes abstract
+ *         mentions a specific conversion algorithm without printing it; this
+ *         is the reading that takes the scale up rather than clipping).
+ * Clamped to [-127, 127], stored as s + 127; amax == 0 gives 0, NaN/Inf 0xFF. */
+uint8_t orc_e8m0_scale_rule(int elem, double amax, int rule) {
   const fmt_t* F = fmt_of(elem);
   if (isnan(amax) || isinf(amax)) return 0xFF;
   if (amax == 0) return 0;
   int s = floor_log2(amax) - F->emax;
+  if (rule == ORC_SCALE_CEIL) {
+    while (ldexp(F->maxval, s) < amax) ++s;       /* smallest s that holds amax */
+    while (ldexp(F->maxval, s - 1) >= amax) --s;
+  }
   if (s < -127) s = -127;
   if (s > 127) s = 127;
   return (uint8_t)(s + 127);
+}
+
+uint8_t orc_e8m0_scale(int elem, double amax) {
+  return orc_e8m0_scale_rule(elem, amax, ORC_SCALE_FLOOR);
 }
 
 /* ------------------------------------------------------------------ */
@@ -266,7 +283,7 @@ void orc_sr_words(uint64_t seed, uint64_t offset, uint64_t n0, int64_t count, ui
 
 /* v: D values of row t; writes D codes (unpacked, one per byte) and D/32 scales.
  * Element index for SR is t*D + d. */
-static void mxcast_row_f64(const double* v, int64_t D, int64_t t, int elem, int rnd,
+static void mxcast_row_f64(const double* v, int64_t D, int64_t t, int elem, int rnd, int rule,
                            uint64_t seed, uint64_t offset, uint8_t* code_row,
                            uint8_t* scale_row) {
   const fmt_t* F = fmt_of(elem);
@@ -278,7 +295,7 @@ static void mxcast_row_f64(const double* v, int64_t D, int64_t t, int elem, int 
       if (!isfinite(b[i])) nonfinite = 1;
       else if (fabs(b[i]) > amax) amax = fabs(b[i]);
     }
-    uint8_t sc = orc_e8m0_scale(elem, nonfinite ? NAN : amax);
+    uint8_t sc = orc_e8m0_scale_rule(elem, nonfinite ? NAN : amax, rule);
     scale_row[k] = sc;
     for (int i = 0; i < 32; ++i) {
       uint8_t c;
@@ -307,18 +324,19 @@ static void store_codes(int elem, const uint8_t* unpacked, int64_t D, uint8_t* o
 
 static int64_t code_bytes_per_row(int elem, int64_t D) { return elem == ORC_E2M1 ? D / 2 : D; }
 
-static int check_args(int64_t T, int64_t D, int elem, int rnd, int64_t row_base) {
+static int check_args(int64_t T, int64_t D, int elem, int rnd, int rule, int64_t row_base) {
   if (T < 0 || D <= 0 || D % 32 != 0 || row_base < 0) return 2;
   if (elem != ORC_E4M3 && elem != ORC_E2M1) return 4;
   if (rnd != ORC_RNE && rnd != ORC_SR) return 4;
+  if (rule != ORC_SCALE_FLOOR && rule != ORC_SCALE_CEIL) return 4;
   return 0;
 }
 
 /* MXCast on an arbitrary row of doubles (test helper for compositions). */
-int orc_mxcast_f64(const double* v, int64_t D, int64_t t, int elem, int rnd, uint64_t seed,
-                   uint64_t offset, uint8_t* codes_unpacked, uint8_t* scales) {
-  if (check_args(1, D, elem, rnd, t)) return 2;
-  mxcast_row_f64(v, D, t, elem, rnd, seed, offset, codes_unpacked, scales);
+int orc_mxcast_f64(const double* v, int64_t D, int64_t t, int elem, int rnd, int rule,
+                   uint64_t seed, uint64_t offset, uint8_t* codes_unpacked, uint8_t* scales) {
+  if (check_args(1, D, elem, rnd, rule, t)) return 2;
+  mxcast_row_f64(v, D, t, elem, rnd, rule, seed, offset, codes_unpacked, scales);
   return 0;
 }
 
@@ -332,17 +350,17 @@ int orc_mxcast_f64(const double* v, int64_t D, int64_t t, int elem, int rnd, uin
  * or [T, D/2] (E2M1), scales [T, D/32] and the per-row arrays are contiguous. */
 
 /* MXCast of a bf16 activation. */
-int orc_mxcast(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, int elem, int rnd,
+int orc_mxcast(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, int elem, int rnd, int rule,
                uint64_t seed, uint64_t offset, int64_t row_base, uint8_t* codes,
                uint8_t* scales) {
-  int rc = check_args(T, D, elem, rnd, row_base);
+  int rc = check_args(T, D, elem, rnd, rule, row_base);
   if (rc) return rc;
   double* v = (double*)malloc(sizeof(double) * (size_t)D);
   uint8_t* cu = (uint8_t*)malloc((size_t)D);
   if (!v || !cu) { free(v); free(cu); return 6; }
   for (int64_t t = 0; t < T; ++t) {
     for (int64_t d = 0; d < D; ++d) v[d] = orc_bf16_to_f64(x[t * ldx + d]);
-    mxcast_row_f64(v, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * (D / 32));
+    mxcast_row_f64(v, D, row_base + t, elem, rnd, rule, seed, offset, cu, scales + t * (D / 32));
     store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));
   }
   free(v);
@@ -367,9 +385,10 @@ double orc_pmean(const double* m, int64_t K, double p) {
  * (I) with inv_inject[t] as the fp32 normaliser. inv_out (nullable) receives
  * the normaliser used (fp64 1/G in mode R). gamma == NULL means gamma == 1. */
 int orc_mxnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T, int64_t D,
-               double p, int elem, int rnd, uint64_t seed, uint64_t offset, int64_t row_base,
-               const float* inv_inject, uint8_t* codes, uint8_t* scales, double* inv_out) {
-  int rc = check_args(T, D, elem, rnd, row_base);
+               double p, int elem, int rnd, int rule, uint64_t seed, uint64_t offset,
+               int64_t row_base, const float* inv_inject, uint8_t* codes, uint8_t* scales,
+               double* inv_out) {
+  int rc = check_args(T, D, elem, rnd, rule, row_base);
   if (rc) return rc;
   if (!(p > 0)) return 5;
   const int64_t K = D / 32;
@@ -405,7 +424,7 @@ int orc_mxnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
       else
         y[d] = xi * gi * inv; /* x*gamma is exact in double */
     }
-    mxcast_row_f64(y, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * K);
+    mxcast_row_f64(y, D, row_base + t, elem, rnd, rule, seed, offset, cu, scales + t * K);
     store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));
   }
   free(y);
@@ -416,10 +435,10 @@ int orc_mxnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
 
 /* Two-pass comparison: RMSNorm (bf16 y) then MXCast(y). */
 int orc_rmsnorm_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
-                       int64_t D, double eps, int elem, int rnd, uint64_t seed,
+                       int64_t D, double eps, int elem, int rnd, int rule, uint64_t seed,
                        uint64_t offset, int64_t row_base, const float* inv_inject,
                        uint16_t* ybf, uint8_t* codes, uint8_t* scales, double* inv_out) {
-  int rc = check_args(T, D, elem, rnd, row_base);
+  int rc = check_args(T, D, elem, rnd, rule, row_base);
   if (rc) return rc;
   if (!(eps >= 0)) return 5;
   const int64_t K = D / 32;
@@ -448,7 +467,7 @@ int orc_rmsnorm_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, in
       ybf[t * D + d] = b;
       y[d] = orc_bf16_to_f64(b);
     }
-    mxcast_row_f64(y, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * K);
+    mxcast_row_f64(y, D, row_base + t, elem, rnd, rule, seed, offset, cu, scales + t * K);
     store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));
   }
   free(y);
@@ -462,10 +481,10 @@ int orc_rmsnorm_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, in
  * (R): inv = 1/sqrt(mean(x^2) + eps) and y = x*gamma*inv in fp64. (I): the
  * injected fp32 inv and y = RN32(RN32(x*gamma)*inv). Outputs as orc_mxnorm. */
 int orc_rmsnorm_fused_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
-                             int64_t D, double eps, int elem, int rnd, uint64_t seed,
+                             int64_t D, double eps, int elem, int rnd, int rule, uint64_t seed,
                              uint64_t offset, int64_t row_base, const float* inv_inject,
                              uint8_t* codes, uint8_t* scales, double* inv_out) {
-  int rc = check_args(T, D, elem, rnd, row_base);
+  int rc = check_args(T, D, elem, rnd, rule, row_base);
   if (rc) return rc;
   if (!(eps >= 0)) return 5;
   const int64_t K = D / 32;
@@ -491,7 +510,7 @@ int orc_rmsnorm_fused_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gam
       double gi = gamma ? orc_bf16_to_f64(gamma[d]) : 1.0;
       y[d] = inv_inject ? (double)rn32((double)rn32(xi * gi) * inv) : xi * gi * inv;
     }
-    mxcast_row_f64(y, D, row_base + t, elem, rnd, seed, offset, cu, scales + t * K);
+    mxcast_row_f64(y, D, row_base + t, elem, rnd, rule, seed, offset, cu, scales + t * K);
     store_codes(elem, cu, D, codes + t * code_bytes_per_row(elem, D));
   }
   free(y);

@@ -229,3 +229,41 @@ def test_e8m0_special_cases(orc):
     assert orc.e8m0_scale("e4m3", 512.0) == 128
     assert orc.e8m0_scale("e2m1", 6.0) == 127
     assert orc.e8m0_scale("e2m1", 8.0) == 128
+
+
+@pytest.mark.parametrize("elem,maxval", [("e4m3", 448.0), ("e2m1", 6.0)])
+def test_e8m0_ceil_rule_smallest_non_saturating_scale(orc, elem, maxval):
+    """Round-up rule: the smallest power of two that brings the block absmax
+    within the element maximum, checked against a search over every byte."""
+    vals = _all_bf16_values()
+    vals = vals[np.isfinite(vals) & (vals > 0)]
+    rng = np.random.default_rng(15)
+    extra = np.ldexp(rng.uniform(1, 2, 20000), rng.integers(-160, 128, 20000))
+    extra = np.concatenate([extra, np.ldexp(maxval, np.arange(-140, 128)),
+                            np.nextafter(np.ldexp(maxval, np.arange(-140, 128)), np.inf)])
+    a = np.concatenate([vals, extra])
+    got = np.array([orc.e8m0_scale(elem, float(v), rule="ceil") for v in a])
+    cand = np.arange(-127, 128)
+    ok = a[:, None] <= np.ldexp(maxval, cand)[None, :]
+    want = np.where(ok.any(1), np.argmax(ok, axis=1), 254)
+    assert (got == want).all()
+    floor = np.array([orc.e8m0_scale(elem, float(v)) for v in a])
+    assert set(np.unique(got - floor)) <= {0, 1}
+
+
+def test_e8m0_ceil_rule_golden_points(orc):
+    for elem in ("e4m3", "e2m1"):
+        assert orc.e8m0_scale(elem, 0.0, rule="ceil") == 0
+        assert orc.e8m0_scale(elem, float("nan"), rule="ceil") == 0xFF
+        assert orc.e8m0_scale(elem, float("inf"), rule="ceil") == 0xFF
+    assert orc.e8m0_scale("e4m3", 448.0, rule="ceil") == 127
+    assert orc.e8m0_scale("e4m3", 449.0, rule="ceil") == 128
+    assert orc.e8m0_scale("e4m3", 896.0, rule="ceil") == 128
+    assert orc.e8m0_scale("e4m3", 897.0, rule="ceil") == 129
+    assert orc.e8m0_scale("e4m3", 256.0, rule="ceil") == 127   # floor rule gives 127 too
+    assert orc.e8m0_scale("e4m3", 224.0, rule="ceil") == 126   # 224 = 448 / 2
+    assert orc.e8m0_scale("e2m1", 6.0, rule="ceil") == 127
+    assert orc.e8m0_scale("e2m1", 6.5, rule="ceil") == 128
+    assert orc.e8m0_scale("e2m1", 3.0, rule="ceil") == 126
+    assert orc.e8m0_scale("e2m1", 4.0, rule="ceil") == 127     # floor rule gives 127
+

@@ -25,7 +25,15 @@ E2M1_POS = np.array([v for _, v in _read_table("e2m1_values.txt")][:8])
 E4M3_POS = torch_e4m3_table()[:127]
 
 
-def mx_reference(y, elem, r=None):
+def ceil_scale_exponent(amax, maxval):
+    """Smallest s in [-127, 127] with amax <= maxval * 2^s (127 if none), found by
+    trying every exponent the E8M0 byte can hold."""
+    cand = np.arange(-127, 128)
+    ok = np.asarray(amax)[..., None] <= np.ldexp(maxval, cand)
+    return np.where(ok.any(-1), cand[np.argmax(ok, axis=-1)], 127)
+
+
+def mx_reference(y, elem, r=None, rule="floor"):
     """Brute-force MXCast of a float64 [T, D] array -> (unpacked codes, scales)."""
     T, D = y.shape
     K = D // 32
@@ -34,9 +42,12 @@ def mx_reference(y, elem, r=None):
     b = y.reshape(T, K, 32)
     bad = ~np.isfinite(b).all(-1)
     amax = np.abs(np.where(np.isfinite(b), b, 0)).max(-1)
-    with np.errstate(divide="ignore"):
-        fr, ex = np.frexp(amax)                     # amax = fr * 2^ex, fr in [0.5, 1)
-    s = np.clip(ex - 1 - emax, -127, 127)
+    if rule == "ceil":
+        s = ceil_scale_exponent(amax, pos[-1])
+    else:
+        with np.errstate(divide="ignore"):
+            fr, ex = np.frexp(amax)                 # amax = fr * 2^ex, fr in [0.5, 1)
+        s = np.clip(ex - 1 - emax, -127, 127)
     scales = np.where(bad, 255, np.where(amax == 0, 0, s + 127)).astype(np.uint8)
     sc = scales.astype(np.int64) - 127
     w = np.ldexp(np.where(np.isfinite(b), b, 0), -sc[..., None])
@@ -93,6 +104,31 @@ def test_mxcast_brute_force_e2m1_and_packing(orc):
     assert s[0, 0] == 127 and (c == 0x72).all()
 
 
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_mxcast_ceil_rule_brute_force_and_no_saturation(orc, elem):
+    x = workloads.random_rows(29, 256, seed=49).clone()
+    x[3] *= 1e4
+    x[4, :32] = 0.0
+    # block absmaxima whose mantissa lies above the format maximum's: the floor
+    # rule clips them, the ceil rule moves the scale up one binade
+    maxval = 448.0 if elem == "e4m3" else 6.0
+    for i, f in enumerate((1.76, 1.8, 1.9, 1.99)):
+        x[5 + i, 7] = f / (1.75 if elem == "e4m3" else 1.5) * maxval
+    codes, scales = orc.mxcast(x, elem, "rne", rule="ceil")
+    got_c = unpack_e2m1(codes) if elem == "e2m1" else codes
+    want_c, want_s = mx_reference(bf16_to_f64(x), elem, rule="ceil")
+    assert (scales == want_s).all()
+    assert (got_c == want_c).all()
+    floor_c, floor_s = orc.mxcast(x, elem, "rne")
+    d = scales.astype(int) - floor_s.astype(int)
+    assert set(np.unique(d)) <= {0, 1} and (d[5:9, 0] == 1).all()
+    # no block saturates: its absmax over the scale fits the element maximum
+    y = bf16_to_f64(x).reshape(29, 8, 32)
+    amax = np.abs(y).max(-1)
+    nz = amax > 0
+    assert (np.ldexp(amax, -(scales.astype(int) - 127))[nz] <= maxval).all()
+
+
 def test_mxcast_sr_uses_logical_element_index(orc):
     T, D, ldx = 9, 96, 128
     xs = workloads.random_rows(T, D, seed=43, ldx=ldx)      # strided view
@@ -127,18 +163,19 @@ def test_mxcast_nonfinite_blocks(orc):
 
 @pytest.mark.parametrize("p", [1.0, 2.0, 3.5, math.inf])
 @pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
-def test_mxnorm_reference_mode(orc, p, elem):
+@pytest.mark.parametrize("rule", ["floor", "ceil"])
+def test_mxnorm_reference_mode(orc, p, elem, rule):
     x = workloads.random_rows(24, 512, seed=45)
     x[2, :64] *= 40.0                                   # outlier blocks
     g = workloads.random_gamma(512, seed=46) * 3.0      # gains far from 1 move block maxima
-    codes, scales, inv = orc.mxnorm(x, g, p, elem)
+    codes, scales, inv = orc.mxnorm(x, g, p, elem, rule=rule)
     y = bf16_to_f64(x) * bf16_to_f64(g)[None, :] * inv[:, None]
-    want_c, want_s = mx_reference(y, elem)
+    want_c, want_s = mx_reference(y, elem, rule=rule)
     got_c = unpack_e2m1(codes) if elem == "e2m1" else codes
     assert (scales == want_s).all()
     assert (got_c == want_c).all()
     # the scale follows y = x * gamma / G, not x: with these gains they differ somewhere
-    xs_c, xs_s = mx_reference(bf16_to_f64(x) * inv[:, None], elem)
+    xs_c, xs_s = mx_reference(bf16_to_f64(x) * inv[:, None], elem, rule=rule)
     assert (xs_s != scales).any()
 
 
