@@ -214,7 +214,7 @@ def main():
         mxq.rmsnorm_mxcast(xs[k], g, 1e-5, "e4m3", "rne", out=outs[k], y=ys[k])
 
     tp_args = [(vp(xs[k].data_ptr()), D, vp(g.data_ptr()), T, D, ctypes.c_float(1e-5),
-                mxq.MXQ_E4M3, mxq.MXQ_RNE, None, vp(ys[k].data_ptr()), vp(outs[k][0].data_ptr()),
+                mxq.MXQ_E4M3, mxq.MXQ_RNE, None, 0, vp(ys[k].data_ptr()), vp(outs[k][0].data_ptr()),
                 vp(outs[k][1].data_ptr()), vp(outs[k][2].data_ptr())) for k in range(ROTATE)]
 
     def two_pass_raw(i):

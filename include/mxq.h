@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 
 typedef enum {
   MXQ_OK = 0,
@@ -92,10 +92,17 @@ typedef struct {
   uint64_t offset;
 } mxq_rng;
 
-/* mxnorm_fwd variant selection (0 = automatic by D). */
+/* Forward flags. FORCE_REG / FORCE_LDS select the variant of the single-pass
+ * entry points (0 = automatic by D). SCALE_CEIL, accepted by every forward
+ * entry point, replaces the OCP floor rule for the E8M0 block scale,
+ * s = floor(log2 amax) - emax, by the round-up rule: the smallest s with
+ * amax <= maxval * 2^s (maxval 448 for E4M3, 6 for E2M1), so no element of
+ * the block saturates. The MXFP8 recipes page names a scale conversion of its
+ * own without printing it; this is the reading that rounds the scale up. */
 enum {
   MXQ_FLAG_FORCE_REG = 1u, /* row held in registers (D <= 8192)               */
-  MXQ_FLAG_FORCE_LDS = 2u  /* row staged in LDS (D <= MXQ_MAX_D)              */
+  MXQ_FLAG_FORCE_LDS = 2u, /* row staged in LDS (D <= MXQ_MAX_D)              */
+  MXQ_FLAG_SCALE_CEIL = 4u /* round-up E8M0 scale rule                        */
 };
 
 /* Largest D of the register-resident MXNorm path and of any path. */
@@ -109,8 +116,8 @@ enum {
  *   p        power of the mean: > 0, or +INFINITY for the block-max maximum.
  *   elem     MXQ_E4M3 (codes [T, D]) or MXQ_E2M1 (codes [T, D/2]).
  *   rnd      MXQ_RNE, or MXQ_SR with rng != NULL.
- *   flags    0, MXQ_FLAG_FORCE_REG or MXQ_FLAG_FORCE_LDS; both variants give
- *            bit-identical results.
+ *   flags    0, MXQ_FLAG_FORCE_REG or MXQ_FLAG_FORCE_LDS (both variants give
+ *            bit-identical results), optionally or-ed with MXQ_FLAG_SCALE_CEIL.
  *   codes, scales  outputs; inv_norm [T] fp32 output, may be NULL.
  * Errors: NULL (x, codes, scales), SHAPE, ALIGN, ARG (p <= 0 or NaN, unknown
  * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large), HIP.
@@ -124,13 +131,14 @@ mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int
  * Two-pass comparison path (MXNorm page, §1.1 and §1.2): RMSNorm writes bf16
  * y to y_workspace [T, D] (contiguous, caller-owned), then MXCast reads it.
  *   eps      >= 0 and finite.
+ *   flags    0 or MXQ_FLAG_SCALE_CEIL (the scale rule of the cast).
  *   inv_rms  [T] fp32 output, may be NULL.
  * Other arguments and errors as for mxnorm_fwd (y_workspace NULL -> NULL).
  */
 mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
                               int64_t T, int64_t D, float eps, mxq_elem elem, mxq_round rnd,
-                              const mxq_rng* rng, uint16_t* y_workspace, uint8_t* codes,
-                              uint8_t* scales, float* inv_rms, void* stream);
+                              const mxq_rng* rng, uint32_t flags, uint16_t* y_workspace,
+                              uint8_t* codes, uint8_t* scales, float* inv_rms, void* stream);
 
 /*
  * Single-pass exact-RMS comparator: RMSNorm's statistic (MXNorm page, §1.1),
@@ -151,10 +159,12 @@ mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16
 /*
  * MXCast of a bf16 activation (MXNorm page, §1.2 and §2.1): block absmax,
  * E8M0 scale and element cast, with no normalisation.
+ *   flags    0 or MXQ_FLAG_SCALE_CEIL (the scale rule).
+ * Other arguments and errors as for mxnorm_fwd (no gamma, p or inv_norm).
  */
 mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
-                      mxq_round rnd, const mxq_rng* rng, uint8_t* codes, uint8_t* scales,
-                      void* stream);
+                      mxq_round rnd, const mxq_rng* rng, uint32_t flags, uint8_t* codes,
+                      uint8_t* scales, void* stream);
 
 /*
  * Straight-through backward of the normalisation (MXNorm page, §2.3, gradient

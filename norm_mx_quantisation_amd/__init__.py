@@ -24,10 +24,10 @@ LIB_PATH = os.path.join(PKG, "libmxq.so")
 MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_HIP = range(7)
 MXQ_E4M3, MXQ_E2M1 = 0, 1
 MXQ_RNE, MXQ_SR = 0, 1
-MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS = 1, 2
+MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS, MXQ_FLAG_SCALE_CEIL = 1, 2, 4
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
            "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mx_gemm", "mxq_strerror",
@@ -63,13 +63,13 @@ def lib():
             rp = ctypes.POINTER(mxq_rng)
             L.mxnorm_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, u32, vp, vp, vp, vp]
             L.mxnorm_fwd.restype = i32
-            L.rmsnorm_mxcast_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, vp, vp, vp,
-                                             vp, vp]
+            L.rmsnorm_mxcast_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, u32, vp, vp,
+                                             vp, vp, vp]
             L.rmsnorm_mxcast_fwd.restype = i32
             L.rmsnorm_mxcast_fused_fwd.argtypes = [vp, i64, vp, i64, i64, f32, i32, i32, rp, u32,
                                                    vp, vp, vp, vp]
             L.rmsnorm_mxcast_fused_fwd.restype = i32
-            L.mxcast_fwd.argtypes = [vp, i64, i64, i64, i32, i32, rp, vp, vp, vp]
+            L.mxcast_fwd.argtypes = [vp, i64, i64, i64, i32, i32, rp, u32, vp, vp, vp]
             L.mxcast_fwd.restype = i32
             L.mxnorm_bwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
@@ -106,10 +106,10 @@ def mxnorm_fwd(x, ldx, gamma, T, D, p, elem, rnd, rng, flags, codes, scales, inv
                             inv_norm, stream)
 
 
-def rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, y_workspace, codes, scales,
-                       inv_rms, stream) -> int:
-    return lib().rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, _rng(rng), y_workspace,
-                                    codes, scales, inv_rms, stream)
+def rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, y_workspace, codes,
+                       scales, inv_rms, stream) -> int:
+    return lib().rmsnorm_mxcast_fwd(x, ldx, gamma, T, D, eps, elem, rnd, _rng(rng), flags,
+                                    y_workspace, codes, scales, inv_rms, stream)
 
 
 def rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, codes, scales,
@@ -118,8 +118,8 @@ def rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, co
                                           codes, scales, inv_rms, stream)
 
 
-def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, codes, scales, stream) -> int:
-    return lib().mxcast_fwd(x, ldx, T, D, elem, rnd, _rng(rng), codes, scales, stream)
+def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, flags, codes, scales, stream) -> int:
+    return lib().mxcast_fwd(x, ldx, T, D, elem, rnd, _rng(rng), flags, codes, scales, stream)
 
 
 def mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, workspace,
@@ -150,6 +150,7 @@ def mxq_abi_version() -> int:
 
 _ELEM = {"e4m3": MXQ_E4M3, "e2m1": MXQ_E2M1}
 _RND = {"rne": MXQ_RNE, "sr": MXQ_SR}
+_RULE = {"floor": 0, "ceil": MXQ_FLAG_SCALE_CEIL}   # E8M0 scale rule -> flag bit
 
 
 def _check_x(x):
@@ -184,10 +185,12 @@ def _outputs(x, T, D, elem, want_inv):
 
 
 def mxnorm(x, gamma=None, p: float = 2.0, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0,
-           offset: int = 0, flags: int = 0, stream=None, out=None):
-    """Fused MXNorm -> MX cast. Returns (codes uint8, scales uint8 E8M0, inv_norm fp32)."""
+           offset: int = 0, flags: int = 0, stream=None, out=None, scale_rule: str = "floor"):
+    """Fused MXNorm -> MX cast. Returns (codes uint8, scales uint8 E8M0, inv_norm fp32).
+    scale_rule "floor" (OCP) or "ceil" (round the E8M0 scale up: no saturation)."""
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
+    flags |= _RULE[scale_rule]
     codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
     if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
         raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
@@ -200,17 +203,19 @@ def mxnorm(x, gamma=None, p: float = 2.0, fmt: str = "e4m3", rounding: str = "rn
 
 
 def rmsnorm_mxcast(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3", rounding: str = "rne",
-                   seed: int = 0, offset: int = 0, stream=None, out=None, y=None):
+                   seed: int = 0, offset: int = 0, stream=None, out=None, y=None,
+                   scale_rule: str = "floor"):
     """Two-pass RMSNorm (bf16 y) -> MXCast. Returns (codes, scales, inv_rms, y)."""
     import torch
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
+    flags = _RULE[scale_rule]
     codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
     if y is None:
         y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
     st = rmsnorm_mxcast_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(eps), elem, rnd,
-                            (seed, offset) if rnd == MXQ_SR else None, _ptr(y), _ptr(codes),
-                            _ptr(scales), _ptr(inv), _stream(stream))
+                            (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(y),
+                            _ptr(codes), _ptr(scales), _ptr(inv), _stream(stream))
     if st != MXQ_OK:
         raise MxqError(st, "rmsnorm_mxcast_fwd")
     return codes, scales, inv, y
@@ -218,10 +223,11 @@ def rmsnorm_mxcast(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3", rounding
 
 def rmsnorm_mxcast_fused(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3",
                          rounding: str = "rne", seed: int = 0, offset: int = 0, flags: int = 0,
-                         stream=None, out=None):
+                         stream=None, out=None, scale_rule: str = "floor"):
     """Single-pass exact-RMS normalise and MX cast. Returns (codes, scales, inv_rms)."""
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
+    flags |= _RULE[scale_rule]
     codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
     if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
         raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
@@ -234,13 +240,13 @@ def rmsnorm_mxcast_fused(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3",
 
 
 def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: int = 0,
-           stream=None, out=None):
+           stream=None, out=None, scale_rule: str = "floor"):
     """MXCast. Returns (codes, scales)."""
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
     codes, scales, _ = out if out is not None else _outputs(x, T, D, elem, False)
     st = mxcast_fwd(_ptr(x), ldx, T, D, elem, rnd, (seed, offset) if rnd == MXQ_SR else None,
-                    _ptr(codes), _ptr(scales), _stream(stream))
+                    _RULE[scale_rule], _ptr(codes), _ptr(scales), _stream(stream))
     if st != MXQ_OK:
         raise MxqError(st, "mxcast_fwd")
     return codes, scales

@@ -115,13 +115,25 @@ __device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, LaneMa
 
 // ------------------------------------------------------------------ scales
 
+// Floor rule: s = floor(log2 a) - emax, read from the fp32 exponent field.
+// Round-up rule: the smallest s with a <= maxval * 2^s. With maxval = 1.M * 2^emax
+// (1.75 * 2^8 for E4M3, 1.5 * 2^2 for E2M1) that is the floor rule plus one
+// exactly when a's mantissa exceeds M; adding 0x7FFFFF - M to the bits carries
+// into the exponent field in exactly those cases (a finite a stays below
+// 0x7F800000 + 0x7FFFFF, so the carry never reaches the sign). adj is 0 for
+// the floor rule and scale_adjust<ELEM>() for the round-up rule. The code is
+// s + 127 clamped at 0; NaN / Inf give 0xFF. a >= 0 here.
 template <int ELEM>
-__device__ __forceinline__ uint32_t e8m0_code(float amax) {
-  // floor(log2 a) - emax + 127 from the fp32 exponent field, clamped at 0;
-  // exponent 0xFF (NaN / Inf) gives 0xFF. a >= 0 here.
+__host__ __device__ constexpr uint32_t scale_adjust() {
+  return 0x7FFFFFu - ((ELEM == MXQ_E4M3) ? 0x600000u : 0x400000u);
+}
+
+template <int ELEM>
+__device__ __forceinline__ uint32_t e8m0_code(float amax, uint32_t adj) {
   constexpr int kEmax = (ELEM == MXQ_E4M3) ? 8 : 2;
-  uint32_t e = (__float_as_uint(amax) >> 23) & 0xFFu;
-  if (e == 0xFFu) return 0xFFu;
+  const uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
+  if (b >= 0x7F800000u) return 0xFFu;
+  const uint32_t e = (b + adj) >> 23;
   return e > (uint32_t)kEmax ? e - kEmax : 0u;
 }
 
@@ -332,6 +344,7 @@ struct NormArgs {
   float Df;    // D, for the RMS statistic
   float eps;   // RMS statistic only
   int sc_vec;  // scales rows can be written in dwords
+  int ceil_rule;  // E8M0 round-up rule instead of the floor rule
   SrStream rng;
 };
 
@@ -372,7 +385,7 @@ __device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* cod
   const float amax = __uint_as_float(vmax_bits) * inv;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
-  const uint32_t code = e8m0_code<ELEM>(amax);
+  const uint32_t code = e8m0_code<ELEM>(amax, A.ceil_rule ? scale_adjust<ELEM>() : 0u);
   encode_store8<ELEM, RND>(codes_row, d, nrow + d, v, code, A.rng);
   return code;
 }
@@ -695,6 +708,7 @@ struct CastArgs {
   int D;
   int K;
   int sc_vec;  // every chunk holds 16 blocks (D % 512 == 0) and scales take dword stores
+  int ceil_rule;  // E8M0 round-up rule instead of the floor rule
   SrStream rng;
 };
 
@@ -722,7 +736,8 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
   for (int u = 0; u < kCastChunksPerWave; ++u) {
     if (g0 + u < A.total_chunks && ds[u] < A.D) {
       const uint32_t mbits = quad_max_u32(absmax_bits8(raw[u]));
-      const uint32_t code = e8m0_code<ELEM>(__uint_as_float(mbits << 16));
+      const uint32_t code = e8m0_code<ELEM>(__uint_as_float(mbits << 16),
+                                            A.ceil_rule ? scale_adjust<ELEM>() : 0u);
       float v[8];
       unpack8(raw[u], v);
       const uint64_t nrow = (uint64_t)rows[u] * (uint64_t)A.D;
@@ -899,7 +914,8 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
                      float p, float eps, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
                      uint32_t flags, uint8_t* codes, uint8_t* scales, float* inv_out,
                      void* stream) {
-  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS | MXQ_FLAG_SCALE_CEIL))
+    return MXQ_ERR_ARG;
   if ((flags & MXQ_FLAG_FORCE_REG) && (flags & MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
   if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
   if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
@@ -923,6 +939,7 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   A.Df = (float)D;
   A.eps = eps;
   A.sc_vec = (A.K % 4 == 0) && aligned(scales, 4);
+  A.ceil_rule = (flags & MXQ_FLAG_SCALE_CEIL) != 0;
   A.rng = make_stream(rng);
   const int nc = (int)((D + kChunk - 1) / kChunk);
   const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
@@ -960,11 +977,12 @@ mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16
 
 mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
                               int64_t T, int64_t D, float eps, mxq_elem elem, mxq_round rnd,
-                              const mxq_rng* rng, uint16_t* y_workspace, uint8_t* codes,
-                              uint8_t* scales, float* inv_rms, void* stream) {
+                              const mxq_rng* rng, uint32_t flags, uint16_t* y_workspace,
+                              uint8_t* codes, uint8_t* scales, float* inv_rms, void* stream) {
   mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
   if (st != MXQ_OK) return st;
   if (!(eps >= 0.0f) || isinf(eps)) return MXQ_ERR_ARG;
+  if (flags & ~(uint32_t)MXQ_FLAG_SCALE_CEIL) return MXQ_ERR_ARG;
   if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
   if (T == 0) return MXQ_OK;
   if (y_workspace == nullptr) return MXQ_ERR_NULL;
@@ -997,15 +1015,17 @@ mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* ga
   C.D = (int)D;
   C.K = (int)(D / 32);
   C.sc_vec = (D % kChunk == 0) && aligned(scales, 4);
+  C.ceil_rule = (flags & MXQ_FLAG_SCALE_CEIL) != 0;
   C.rng = make_stream(rng);
   return dispatch_cast(C, elem, rnd, s);
 }
 
 mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
-                      mxq_round rnd, const mxq_rng* rng, uint8_t* codes, uint8_t* scales,
-                      void* stream) {
+                      mxq_round rnd, const mxq_rng* rng, uint32_t flags, uint8_t* codes,
+                      uint8_t* scales, void* stream) {
   mxq_status st = check_common(x, ldx, T, D, elem, rnd, rng, codes, scales);
   if (st != MXQ_OK) return st;
+  if (flags & ~(uint32_t)MXQ_FLAG_SCALE_CEIL) return MXQ_ERR_ARG;
   if (T == 0) return MXQ_OK;
   const uint64_t nc = (uint64_t)((D + kChunk - 1) / kChunk);
   if ((uint64_t)T * nc >= (1ull << 32) - kThreads) return MXQ_ERR_UNSUPPORTED;
@@ -1019,6 +1039,7 @@ mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_
   C.D = (int)D;
   C.K = (int)(D / 32);
   C.sc_vec = (D % kChunk == 0) && aligned(scales, 4);
+  C.ceil_rule = (flags & MXQ_FLAG_SCALE_CEIL) != 0;
   C.rng = make_stream(rng);
   return dispatch_cast(C, elem, rnd, (hipStream_t)stream);
 }

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_messages():
-    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 1
+    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 2
     for st in range(7):
         assert isinstance(mxq.mxq_strerror(st), str) and mxq.mxq_strerror(st)
     assert mxq.mxq_strerror(99) == "unknown status"
@@ -58,11 +58,11 @@ def norm(**kw):
 
 def rms(**kw):
     a = dict(x=A16, ldx=4096, gamma=None, T=8, D=4096, eps=1e-5, elem=0, rnd=0, rng=None,
-             y=A16, codes=A16, scales=A16, inv=None, stream=None)
+             flags=0, y=A16, codes=A16, scales=A16, inv=None, stream=None)
     a.update(kw)
     return mxq.rmsnorm_mxcast_fwd(a["x"], a["ldx"], a["gamma"], a["T"], a["D"], a["eps"], a["elem"],
-                                  a["rnd"], a["rng"], a["y"], a["codes"], a["scales"], a["inv"],
-                                  a["stream"])
+                                  a["rnd"], a["rng"], a["flags"], a["y"], a["codes"], a["scales"],
+                                  a["inv"], a["stream"])
 
 
 def rms_fused(**kw):
@@ -75,10 +75,11 @@ def rms_fused(**kw):
 
 
 def cast(**kw):
-    a = dict(x=A16, ldx=4096, T=8, D=4096, elem=0, rnd=0, rng=None, codes=A16, scales=A16, stream=None)
+    a = dict(x=A16, ldx=4096, T=8, D=4096, elem=0, rnd=0, rng=None, flags=0, codes=A16,
+             scales=A16, stream=None)
     a.update(kw)
     return mxq.mxcast_fwd(a["x"], a["ldx"], a["T"], a["D"], a["elem"], a["rnd"], a["rng"],
-                          a["codes"], a["scales"], a["stream"])
+                          a["flags"], a["codes"], a["scales"], a["stream"])
 
 
 @pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])
@@ -113,6 +114,7 @@ def test_mxnorm_argument_errors():
     assert norm(p=float("nan")) == mxq.MXQ_ERR_ARG
     assert norm(flags=3) == mxq.MXQ_ERR_ARG
     assert norm(flags=8) == mxq.MXQ_ERR_ARG
+    assert norm(flags=mxq.MXQ_FLAG_SCALE_CEIL | 3) == mxq.MXQ_ERR_ARG
     assert norm(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(gamma=A8) == mxq.MXQ_ERR_ALIGN
@@ -137,6 +139,16 @@ def test_rmsnorm_argument_errors():
     assert rms(y=None) == mxq.MXQ_ERR_NULL
     assert rms(y=A8) == mxq.MXQ_ERR_ALIGN
     assert rms(gamma=A8) == mxq.MXQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("call", [rms, cast])
+def test_cast_flags_take_only_the_scale_rule(call):
+    # the two-pass path and the plain cast have no variants to force
+    assert call(flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_ARG
+    assert call(flags=mxq.MXQ_FLAG_FORCE_LDS) == mxq.MXQ_ERR_ARG
+    assert call(flags=mxq.MXQ_FLAG_SCALE_CEIL | 8) == mxq.MXQ_ERR_ARG
+    # the flag is validated after the shape: a bad shape still reports SHAPE
+    assert call(D=0, flags=mxq.MXQ_FLAG_SCALE_CEIL) == mxq.MXQ_ERR_SHAPE
 
 
 @pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])

@@ -32,9 +32,9 @@ def _gpu():
     oracle.lib()
 
 
-def gpu_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, seed=SEED, offset=OFFSET):
+def gpu_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, seed=SEED, offset=OFFSET, rule="floor"):
     """Device outputs (codes, scales, inv_norm) of the fused kernel."""
-    out = mxq.mxnorm(x, g, p, elem, rnd, seed, offset, flags)
+    out = mxq.mxnorm(x, g, p, elem, rnd, seed, offset, flags, scale_rule=rule)
     torch.cuda.synchronize()
     return out
 
@@ -43,65 +43,68 @@ def same_outputs(a, b):
     return all(torch.equal(u.view(torch.uint8), v.view(torch.uint8)) for u, v in zip(a, b))
 
 
-def check_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, rows=None, what="", ref=True):
+def check_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, rows=None, what="", ref=True,
+                 rule="floor"):
     """Run the kernel on x (device) and check rows [r0, r1) (default all)."""
-    codes, scales, inv = gpu_mxnorm(x, g, p, elem, rnd, flags)
+    codes, scales, inv = gpu_mxnorm(x, g, p, elem, rnd, flags, rule=rule)
     r0, r1 = (0, x.shape[0]) if rows is None else rows
     xs, gs = host(x[r0:r1]), host(g)
     c, s, i = np_(codes[r0:r1]), np_(scales[r0:r1]), np_(inv[r0:r1])
     oc, os_, _ = oracle.mxnorm(xs, gs, p, elem, rnd, SEED, OFFSET, inv_inject=i, row_base=r0,
-                               threads=THREADS)
+                               threads=THREADS, rule=rule)
     assert_bits(s, os_, f"{what} scales (I)")
     assert_bits(c, oc, f"{what} codes (I)")
     if ref:
         rc, rs, rinv = oracle.mxnorm(xs, gs, p, elem, rnd, SEED, OFFSET, row_base=r0,
-                                     threads=THREADS)
+                                     threads=THREADS, rule=rule)
         check_normaliser(i, rinv, what)
         compare_reference(c, s, rc, rs, elem, what)
     return c, s, i
 
 
-def check_mxcast(x, elem="e4m3", rnd="rne", rows=None, what=""):
-    codes, scales = mxq.mxcast(x, elem, rnd, SEED, OFFSET)
+def check_mxcast(x, elem="e4m3", rnd="rne", rows=None, what="", rule="floor"):
+    codes, scales = mxq.mxcast(x, elem, rnd, SEED, OFFSET, scale_rule=rule)
     torch.cuda.synchronize()
     r0, r1 = (0, x.shape[0]) if rows is None else rows
-    oc, os_ = oracle.mxcast(host(x[r0:r1]), elem, rnd, SEED, OFFSET, row_base=r0, threads=THREADS)
+    oc, os_ = oracle.mxcast(host(x[r0:r1]), elem, rnd, SEED, OFFSET, row_base=r0, threads=THREADS,
+                            rule=rule)
     assert_bits(np_(scales[r0:r1]), os_, f"{what} scales")
     assert_bits(np_(codes[r0:r1]), oc, f"{what} codes")
     return codes, scales
 
 
-def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what=""):
-    codes, scales, inv, y = mxq.rmsnorm_mxcast(x, g, eps, elem, rnd, SEED, OFFSET)
+def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what="", rule="floor"):
+    codes, scales, inv, y = mxq.rmsnorm_mxcast(x, g, eps, elem, rnd, SEED, OFFSET, scale_rule=rule)
     torch.cuda.synchronize()
     r0, r1 = (0, x.shape[0]) if rows is None else rows
     xs, gs = host(x[r0:r1]), host(g)
     i = np_(inv[r0:r1])
     oy, oc, os_, _ = oracle.rmsnorm_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, inv_inject=i,
-                                           row_base=r0, threads=THREADS)
+                                           row_base=r0, threads=THREADS, rule=rule)
     assert_bits(np_(y[r0:r1].view(torch.int16)).view(np.uint16), oy, f"{what} y (I)")
     assert_bits(np_(scales[r0:r1]), os_, f"{what} scales (I)")
     assert_bits(np_(codes[r0:r1]), oc, f"{what} codes (I)")
     ry, rc, rs, rinv = oracle.rmsnorm_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, row_base=r0,
-                                             threads=THREADS)
+                                             threads=THREADS, rule=rule)
     check_normaliser(i, rinv, what)
     compare_reference(np_(codes[r0:r1]), np_(scales[r0:r1]), rc, rs, elem, what)
 
 
 def check_rms_fused(x, g, eps=1e-5, elem="e4m3", rnd="rne", flags=0, rows=None, what="",
-                    ref=True):
-    codes, scales, inv = mxq.rmsnorm_mxcast_fused(x, g, eps, elem, rnd, SEED, OFFSET, flags)
+                    ref=True, rule="floor"):
+    codes, scales, inv = mxq.rmsnorm_mxcast_fused(x, g, eps, elem, rnd, SEED, OFFSET, flags,
+                                                  scale_rule=rule)
     torch.cuda.synchronize()
     r0, r1 = (0, x.shape[0]) if rows is None else rows
     xs, gs = host(x[r0:r1]), host(g)
     c, s, i = np_(codes[r0:r1]), np_(scales[r0:r1]), np_(inv[r0:r1])
     oc, os_, _ = oracle.rmsnorm_fused_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, inv_inject=i,
-                                             row_base=r0, threads=THREADS)
+                                             row_base=r0, threads=THREADS, rule=rule)
     assert_bits(s, os_, f"{what} scales (I)")
     assert_bits(c, oc, f"{what} codes (I)")
     if ref:
         rc, rs, rinv = oracle.rmsnorm_fused_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET,
-                                                   row_base=r0, threads=THREADS)
+                                                   row_base=r0, threads=THREADS, rule=rule)
         check_normaliser(i, rinv, what)
         compare_reference(c, s, rc, rs, elem, what)
     return c, s, i
@@ -525,6 +528,113 @@ def test_gemm_consumes_mxnorm_output():
     B, SB = mxq.mxcast(wg)
     for r0 in (0, 4096, x.shape[0] - 16):
         check_gemm(A, SA, B, SB, torch.bfloat16, rows=(r0, r0 + 16), what=f"mxnormlinear {r0}")
+
+
+# ---------------------------------------------------------------- E8M0 round-up scale rule
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("width", [32, 1024])
+def test_ceil_rule_mxcast_every_bf16_pattern(elem, width):
+    x = _all_bf16_rows(width).to(DEV)
+    check_mxcast(x, elem, "rne", what=f"ceil all-bf16 w={width}", rule="ceil")
+
+
+def _boundary_rows(binades):
+    """One row per binade e: block j's absmax has bf16 exponent e and mantissa j
+    (every 7-bit mantissa, both sides of 1.5 and 1.75), the other 31 elements
+    random with smaller magnitude and random signs."""
+    g = torch.Generator().manual_seed(91)
+    T, D = len(binades), 128 * 32
+    e = torch.tensor(binades).reshape(T, 1, 1)
+    man = torch.randint(0, 128, (T, 128, 32), generator=g)
+    ex = (e - torch.randint(1, 6, (T, 128, 32), generator=g)).clamp(min=0)
+    ex[:, :, 0] = e[:, :, 0]
+    man[:, :, 0] = torch.arange(128)
+    sgn = torch.randint(0, 2, (T, 128, 32), generator=g)
+    perm = torch.argsort(torch.rand(T, 128, 32, generator=g), dim=-1)   # absmax anywhere in the block
+    bits = ((sgn << 15) | (ex << 7) | man).gather(-1, perm)
+    return bits.reshape(T, D).to(torch.int32).to(torch.int16).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_ceil_rule_mxcast_mantissa_boundaries(elem, rnd):
+    x = _boundary_rows([1, 2, 3, 9, 10, 60, 127, 128, 200, 250, 253, 254]).to(DEV)
+    codes, scales = check_mxcast(x, elem, rnd, what=f"ceil boundaries {rnd}", rule="ceil")
+    _, floor_s = mxq.mxcast(x, elem, rnd, SEED, OFFSET)
+    d = np_(scales).astype(int) - np_(floor_s).astype(int)
+    thr = 0x60 if elem == "e4m3" else 0x40            # mantissa of 448 = 1.75 * 2^8, 6 = 1.5 * 2^2
+    bump = (np.arange(128) > thr)[None, :] & (np.array([1, 2, 3, 9, 10, 60, 127, 128, 200, 250,
+                                                         253, 254])[:, None] > 0)
+    # the rule moves the scale up one binade exactly when the absmax mantissa
+    # exceeds the format maximum's (and the floor code is not clamped at 0)
+    nz = np_(floor_s) > 0
+    assert (d[nz] == bump[nz]).all()
+    assert set(np.unique(d)) <= {0, 1}
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_ceil_rule_mxcast_exponent_windows(elem):
+    g = torch.Generator().manual_seed(93)
+    T, D = 256, 1024
+    top = torch.randint(1, 254, (T, D // 32, 1), generator=g)
+    ex = (top - torch.randint(0, 14, (T, D // 32, 32), generator=g)).clamp(0, 254)
+    man = torch.randint(0, 128, (T, D // 32, 32), generator=g)
+    sgn = torch.randint(0, 2, (T, D // 32, 32), generator=g)
+    bits = (sgn << 15) | (ex << 7) | man
+    x = bits.reshape(T, D).to(torch.int32).to(torch.int16).view(torch.bfloat16).to(DEV)
+    check_mxcast(x, elem, "rne", what="ceil windows", rule="ceil")
+    check_mxcast(x, elem, "sr", what="ceil windows sr", rule="ceil")
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("p", [1.0, 2.0, math.inf])
+def test_ceil_rule_mxnorm(elem, rnd, p):
+    x = workloads.random_rows(37, 4096, seed=95, device=DEV)
+    x[2, :64] *= 40.0
+    g = workloads.random_gamma(4096, seed=96, device=DEV) * 3.0
+    check_mxnorm(x, g, p, elem, rnd, what=f"ceil {elem} {rnd} p={p}", rule="ceil")
+    check_mxnorm(x, None, p, elem, rnd, what=f"ceil {elem} {rnd} p={p} no gamma", rule="ceil")
+
+
+@pytest.mark.parametrize("D", [96, 4096, 8224])
+def test_ceil_rule_mxnorm_variants_and_special_rows(D):
+    x = workloads.random_rows(10, D, seed=97).clone()
+    x[1, 5] = float("nan")
+    x[2] = 0.0
+    x[3] = x[3] * 2.0**-128
+    x[4] = x[4] * 1e30
+    xg = x.to(DEV)
+    g = workloads.random_gamma(D, seed=98, device=DEV)
+    for flags in ((mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS) if D <= mxq.MXQ_MAX_D_REG
+                  else (mxq.MXQ_FLAG_FORCE_LDS,)):
+        check_mxnorm(xg, g, 2.0, flags=flags, what=f"ceil special D={D} flags={flags}",
+                     rule="ceil")
+    if D <= mxq.MXQ_MAX_D_REG:
+        a = gpu_mxnorm(xg, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_REG, rule="ceil")
+        b = gpu_mxnorm(xg, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_LDS, rule="ceil")
+        assert same_outputs(a, b)
+
+
+@pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e4m3", "sr"), ("e2m1", "rne")])
+def test_ceil_rule_two_pass_and_rms_fused(elem, rnd):
+    x = workloads.random_rows(29, 4096, seed=99, device=DEV)
+    g = workloads.random_gamma(4096, seed=100, device=DEV) * 3.0
+    check_two_pass(x, g, 1e-5, elem, rnd, what=f"ceil two-pass {elem} {rnd}", rule="ceil")
+    check_rms_fused(x, g, 1e-5, elem, rnd, what=f"ceil rms-fused {elem} {rnd}", rule="ceil")
+
+
+def test_ceil_rule_llama3_workload_sampled():
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV)
+    T = x.shape[0]
+    codes, scales, inv = gpu_mxnorm(x, g, 2.0, rule="ceil")
+    _, floor_s, floor_i = gpu_mxnorm(x, g, 2.0)
+    assert torch.equal(inv, floor_i)                 # the statistic does not see the rule
+    d = scales.int() - floor_s.int()
+    assert int(d.min()) >= 0 and int(d.max()) <= 1
+    for r0 in (0, T // 2, T - 256):
+        check_mxnorm(x, g, 2.0, rows=(r0, r0 + 256), what=f"ceil llama3 rows {r0}", rule="ceil")
 
 
 # ---------------------------------------------------------------- the five workloads
