@@ -28,6 +28,8 @@ CASES = (
     ("llama3_8b_preattn mxnorm p=1", "llama3_8b_preattn", "mxnorm", {"p": 1.0}),
     ("llama3_8b_preattn mxnorm p=2 gamma folded", "llama3_8b_preattn", "mxnorm",
      {"p": 2.0, "gamma": False}),
+    ("llama3_8b_preattn mxnorm p=2 round-up scales", "llama3_8b_preattn", "mxnorm",
+     {"p": 2.0, "flags": mxq.MXQ_FLAG_SCALE_CEIL}),
     ("llama3_8b_preattn rms single-pass", "llama3_8b_preattn", "rms_fused", {}),
     ("llama3_8b_preattn two-pass", "llama3_8b_preattn", "two_pass", {}),
     ("longseq_t3 mxnorm register rows", "longseq_t3", "mxnorm",
@@ -35,6 +37,8 @@ CASES = (
     ("longseq_t3 mxnorm LDS rows", "longseq_t3", "mxnorm", {"flags": mxq.MXQ_FLAG_FORCE_LDS}),
     ("swiglu_downproj mxcast rne", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_RNE}),
     ("swiglu_downproj mxcast sr", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_SR}),
+    ("swiglu_downproj mxcast rne round-up scales", "swiglu_downproj", "mxcast",
+     {"rnd": mxq.MXQ_RNE, "flags": mxq.MXQ_FLAG_SCALE_CEIL}),
     ("mxfp4 mxnorm e2m1", "mxfp4", "mxnorm", {"elem": mxq.MXQ_E2M1}),
     ("llama3_8b_preattn backward dx+dgamma", "llama3_8b_preattn", "backward", {}),
     ("llama3_8b_preattn backward dx only", "llama3_8b_preattn", "backward", {"dgamma": False}),
@@ -153,9 +157,10 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
                               stream)
         elif op == "two_pass":
             st = L.rmsnorm_mxcast_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
-                                      vp(ys[k].data_ptr()), cp, sp, ip, stream)
+                                      opt.get("flags", 0), vp(ys[k].data_ptr()), cp, sp, ip,
+                                      stream)
         else:
-            st = L.mxcast_fwd(xp, D, T, D, elem, rnd, rngp, cp, sp, stream)
+            st = L.mxcast_fwd(xp, D, T, D, elem, rnd, rngp, opt.get("flags", 0), cp, sp, stream)
         if st != mxq.MXQ_OK:
             raise mxq.MxqError(st, name)
 
