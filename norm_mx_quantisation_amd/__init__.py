@@ -175,6 +175,46 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_buf(t, what, shape, dtype, device, optional=False):
+    """A caller-supplied buffer must match exactly what the kernel writes or
+    reads: a contiguous tensor of this dtype and shape on the input's device
+    (a wrong size or a host tensor would be an out-of-bounds GPU access)."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{what} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be {dtype} of shape {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{what} must live on {device}, got {t.device}")
+
+
+def _check_gamma(gamma, D, device):
+    import torch
+    _check_buf(gamma, "gamma", (D,), torch.bfloat16, device, optional=True)
+
+
+def _check_outputs(out, T, D, elem, device, want_inv):
+    """out = (codes, scales[, inv]) from a caller; checked like _outputs' own."""
+    import torch
+    if not isinstance(out, (tuple, list)) or len(out) not in (2, 3):
+        raise ValueError("out must be (codes, scales) or (codes, scales, inv)")
+    codes, scales = out[0], out[1]
+    inv = out[2] if len(out) == 3 else None
+    cb = D // 2 if elem == MXQ_E2M1 else D
+    _check_buf(codes, "codes", (T, cb), torch.uint8, device)
+    _check_buf(scales, "scales", (T, D // 32), torch.uint8, device)
+    if want_inv:
+        _check_buf(inv, "inv", (T,), torch.float32, device, optional=True)
+    return codes, scales, inv
+
+
 def _outputs(x, T, D, elem, want_inv):
     import torch
     cb = D // 2 if elem == MXQ_E2M1 else D
@@ -191,9 +231,9 @@ def mxnorm(x, gamma=None, p: float = 2.0, fmt: str = "e4m3", rounding: str = "rn
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
     flags |= _RULE[scale_rule]
-    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
-    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
-        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    codes, scales, inv = (_check_outputs(out, T, D, elem, x.device, True) if out is not None
+                          else _outputs(x, T, D, elem, True))
+    _check_gamma(gamma, D, x.device)
     st = mxnorm_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(p), elem, rnd,
                     (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(codes), _ptr(scales),
                     _ptr(inv), _stream(stream))
@@ -210,9 +250,12 @@ def rmsnorm_mxcast(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3", rounding
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
     flags = _RULE[scale_rule]
-    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
+    codes, scales, inv = (_check_outputs(out, T, D, elem, x.device, True) if out is not None
+                          else _outputs(x, T, D, elem, True))
+    _check_gamma(gamma, D, x.device)
     if y is None:
         y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    _check_buf(y, "y", (T, D), torch.bfloat16, x.device)
     st = rmsnorm_mxcast_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(eps), elem, rnd,
                             (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(y),
                             _ptr(codes), _ptr(scales), _ptr(inv), _stream(stream))
@@ -228,9 +271,9 @@ def rmsnorm_mxcast_fused(x, gamma=None, eps: float = 1e-5, fmt: str = "e4m3",
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
     flags |= _RULE[scale_rule]
-    codes, scales, inv = out if out is not None else _outputs(x, T, D, elem, True)
-    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
-        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    codes, scales, inv = (_check_outputs(out, T, D, elem, x.device, True) if out is not None
+                          else _outputs(x, T, D, elem, True))
+    _check_gamma(gamma, D, x.device)
     st = rmsnorm_mxcast_fused_fwd(_ptr(x), ldx, _ptr(gamma), T, D, float(eps), elem, rnd,
                                   (seed, offset) if rnd == MXQ_SR else None, flags, _ptr(codes),
                                   _ptr(scales), _ptr(inv), _stream(stream))
@@ -244,7 +287,8 @@ def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: i
     """MXCast. Returns (codes, scales)."""
     T, D, ldx = _check_x(x)
     elem, rnd = _ELEM[fmt], _RND[rounding]
-    codes, scales, _ = out if out is not None else _outputs(x, T, D, elem, False)
+    codes, scales, _ = (_check_outputs(out, T, D, elem, x.device, False) if out is not None
+                        else _outputs(x, T, D, elem, False))
     st = mxcast_fwd(_ptr(x), ldx, T, D, elem, rnd, (seed, offset) if rnd == MXQ_SR else None,
                     _RULE[scale_rule], _ptr(codes), _ptr(scales), _stream(stream))
     if st != MXQ_OK:
@@ -260,12 +304,21 @@ def mxnorm_backward(x, gamma, dy, inv_norm, want_dgamma: bool = True, stream=Non
     Td, Dd, lddy = _check_x(dy)
     if (Td, Dd) != (T, D):
         raise ValueError("dy must have the shape of x")
-    if inv_norm.dtype != torch.float32 or inv_norm.numel() != T or not inv_norm.is_contiguous():
-        raise ValueError("inv_norm must be a contiguous fp32 tensor of T elements")
-    if gamma is not None and (gamma.dtype != x.dtype or gamma.numel() != D or not gamma.is_contiguous()):
-        raise ValueError("gamma must be a contiguous bf16 tensor of D elements")
+    if dy.device != x.device:
+        raise ValueError("dy must live on the device of x")
+    if (not isinstance(inv_norm, torch.Tensor) or inv_norm.dtype != torch.float32
+            or inv_norm.numel() != T or not inv_norm.is_contiguous() or inv_norm.device != x.device):
+        raise ValueError("inv_norm must be a contiguous fp32 tensor of T elements on x's device")
+    _check_gamma(gamma, D, x.device)
     if out is not None:
         dx, row_dot, dgamma, ws = out
+        _check_buf(dx, "dx", (T, D), torch.bfloat16, x.device)
+        _check_buf(row_dot, "row_dot", (T,), torch.float32, x.device)
+        _check_buf(dgamma, "dgamma", (D,), torch.float32, x.device, optional=True)
+        if dgamma is not None:
+            if ws is None:
+                raise ValueError("dgamma needs a workspace")
+            _check_buf(ws, "workspace", tuple(ws.shape), ws.dtype, x.device)
     else:
         dx = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
         row_dot = torch.empty((T,), dtype=torch.float32, device=x.device)
@@ -293,9 +346,21 @@ def mx_matmul(a_codes, a_scales, b_codes, b_scales, out_dtype=None, stream=None,
     N = b_codes.shape[0]
     if b_codes.shape[1] != K or a_scales.shape != (M, K // 32) or b_scales.shape != (N, K // 32):
         raise ValueError("MX operand shapes do not match")
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dev = a_codes.device
+    if any(t.device != dev for t in (a_scales, b_codes, b_scales)):
+        raise ValueError("MX operands must live on one device")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     ct = {torch.float32: MXQ_OUT_F32, torch.bfloat16: MXQ_OUT_BF16}[out_dtype]
-    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out is not None:
+        # the kernel writes M rows of N elements of out_dtype at out's row stride
+        if not isinstance(out, torch.Tensor) or out.dtype != out_dtype or tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be {out_dtype} of shape {(M, N)}")
+        if out.device != dev or (N > 1 and out.stride(1) != 1) or (M > 1 and out.stride(0) < N):
+            raise ValueError("out must be on the operands' device with unit column stride")
+    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
     ld = lambda t: t.stride(0) if t.shape[0] > 1 else t.shape[1]
     st = mx_gemm(_ptr(a_codes), ld(a_codes), _ptr(a_scales), ld(a_scales), _ptr(b_codes),
                  ld(b_codes), _ptr(b_scales), ld(b_scales), M, N, K, MXQ_E4M3, MXQ_E4M3, _ptr(c),

@@ -5,17 +5,20 @@
 // Reusing MXFP block scales for efficient tensor normalisation", §2.1), B the
 // next linear layer's weight [N, K], gain folded and MX-cast along K (§2.3,
 // MXNormLinear). The products run on the gfx950 block-scaled matrix cores
-// (v_mfma_scale_f32_16x16x128_f8f6f4), which apply both operands' E8M0 scales
-// and accumulate in fp32.
+// (v_mfma_scale_f32_32x32x64_f8f6f4), which apply both operands' E8M0 scales
+// and accumulate in fp32. (Its 16 x 16 x 128 sibling measures at less than
+// half its rate with 8-bit operands on MI355X, the 32 x 32 x 64 form near the
+// 5 PFLOP/s MXFP8 peak.)
 //
 // Operand layout of that instruction for 8-bit data (probed on the device):
-// lane l carries row l % 16 of its 16 x 128 operand; its 32 bytes are K
-// [16 g, 16 g + 16) then [64 + 16 g, 64 + 16 g + 16), g = l / 16; the scale of
-// K block b (32 columns) of row r is the low byte of lane r + 16 b's scale
-// register, whose other bytes must be zero. The result's
-// lane l holds column l % 16, rows 4 (l / 16) + i in its 4 registers.
-// Here the instruction takes B as its row operand and A as its column
-// operand, so each lane's 4 registers are 4 consecutive columns of C.
+// lane l carries row l % 32 of its 32 x 64 operand; its 32 bytes are K
+// [16 g, 16 g + 16) then [32 + 16 g, 32 + 16 g + 16), g = l / 32; the scale
+// of K block b (32 columns) of row r is the low byte of lane r + 32 b's scale
+// register, whose other bytes must be zero. Result element v of lane l is
+// row 8 (v / 4) + 4 (l / 32) + v % 4 (of the first operand) and column l % 32
+// (of the second). Here the instruction takes B as its first operand and A
+// as its second, so each lane's 16 results are C row l % 32 at 4 groups of 4
+// consecutive columns.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,13 +31,15 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;   // 4 waves, 2 x 2 over the tile
 constexpr int kBM = 256;        // tile rows (A)
 constexpr int kBN = 256;        // tile columns (B rows)
-constexpr int kBK = 128;        // K per step: 4 MX blocks, one MFMA deep
+constexpr int kBK = 128;        // K per step: 4 MX blocks, two MFMAs deep
 constexpr int kChunks = kBK / 16;   // 16-byte chunks per row and step
 
 struct GemmArgs {
@@ -52,18 +57,25 @@ struct GemmArgs {
 // One K step of both operands in LDS. Code rows hold 8 chunks of 16 bytes;
 // chunk c of row r sits at position c ^ (r & 7), so the 8 lanes that read one
 // 128-byte stretch of a row group touch all 32 banks once.
+// The scale words (the step's 4 E8M0 bytes of a row) are stored in the order
+// the MFMA lanes consume them: position h * 128 + rl * 4 + blk holds row
+// h * 128 + blk * 32 + rl, so a lane's 4 words are contiguous.
 struct Stage {
   uint4 a[kBM * kChunks];
   uint4 b[kBN * kChunks];
-  uint32_t sa[kBM];   // the step's 4 scale bytes of each row
+  uint32_t sa[kBM];
   uint32_t sb[kBN];
 };
+
+__device__ __forceinline__ int scale_row(int p) {
+  return (p >> 7) * 128 + (p & 3) * 32 + ((p >> 2) & 31);
+}
 
 // Direct-to-LDS loads of one K step. A wave instruction moves 64 x 16 bytes
 // = 8 rows; lane i lands at position i, i.e. row i / 8, physical chunk i % 8,
 // so it fetches logical chunk (i % 8) ^ (row & 7). Rows past the matrix end
 // re-read its last row (their results are never stored).
-__device__ __forceinline__ void load_stage(const GemmArgs& G, Stage& S, int m0, int n0, int ks,
+__device__ __forceinline__ void load_stage(const GemmArgs& G, Stage* S, int m0, int n0, int ks,
                                            int wave, int lane) {
   const int k0 = ks * kBK;
 #pragma unroll
@@ -73,7 +85,7 @@ __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage& S, int m0, 
     const int c = (lane & 7) ^ (r & 7);
     const int ra = min(m0 + r, G.M - 1);
     __builtin_amdgcn_global_load_lds((const void*)(G.a + (int64_t)ra * G.lda + k0 + c * 16),
-                                     (lds_void*)&S.a[blk * kWave], 16, 0, 0);
+                                     (lds_void*)&S->a[blk * kWave], 16, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < kBN / 8 / 4; ++q) {
@@ -82,153 +94,253 @@ __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage& S, int m0, 
     const int c = (lane & 7) ^ (r & 7);
     const int rb = min(n0 + r, G.N - 1);
     __builtin_amdgcn_global_load_lds((const void*)(G.b + (int64_t)rb * G.ldb + k0 + c * 16),
-                                     (lds_void*)&S.b[blk * kWave], 16, 0, 0);
+                                     (lds_void*)&S->b[blk * kWave], 16, 0, 0);
   }
-  // scales: 4 bytes (the step's 4 blocks) per row, 64 rows per wave
-  const int rs = wave * kWave + lane;
+  // scales: 4 bytes (the step's 4 blocks) per row; lane i of wave w fills
+  // position w * 64 + i
+  const int rs = scale_row(wave * kWave + lane);
   __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + rs, G.M - 1) * G.ldsa + ks * 4),
-                                   (lds_void*)&S.sa[wave * kWave], 4, 0, 0);
+                                   (lds_void*)&S->sa[wave * kWave], 4, 0, 0);
   __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + rs, G.N - 1) * G.ldsb + ks * 4),
-                                   (lds_void*)&S.sb[wave * kWave], 4, 0, 0);
+                                   (lds_void*)&S->sb[wave * kWave], 4, 0, 0);
 }
-// The 32-byte MFMA operand of lane (row r, group g): chunks g and 4 + g.
-__device__ __forceinline__ v8i operand(const uint4* rows, int r, int g) {
-  const uint4 lo = rows[r * kChunks + (g ^ (r & 7))];
-  const uint4 hi = rows[r * kChunks + ((4 + g) ^ (r & 7))];
+
+// The 32-byte MFMA operand of lane (row r, half g) for the K half kk of the
+// step (64 of its 128 bytes): chunks 4 kk + g and 4 kk + 2 + g.
+__device__ __forceinline__ v8i operand(const uint4* rows, int r, int kk, int g) {
+  const uint4 lo = rows[r * kChunks + ((4 * kk + g) ^ (r & 7))];
+  const uint4 hi = rows[r * kChunks + ((4 * kk + 2 + g) ^ (r & 7))];
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Workgroup barrier without the memory fence __syncthreads() carries (that
-// fence waits for every load in flight, including the next step's prefetch).
-// LDS hazards are handled by the explicit waits around it.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// The scale words of the lane's 4 operand rows h * 128 + blk * 32 + rl
+// (blk = 0..3).
+__device__ __forceinline__ uint4 scale_words(const uint32_t* sc, int h, int rl) {
+  return *reinterpret_cast<const uint4*>(sc + h * 128 + rl * 4);
+}
+
+// E8M0 byte `b` of a scale word, alone in its register (the instruction
+// requires the other bytes to be zero).
+__device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >> (8 * b)) & 0xFFu); }
+
+// One K step of the wave's 128 x 128 quarter: the next step's DMA into
+// `fill`, then this step's operands from `use` into the MFMAs, in two K
+// halves of 64 (the MX blocks 2 kk and 2 kk + 1 of the step). Per half, the
+// 4 B operands are read first and the A operand one 32-row block ahead of
+// the 4 MFMAs that use it, so the reads overlap the MFMAs. That `use` has
+// landed is the caller's wait and barrier. When `fill` and `use` are two
+// distinct LDS objects known at compile time, the compiler's alias analysis
+// tells the DMA's writes from these reads and the reads overlap the DMA;
+// with a stage chosen at run time it waits for the DMA before the first
+// read.
+__device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Stage* use, int fm0,
+                                       int fn0, int fks, int wave, int lane, int wm, int wn,
+                                       v16f (&acc)[4][4]) {
+  load_stage(G, fill, fm0, fn0, fks, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);  // the DMA goes out first: it has the whole step to land
+  const int g = lane >> 5, rl = lane & 31;
+  const uint4 sbw = scale_words(use->sb, wn, rl);
+  const uint4 saw = scale_words(use->sa, wm, rl);
+  const uint32_t sbw4[4] = {sbw.x, sbw.y, sbw.z, sbw.w};
+  const uint32_t saw4[4] = {saw.x, saw.y, saw.z, saw.w};
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    v8i bo[4];
+    int sbv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bo[j] = operand(use->b, wn * 128 + j * 32 + rl, kk, g);
+      sbv[j] = scale_byte(sbw4[j], 2 * kk + g);
+    }
+    v8i ao = operand(use->a, wm * 128 + rl, kk, g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v8i ao_next;
+      if (i + 1 < 4) ao_next = operand(use->a, wm * 128 + (i + 1) * 32 + rl, kk, g);
+      const int sav = scale_byte(saw4[i], 2 * kk + g);
+      // B is the first operand, so each lane's results are consecutive columns of C
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo[j], ao, acc[i][j], 0, 0, 0,
+                                                                    sbv[j], 0, sav);
+      if (i + 1 < 4) ao = ao_next;
+      // keep the next block's reads ahead of this block's MFMAs (the
+      // scheduler would otherwise sink them to their use and wait on each)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The start of a step: this wave's DMA has landed and its LDS reads of the
+// previous step are complete (s_waitcnt vmcnt(0) lgkmcnt(0): encoding 0x0070,
+// expcnt left at its maximum), then a barrier. After it every wave's share of
+// this step is visible, and no wave still reads the stage this step's DMA
+// refills. The wait is the intrinsic, not inline assembly, so the compiler's
+// own wait insertion knows the DMA is complete. The barrier carries no memory
+// fence (__syncthreads() would also wait for loads the compiler still thinks
+// in flight).
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Four consecutive elements of C at element offset off: one 8-byte (bf16) or
+// 16-byte (fp32) store. Ordinary (write-back) stores: L2 merges the partial
+// lines of a tile's rows before they go to memory.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mx_gemm_e4m3_kernel(GemmArgs G) {
-  __shared__ Stage S[2];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int wm = wave >> 1, wn = wave & 1;   // wave's 128 x 128 quarter of the tile
-
-  // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = grid
-  // size, a multiple of 8), walked as one flattened sequence of (tile, K
-  // step) pairs, so the next tile's first DMA streams during this tile's last
-  // step and the epilogue's stores drain while the next tile computes.
-  const int nb = G.tiles_m * G.tiles_n;
-  const int nk = G.K / kBK;
-  const int my_tiles = (nb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int total = my_tiles * nk;
-  const int g = lane >> 4;
-  const int rl = lane & 15;
-
-  // Tile order: the 8 XCDs take workgroup ids round robin, so tile t is first
-  // mapped to slot (t % 8) * (n / 8) + t / 8, giving each XCD (and its L2) a
-  // contiguous run of the sequence (tiles b + j G stay on b's XCD); the
-  // sequence walks groups of 4 tile rows column by column, so neighbours
-  // share A rows or B rows.
-  auto tile_origin = [&](int t, int& m0, int& n0) {
-    int pid = t;
-    if (nb % 8 == 0) pid = (pid % 8) * (nb / 8) + pid / 8;
-    constexpr int kGroup = 4;
-    const int group = pid / (kGroup * G.tiles_n);
-    const int first = group * kGroup;
-    const int gsz = min(G.tiles_m - first, kGroup);
-    const int in_group = pid % (kGroup * G.tiles_n);
-    m0 = (first + in_group % gsz) * kBM;
-    n0 = (in_group / gsz) * kBN;
-  };
-
-  v4f acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // Two LDS stages. Per step: wait for the step's DMA (the only memory
-  // loads in flight), barrier, issue every LDS read of the step's operands
-  // and scales, then the next step's DMA into the other stage, then the 64
-  // MFMAs, which consume the reads as they land. No LDS read follows a DMA in
-  // program order within the step, so the compiler's wait before LDS reads
-  // (any read may alias an LDS DMA in flight) never fires; the DMA overlaps
-  // the MFMAs and the reads overlap the first MFMAs. The barrier also orders
-  // the refill of a stage after every wave's reads of it, two steps earlier.
-  int m0, n0;
-  tile_origin(blockIdx.x, m0, n0);
-  if (total > 0) load_stage(G, S[0], m0, n0, 0, wave, lane);
-  for (int jt = 0; jt < my_tiles; ++jt) {
-  for (int ks = 0; ks < nk; ++ks) {
-    const int step = jt * nk + ks;
-    Stage& cur = S[step & 1];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier();  // every wave's share of this step is in LDS
-    v8i ao[8], bo[8];
-    int sav[8], sbv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rb = wn * 128 + i * 16 + rl;
-      bo[i] = operand(cur.b, rb, g);
-      sbv[i] = (int)((cur.sb[rb] >> (8 * g)) & 0xFFu);  // the other bytes must be zero
-      const int ra = wm * 128 + i * 16 + rl;
-      ao[i] = operand(cur.a, ra, g);
-      sav[i] = (int)((cur.sa[ra] >> (8 * g)) & 0xFFu);
-    }
-    if (step + 1 < total) {
-      int nm0 = m0, nn0 = n0;
-      if (ks + 1 == nk) tile_origin(blockIdx.x + (jt + 1) * gridDim.x, nm0, nn0);
-      load_stage(G, S[(step + 1) & 1], nm0, nn0, ks + 1 == nk ? 0 : ks + 1, wave, lane);
-    }
-    // the instruction computes B A^T here (B as its row operand), so that each
-    // lane ends with 4 consecutive columns of C for the epilogue
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bo[j], ao[i], acc[i][j], 0, 0, 0,
-                                                                     sbv[j], 0, sav[i]);
+__device__ __forceinline__ void store4(void* c, int64_t off, const v4f& v) {
+  if (OUT_BF16) {
+    const u32x2 w = {(uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
+                     (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c) + off) = w;
+  } else {
+    *reinterpret_cast<v4f*>(static_cast<float*>(c) + off) = v;
   }
+}
 
-    // Epilogue of the tile. acc[i][j] holds (B A^T) for B rows j*16 + 4g .. +3
-    // and A row i*16 + rl: lane (rl, g) has C[row i*16 + rl][columns
-    // j*16 + 4g .. +3], stored as one 8-byte (bf16) or 16-byte (fp32) store; a
-    // tile wholly inside C stores without per-element checks.
-    const bool full = G.vec && m0 + kBM <= G.M && n0 + kBN <= G.N;
+// Epilogue of a tile. acc[i][j] element 4 q + t holds C[row i*32 + rl]
+// [column j*32 + 8 q + 4 g + t] (rl = lane % 32, g = lane / 32): each lane
+// stores 4 groups of 4 consecutive elements, each as one 8-byte (bf16) or
+// 16-byte (fp32) store. A tile wholly inside C (a wave-uniform test) takes
+// straight-line stores; an edge tile checks each element. The accumulators
+// are cleared for the next tile.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const GemmArgs& G, int m0, int n0, int wm, int wn,
+                                           int lane, v16f (&acc)[4][4]) {
+  const int g = lane >> 5, rl = lane & 31;
+  if (G.vec && m0 + kBM <= G.M && n0 + kBN <= G.N) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = m0 + wm * 128 + i * 16 + rl;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + wm * 128 + i * 32 + rl;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + wn * 128 + j * 16 + 4 * g;
-        const v4f v = acc[i][j];
-        acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        if (full || (G.vec && row < G.M && col + 3 < G.N)) {
-          if (OUT_BF16) {
-            const uint2 w = make_uint2((uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
-                                       (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16));
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(G.c) + (int64_t)row * G.ldc + col) = w;
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(G.c) + (int64_t)row * G.ldc + col) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
-        } else if (row < G.M) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col + e < G.N) {
-              if (OUT_BF16)
-                static_cast<uint16_t*>(G.c)[(int64_t)row * G.ldc + col + e] = bf16_rne(v[e]);
-              else
-                static_cast<float*>(G.c)[(int64_t)row * G.ldc + col + e] = v[e];
+        for (int q = 0; q < 4; ++q) {
+          const v16f& a = acc[i][j];
+          store4<OUT_BF16>(G.c, row * G.ldc + n0 + wn * 128 + j * 32 + 8 * q + 4 * g,
+                           v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + rl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+          const v16f& a = acc[i][j];
+          const v4f v = v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          if (G.vec && row < G.M && col + 3 < G.N) {
+            store4<OUT_BF16>(G.c, (int64_t)row * G.ldc + col, v);
+          } else if (row < G.M) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (col + e < G.N) {
+                if (OUT_BF16)
+                  static_cast<uint16_t*>(G.c)[(int64_t)row * G.ldc + col + e] = bf16_rne(v[e]);
+                else
+                  static_cast<float*>(G.c)[(int64_t)row * G.ldc + col + e] = v[e];
+              }
             }
           }
         }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+}
+
+// Tile order: the 8 XCDs take workgroup ids round robin, so tile t is first
+// mapped to slot (t % 8) * (n / 8) + t / 8, giving each XCD (and its L2) a
+// contiguous run of the sequence (tiles b + j G stay on b's XCD); the
+// sequence walks groups of 4 tile rows column by column, so neighbours share
+// A rows or B rows.
+__device__ __forceinline__ void tile_origin(const GemmArgs& G, int t, int& m0, int& n0) {
+  const int nb = G.tiles_m * G.tiles_n;
+  int pid = t;
+  if (nb % 8 == 0) pid = (pid % 8) * (nb / 8) + pid / 8;
+  constexpr int kGroup = 4;
+  const int group = pid / (kGroup * G.tiles_n);
+  const int first = group * kGroup;
+  const int gsz = min(G.tiles_m - first, kGroup);
+  const int in_group = pid % (kGroup * G.tiles_n);
+  m0 = (first + in_group % gsz) * kBM;
+  n0 = (in_group / gsz) * kBN;
+}
+
+// Persistent kernel: workgroup b takes tiles b, b + G, b + 2G, ... (G = grid
+// size, a multiple of 8), as one sequence of (tile, K step) pairs, so the
+// next tile's first DMA streams during this tile's last step. Two LDS
+// stages. Each step waits for its own DMA (the only loads in flight); a
+// barrier then makes every wave's share visible and orders the refill of the
+// other stage after every wave's reads of it in the previous step. The step
+// issues the next step's DMA, then computes.
+//
+// PAIRS (the number of K steps per tile is even): the loop body is two steps,
+// the first reading S0 and filling S1, the second the reverse, so both stages
+// are named at compile time and the LDS reads overlap the DMA in flight.
+// Otherwise the stage alternates at run time and each step's reads wait for
+// the DMA it issued (correct, slower).
+template <bool OUT_BF16, bool PAIRS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_gemm_e4m3_kernel(GemmArgs G) {
+  __shared__ Stage S0, S1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave >> 1, wn = wave & 1;   // wave's 128 x 128 quarter of the tile
+  const int nb = G.tiles_m * G.tiles_n;
+  const int nk = G.K / kBK;
+  const int my_tiles = (nb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  if (my_tiles <= 0) return;
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  int m0, n0;
+  tile_origin(G, blockIdx.x, m0, n0);
+  load_stage(G, &S0, m0, n0, 0, wave, lane);
+  for (int jt = 0; jt < my_tiles; ++jt) {
+    // the tile after this one (past the last: this one again; its DMA then
+    // fills a stage no later step reads)
+    int nm0 = m0, nn0 = n0;
+    if (jt + 1 < my_tiles) tile_origin(G, blockIdx.x + (jt + 1) * gridDim.x, nm0, nn0);
+    if (PAIRS) {
+      for (int ks = 0; ks < nk; ks += 2) {
+        step_barrier();
+        k_step(G, &S1, &S0, m0, n0, ks + 1, wave, lane, wm, wn, acc);
+        const bool last = ks + 2 == nk;
+        step_barrier();
+        k_step(G, &S0, &S1, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 2, wave, lane,
+               wm, wn, acc);
+      }
+    } else {
+      for (int ks = 0; ks < nk; ++ks) {
+        const int step = jt * nk + ks;
+        const bool last = ks + 1 == nk;
+        step_barrier();
+        Stage* fill = (step & 1) ? &S0 : &S1;
+        const Stage* use = (step & 1) ? &S1 : &S0;
+        k_step(G, fill, use, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 1, wave, lane, wm,
+               wn, acc);
       }
     }
-    if (jt + 1 < my_tiles) tile_origin(blockIdx.x + (jt + 1) * gridDim.x, m0, n0);
+    store_tile<OUT_BF16>(G, m0, n0, wm, wn, lane, acc);
+    m0 = nm0;
+    n0 = nn0;
   }
+  // the last (repeated) DMA lands before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -295,10 +407,18 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   if (grid_i >= 8) grid_i -= grid_i % 8;
   const unsigned grid = (unsigned)grid_i;
   hipStream_t s = (hipStream_t)stream;
-  if (c_type == MXQ_OUT_BF16)
-    hipLaunchKernelGGL(mx_gemm_e4m3_kernel<true>, dim3(grid), dim3(kThreads), 0, s, G);
-  else
-    hipLaunchKernelGGL(mx_gemm_e4m3_kernel<false>, dim3(grid), dim3(kThreads), 0, s, G);
+  const bool pairs = (K / kBK) % 2 == 0;
+  if (c_type == MXQ_OUT_BF16) {
+    if (pairs)
+      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, G);
+    else
+      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, G);
+  } else {
+    if (pairs)
+      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, G);
+    else
+      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, G);
+  }
   if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP;
   return MXQ_OK;
 }

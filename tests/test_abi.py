@@ -166,6 +166,36 @@ def test_torch_helpers_refuse_cpu_tensors():
         mxq.mxcast(x.float())
 
 
+def test_caller_buffers_are_checked_before_any_launch():
+    # a buffer of the wrong size, dtype or layout would be an out-of-bounds GPU
+    # access, so the torch helpers refuse it on the host
+    import torch
+    cpu = torch.device("cpu")
+    codes = torch.zeros(4, 64, dtype=torch.uint8)
+    scales = torch.zeros(4, 2, dtype=torch.uint8)
+    inv = torch.zeros(4, dtype=torch.float32)
+    assert mxq._check_outputs((codes, scales, inv), 4, 64, mxq.MXQ_E4M3, cpu, True)[0] is codes
+    with pytest.raises(ValueError):      # E2M1 packs two codes per byte: [4, 32]
+        mxq._check_outputs((codes, scales, inv), 4, 64, mxq.MXQ_E2M1, cpu, True)
+    with pytest.raises(ValueError):
+        mxq._check_outputs((codes, scales[:, :1], inv), 4, 64, mxq.MXQ_E4M3, cpu, True)
+    with pytest.raises(ValueError):
+        mxq._check_outputs((codes, scales, inv.double()), 4, 64, mxq.MXQ_E4M3, cpu, True)
+    with pytest.raises(ValueError):
+        mxq._check_outputs((codes.t().contiguous().t(), scales, inv), 4, 64, mxq.MXQ_E4M3, cpu,
+                           True)
+    with pytest.raises(ValueError):
+        mxq._check_outputs((codes,), 4, 64, mxq.MXQ_E4M3, cpu, True)
+    with pytest.raises(ValueError):      # on another device than x
+        mxq._check_outputs((codes, scales, inv), 4, 64, mxq.MXQ_E4M3, torch.device("meta"), True)
+    mxq._check_gamma(None, 64, cpu)
+    mxq._check_gamma(torch.ones(64, dtype=torch.bfloat16), 64, cpu)
+    with pytest.raises(ValueError):
+        mxq._check_gamma(torch.ones(64, dtype=torch.float32), 64, cpu)
+    with pytest.raises(ValueError):
+        mxq._check_gamma(torch.ones(128, dtype=torch.bfloat16)[::2], 64, cpu)
+
+
 def test_product_path_does_not_touch_the_oracle():
     # the package and its sources never import or load the oracle
     pkg = os.path.join(ROOT, "norm_mx_quantisation_amd")

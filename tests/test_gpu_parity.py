@@ -695,6 +695,37 @@ def test_workload_mxfp4_sampled():
         check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r0 + 512), what=f"mxfp4 rows {r0}")
 
 
+# ---------------------------------------------------------------- caller buffers
+
+def test_helpers_refuse_mismatched_buffers_before_launching():
+    x = workloads.random_rows(8, 256, seed=5, device=DEV)
+    g = workloads.random_gamma(256, seed=6, device=DEV)
+    codes, scales, inv = mxq.mxnorm(x, g)
+    with pytest.raises(ValueError):
+        mxq.mxnorm(x, g, out=(codes[:4], scales, inv))
+    with pytest.raises(ValueError):
+        mxq.mxnorm(x, g.cpu())
+    with pytest.raises(ValueError):
+        mxq.mxcast(x, "e2m1", out=(codes, scales))          # E2M1 codes are [8, 128]
+    with pytest.raises(ValueError):
+        mxq.rmsnorm_mxcast(x, g, y=torch.empty(8, 128, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        mxq.mxnorm_backward(x, g, x, inv.cpu())
+    # mx_matmul: the output type follows out when out_dtype is not given, and
+    # an out of another type or shape is refused
+    a, sa = mxq.mxcast(x)
+    c16 = torch.empty(8, 8, dtype=torch.bfloat16, device=DEV)
+    r16 = mxq.mx_matmul(a, sa, a, sa, out=c16)
+    want = mxq.mx_matmul(a, sa, a, sa, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert r16 is c16 and torch.equal(c16, want)
+    with pytest.raises(ValueError):
+        mxq.mx_matmul(a, sa, a, sa, out_dtype=torch.float32, out=c16)
+    with pytest.raises(ValueError):
+        mxq.mx_matmul(a, sa, a, sa, out=torch.empty(8, 4, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- graph capture
 
 def test_graph_replays_match_eager():
