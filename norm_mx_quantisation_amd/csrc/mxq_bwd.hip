@@ -229,9 +229,17 @@ __global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int 
       a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
     }
   }
-  for (; r < r1; ++r) {
-    const float4 v = src[(size_t)r * D4 + qc];
-    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  {  // the last < 8 rows: every load in flight first, then the adds in row order
+    const int n = r1 - r;
+    float4 v[7];
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (u < n) v[u] = src[(size_t)(r + u) * D4 + qc];
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (u < n) {
+        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+      }
   }
   if (wave > 0) part[wave - 1][lane] = a;
   __syncthreads();
