@@ -212,14 +212,16 @@ typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;
  * cores with fp32 accumulation (order not specified); C is fp32 or bf16
  * (round to nearest even) [M, N] with row stride ldc elements. A NaN code or a
  * 0xFF scale makes the outputs it reaches NaN.
- *   a, b       codes, lda / ldb bytes per row (>= K), 16-byte aligned rows.
+ *   a, b       codes, lda / ldb bytes per row (>= K for E4M3, >= K/2 for packed
+ *              E2M1, element 2j in the low nibble of byte j), 16-byte aligned rows.
  *   a_scales, b_scales  E8M0 bytes, ldsa / ldsb per row (>= K/32, % 4 == 0),
  *              4-byte aligned.
- *   elem_a, elem_b  MXQ_E4M3 (MXQ_E2M1 is reserved: UNSUPPORTED).
+ *   elem_a, elem_b  MXQ_E4M3 or MXQ_E2M1, each operand its own (mixed pairs
+ *              allowed).
  *   c          aligned to its element; 16-byte (fp32) or 8-byte (bf16) aligned
  *              rows with ldc % 4 == 0 take vector stores.
  * Errors: SHAPE (M, N < 0, K <= 0, K % 32, a leading dimension too small), ARG
- * (unknown element or output type), UNSUPPORTED (E2M1, K % 128 != 0, sizes of
+ * (unknown element or output type), UNSUPPORTED (K % 128 != 0, sizes of
  * 2^31 or more), NULL, ALIGN, HIP. M == 0 or N == 0 is a no-op.
  */
 mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_scales, int64_t ldsa,

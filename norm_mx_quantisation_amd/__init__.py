@@ -333,18 +333,26 @@ def mxnorm_backward(x, gamma, dy, inv_norm, want_dgamma: bool = True, stream=Non
     return dx, row_dot, dgamma
 
 
-def mx_matmul(a_codes, a_scales, b_codes, b_scales, out_dtype=None, stream=None, out=None):
-    """C = A B^T for MX operands (uint8 codes [M, K] / [N, K], E8M0 scales [M, K/32] /
-    [N, K/32], E4M3). out_dtype torch.float32 (default) or torch.bfloat16."""
+def mx_matmul(a_codes, a_scales, b_codes, b_scales, out_dtype=None, stream=None, out=None,
+              fmt_a: str = "e4m3", fmt_b: str = "e4m3"):
+    """C = A B^T for MX operands: uint8 codes [M, K] / [N, K] (E4M3) or [M, K/2] /
+    [N, K/2] (packed E2M1, per fmt_a / fmt_b), E8M0 scales [M, K/32] / [N, K/32].
+    out_dtype torch.float32 (default) or torch.bfloat16."""
     import torch
     for t in (a_codes, a_scales, b_codes, b_scales):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 2 or not t.is_cuda:
             raise TypeError("MX operands must be 2-D uint8 GPU tensors")
         if t.stride(1) != 1:
             raise ValueError("MX operands need unit column stride")
-    M, K = a_codes.shape
+    if fmt_a not in _ELEM or fmt_b not in _ELEM:
+        raise ValueError(f"fmt_a / fmt_b must be one of {sorted(_ELEM)}")
+    ea, eb = _ELEM[fmt_a], _ELEM[fmt_b]
+    per_byte = lambda e: 2 if e == MXQ_E2M1 else 1   # elements per code byte
+    M = a_codes.shape[0]
     N = b_codes.shape[0]
-    if b_codes.shape[1] != K or a_scales.shape != (M, K // 32) or b_scales.shape != (N, K // 32):
+    K = a_codes.shape[1] * per_byte(ea)
+    if (b_codes.shape[1] * per_byte(eb) != K or a_scales.shape != (M, K // 32)
+            or b_scales.shape != (N, K // 32)):
         raise ValueError("MX operand shapes do not match")
     dev = a_codes.device
     if any(t.device != dev for t in (a_scales, b_codes, b_scales)):
@@ -363,7 +371,7 @@ def mx_matmul(a_codes, a_scales, b_codes, b_scales, out_dtype=None, stream=None,
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
     ld = lambda t: t.stride(0) if t.shape[0] > 1 else t.shape[1]
     st = mx_gemm(_ptr(a_codes), ld(a_codes), _ptr(a_scales), ld(a_scales), _ptr(b_codes),
-                 ld(b_codes), _ptr(b_scales), ld(b_scales), M, N, K, MXQ_E4M3, MXQ_E4M3, _ptr(c),
+                 ld(b_codes), _ptr(b_scales), ld(b_scales), M, N, K, ea, eb, _ptr(c),
                  ld(c) if M > 1 else N, ct, _stream(stream))
     if st != MXQ_OK:
         raise MxqError(st, "mx_gemm")

@@ -10,6 +10,10 @@
 // half its rate with 8-bit operands on MI355X, the 32 x 32 x 64 form near the
 // 5 PFLOP/s MXFP8 peak.)
 //
+// Either operand may be E2M1 (FP4, packed two to a byte, element 2j in the
+// low nibble): the same instruction with format code 4 runs FP4 operands at
+// nearly twice its 8-bit rate.
+//
 // Operand layout of that instruction for 8-bit data (probed on the device):
 // lane l carries row l % 32 of its 32 x 64 operand; its 32 bytes are K
 // [16 g, 16 g + 16) then [32 + 16 g, 32 + 16 g + 16), g = l / 32; the scale
@@ -18,7 +22,9 @@
 // row 8 (v / 4) + 4 (l / 32) + v % 4 (of the first operand) and column l % 32
 // (of the second). Here the instruction takes B as its first operand and A
 // as its second, so each lane's 16 results are C row l % 32 at 4 groups of 4
-// consecutive columns.
+// consecutive columns. For FP4 data (probed too) lane l carries K
+// [32 g, 32 g + 32) of row l % 32 as 32 nibbles in its first 16 bytes, even K
+// in the low nibble: exactly 16 consecutive bytes of a packed E2M1 row.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,7 +46,19 @@ constexpr int kThreads = 256;   // 4 waves, 2 x 2 over the tile
 constexpr int kBM = 256;        // tile rows (A)
 constexpr int kBN = 256;        // tile columns (B rows)
 constexpr int kBK = 128;        // K per step: 4 MX blocks, two MFMAs deep
-constexpr int kChunks = kBK / 16;   // 16-byte chunks per row and step
+constexpr int kChunks = kBK / 16;   // 16-byte chunks per row and step (8-bit codes)
+
+// MFMA format codes of the element types, and the 16-byte chunks a row of
+// that type holds per K step (8 for E4M3, 4 for packed E2M1).
+constexpr int kFmtE4M3 = 0, kFmtE2M1 = 4;
+template <int F> constexpr int chunks_of() { return F == kFmtE2M1 ? 4 : 8; }
+
+// Chunk c of row r sits at position c ^ swz(r): conflict-free for the 8
+// consecutive rows a quarter-wave reads (rows of 128 bytes: r & 7; rows of 64
+// bytes: (r >> 1) & 3, so two rows share the 32 banks and the 8 land apart).
+template <int CH> __device__ __forceinline__ int swz(int r) {
+  return CH == 8 ? (r & 7) : ((r >> 1) & 3);
+}
 
 struct GemmArgs {
   const uint8_t* a;
@@ -54,9 +72,8 @@ struct GemmArgs {
   int vec;  // C rows allow 4-element vector stores (aligned base, ldc % 4 == 0)
 };
 
-// One K step of both operands in LDS. Code rows hold 8 chunks of 16 bytes;
-// chunk c of row r sits at position c ^ (r & 7), so the 8 lanes that read one
-// 128-byte stretch of a row group touch all 32 banks once.
+// One K step of both operands in LDS. Code rows hold 8 (E4M3) or 4 (E2M1)
+// chunks of 16 bytes, swizzled as swz above.
 // The scale words (the step's 4 E8M0 bytes of a row) are stored in the order
 // the MFMA lanes consume them: position h * 128 + rl * 4 + blk holds row
 // h * 128 + blk * 32 + rl, so a lane's 4 words are contiguous.
@@ -71,31 +88,31 @@ __device__ __forceinline__ int scale_row(int p) {
   return (p >> 7) * 128 + (p & 3) * 32 + ((p >> 2) & 31);
 }
 
-// Direct-to-LDS loads of one K step. A wave instruction moves 64 x 16 bytes
-// = 8 rows; lane i lands at position i, i.e. row i / 8, physical chunk i % 8,
-// so it fetches logical chunk (i % 8) ^ (row & 7). Rows past the matrix end
-// re-read its last row (their results are never stored).
+// Direct-to-LDS loads of one operand's K step, CH chunks per row: a wave
+// instruction moves 64 x 16 bytes = 64 / CH rows; lane i lands at position
+// i, i.e. row i / CH, physical chunk i % CH, so it fetches logical chunk
+// (i % CH) ^ swz(row). Each wave moves CH such instructions. Rows past the
+// matrix end re-read its last row (their results are never stored).
+template <int CH>
+__device__ __forceinline__ void load_operand(const uint8_t* base, int64_t ld, int rows_valid,
+                                             uint4* dst, int r0, int ks, int wave, int lane) {
+  constexpr int kRows = kWave / CH;
+#pragma unroll
+  for (int q = 0; q < CH; ++q) {
+    const int blk = wave * CH + q;
+    const int r = blk * kRows + lane / CH;
+    const int c = (lane % CH) ^ swz<CH>(r);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(base + (int64_t)min(r0 + r, rows_valid - 1) * ld + ks * (16 * CH) + c * 16),
+        (lds_void*)&dst[blk * kWave], 16, 0, 0);
+  }
+}
+
+template <int FA, int FB>
 __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage* S, int m0, int n0, int ks,
                                            int wave, int lane) {
-  const int k0 = ks * kBK;
-#pragma unroll
-  for (int q = 0; q < kBM / 8 / 4; ++q) {
-    const int blk = wave * (kBM / 8 / 4) + q;
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    const int ra = min(m0 + r, G.M - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(G.a + (int64_t)ra * G.lda + k0 + c * 16),
-                                     (lds_void*)&S->a[blk * kWave], 16, 0, 0);
-  }
-#pragma unroll
-  for (int q = 0; q < kBN / 8 / 4; ++q) {
-    const int blk = wave * (kBN / 8 / 4) + q;
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    const int rb = min(n0 + r, G.N - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(G.b + (int64_t)rb * G.ldb + k0 + c * 16),
-                                     (lds_void*)&S->b[blk * kWave], 16, 0, 0);
-  }
+  load_operand<chunks_of<FA>()>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane);
+  load_operand<chunks_of<FB>()>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane);
   // scales: 4 bytes (the step's 4 blocks) per row; lane i of wave w fills
   // position w * 64 + i
   const int rs = scale_row(wave * kWave + lane);
@@ -105,12 +122,18 @@ __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage* S, int m0, 
                                    (lds_void*)&S->sb[wave * kWave], 4, 0, 0);
 }
 
-// The 32-byte MFMA operand of lane (row r, half g) for the K half kk of the
-// step (64 of its 128 bytes): chunks 4 kk + g and 4 kk + 2 + g.
+// The MFMA operand of lane (row r, half g) for the K half kk of the step.
+// 8-bit rows: chunks 4 kk + g and 4 kk + 2 + g (32 bytes). Packed FP4 rows:
+// chunk 2 kk + g (16 bytes; the upper half of the register block is unused).
+template <int CH>
 __device__ __forceinline__ v8i operand(const uint4* rows, int r, int kk, int g) {
-  const uint4 lo = rows[r * kChunks + ((4 * kk + g) ^ (r & 7))];
-  const uint4 hi = rows[r * kChunks + ((4 * kk + 2 + g) ^ (r & 7))];
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  if (CH == 8) {
+    const uint4 lo = rows[r * CH + ((4 * kk + g) ^ swz<CH>(r))];
+    const uint4 hi = rows[r * CH + ((4 * kk + 2 + g) ^ swz<CH>(r))];
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  const uint4 lo = rows[r * CH + ((2 * kk + g) ^ swz<CH>(r))];
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
 }
 
 // The scale words of the lane's 4 operand rows h * 128 + blk * 32 + rl
@@ -133,10 +156,12 @@ __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >
 // tells the DMA's writes from these reads and the reads overlap the DMA;
 // with a stage chosen at run time it waits for the DMA before the first
 // read.
+template <int FA, int FB>
 __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Stage* use, int fm0,
                                        int fn0, int fks, int wave, int lane, int wm, int wn,
                                        v16f (&acc)[4][4]) {
-  load_stage(G, fill, fm0, fn0, fks, wave, lane);
+  constexpr int CA = chunks_of<FA>(), CB = chunks_of<FB>();
+  load_stage<FA, FB>(G, fill, fm0, fn0, fks, wave, lane);
   __builtin_amdgcn_sched_barrier(0);  // the DMA goes out first: it has the whole step to land
   const int g = lane >> 5, rl = lane & 31;
   const uint4 sbw = scale_words(use->sb, wn, rl);
@@ -149,20 +174,20 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
     int sbv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bo[j] = operand(use->b, wn * 128 + j * 32 + rl, kk, g);
+      bo[j] = operand<CB>(use->b, wn * 128 + j * 32 + rl, kk, g);
       sbv[j] = scale_byte(sbw4[j], 2 * kk + g);
     }
-    v8i ao = operand(use->a, wm * 128 + rl, kk, g);
+    v8i ao = operand<CA>(use->a, wm * 128 + rl, kk, g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v8i ao_next;
-      if (i + 1 < 4) ao_next = operand(use->a, wm * 128 + (i + 1) * 32 + rl, kk, g);
+      if (i + 1 < 4) ao_next = operand<CA>(use->a, wm * 128 + (i + 1) * 32 + rl, kk, g);
       const int sav = scale_byte(saw4[i], 2 * kk + g);
       // B is the first operand, so each lane's results are consecutive columns of C
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo[j], ao, acc[i][j], 0, 0, 0,
-                                                                    sbv[j], 0, sav);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo[j], ao, acc[i][j], FB, FA,
+                                                                    0, sbv[j], 0, sav);
       if (i + 1 < 4) ao = ao_next;
       // keep the next block's reads ahead of this block's MFMAs (the
       // scheduler would otherwise sink them to their use and wait on each)
@@ -289,9 +314,9 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& G, int t, int& m0, i
 // are named at compile time and the LDS reads overlap the DMA in flight.
 // Otherwise the stage alternates at run time and each step's reads wait for
 // the DMA it issued (correct, slower).
-template <bool OUT_BF16, bool PAIRS>
+template <bool OUT_BF16, bool PAIRS, int FA, int FB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mx_gemm_e4m3_kernel(GemmArgs G) {
+void mx_gemm_kernel(GemmArgs G) {
   __shared__ Stage S0, S1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -309,7 +334,7 @@ void mx_gemm_e4m3_kernel(GemmArgs G) {
 
   int m0, n0;
   tile_origin(G, blockIdx.x, m0, n0);
-  load_stage(G, &S0, m0, n0, 0, wave, lane);
+  load_stage<FA, FB>(G, &S0, m0, n0, 0, wave, lane);
   for (int jt = 0; jt < my_tiles; ++jt) {
     // the tile after this one (past the last: this one again; its DMA then
     // fills a stage no later step reads)
@@ -318,11 +343,11 @@ void mx_gemm_e4m3_kernel(GemmArgs G) {
     if (PAIRS) {
       for (int ks = 0; ks < nk; ks += 2) {
         step_barrier();
-        k_step(G, &S1, &S0, m0, n0, ks + 1, wave, lane, wm, wn, acc);
+        k_step<FA, FB>(G, &S1, &S0, m0, n0, ks + 1, wave, lane, wm, wn, acc);
         const bool last = ks + 2 == nk;
         step_barrier();
-        k_step(G, &S0, &S1, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 2, wave, lane,
-               wm, wn, acc);
+        k_step<FA, FB>(G, &S0, &S1, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 2, wave,
+                       lane, wm, wn, acc);
       }
     } else {
       for (int ks = 0; ks < nk; ++ks) {
@@ -331,8 +356,8 @@ void mx_gemm_e4m3_kernel(GemmArgs G) {
         step_barrier();
         Stage* fill = (step & 1) ? &S0 : &S1;
         const Stage* use = (step & 1) ? &S1 : &S0;
-        k_step(G, fill, use, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 1, wave, lane, wm,
-               wn, acc);
+        k_step<FA, FB>(G, fill, use, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 1, wave,
+                       lane, wm, wn, acc);
       }
     }
     store_tile<OUT_BF16>(G, m0, n0, wm, wn, lane, acc);
@@ -363,6 +388,21 @@ int cu_count() {
 
 }  // namespace
 
+template <int FA, int FB>
+void launch_gemm(const GemmArgs& G, bool bf16, bool pairs, unsigned grid, hipStream_t s) {
+  if (bf16) {
+    if (pairs)
+      hipLaunchKernelGGL((mx_gemm_kernel<true, true, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<true, false, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
+  } else {
+    if (pairs)
+      hipLaunchKernelGGL((mx_gemm_kernel<false, true, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<false, false, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
+  }
+}
+
 extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_scales, int64_t ldsa,
                               const uint8_t* b, int64_t ldb, const uint8_t* b_scales, int64_t ldsb,
                               int64_t M, int64_t N, int64_t K, mxq_elem elem_a, mxq_elem elem_b,
@@ -371,8 +411,9 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   if (elem_a != MXQ_E4M3 && elem_a != MXQ_E2M1) return MXQ_ERR_ARG;
   if (elem_b != MXQ_E4M3 && elem_b != MXQ_E2M1) return MXQ_ERR_ARG;
   if (c_type != MXQ_OUT_F32 && c_type != MXQ_OUT_BF16) return MXQ_ERR_ARG;
-  if (lda < K || ldb < K || ldsa < K / 32 || ldsb < K / 32 || ldc < N) return MXQ_ERR_SHAPE;
-  if (elem_a != MXQ_E4M3 || elem_b != MXQ_E4M3) return MXQ_ERR_UNSUPPORTED;
+  // code bytes per row: K for E4M3, K / 2 for packed E2M1
+  const int64_t row_a = elem_a == MXQ_E2M1 ? K / 2 : K, row_b = elem_b == MXQ_E2M1 ? K / 2 : K;
+  if (lda < row_a || ldb < row_b || ldsa < K / 32 || ldsb < K / 32 || ldc < N) return MXQ_ERR_SHAPE;
   if (K % kBK != 0 || M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31))
     return MXQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MXQ_OK;
@@ -408,17 +449,15 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   const unsigned grid = (unsigned)grid_i;
   hipStream_t s = (hipStream_t)stream;
   const bool pairs = (K / kBK) % 2 == 0;
-  if (c_type == MXQ_OUT_BF16) {
-    if (pairs)
-      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, G);
-    else
-      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, G);
-  } else {
-    if (pairs)
-      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, G);
-    else
-      hipLaunchKernelGGL((mx_gemm_e4m3_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, G);
-  }
+  const bool bf16 = c_type == MXQ_OUT_BF16;
+  if (elem_a == MXQ_E4M3 && elem_b == MXQ_E4M3)
+    launch_gemm<kFmtE4M3, kFmtE4M3>(G, bf16, pairs, grid, s);
+  else if (elem_a == MXQ_E4M3)
+    launch_gemm<kFmtE4M3, kFmtE2M1>(G, bf16, pairs, grid, s);
+  else if (elem_b == MXQ_E4M3)
+    launch_gemm<kFmtE2M1, kFmtE4M3>(G, bf16, pairs, grid, s);
+  else
+    launch_gemm<kFmtE2M1, kFmtE2M1>(G, bf16, pairs, grid, s);
   if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP;
   return MXQ_OK;
 }

@@ -48,9 +48,14 @@ CASES = (
     # and the feed-forward up projection (14336 rows)
     ("llama3_8b_preattn mx_gemm qkv N=6144", "llama3_8b_preattn", "gemm", {"N": 6144}),
     ("llama3_8b_preattn mx_gemm ffn-up N=14336", "llama3_8b_preattn", "gemm", {"N": 14336}),
+    # the same projections in MXFP4: E2M1 activations of mxfp4 [32768, 4096]
+    # times an E2M1 weight
+    ("mxfp4 mx_gemm e2m1 qkv N=6144", "mxfp4", "gemm", {"N": 6144, "elem": mxq.MXQ_E2M1}),
+    ("mxfp4 mx_gemm e2m1 ffn-up N=14336", "mxfp4", "gemm", {"N": 14336, "elem": mxq.MXQ_E2M1}),
 )
 
-PEAK_MXFP8_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
+PEAK_MXFP8_TFLOPS = 5000.0    # MI355X dense FP8 / MXFP8 matrix peak
+PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense FP4 / MXFP4 matrix peak
 
 
 def algorithmic_bytes(op, T, D, elem):
@@ -68,15 +73,18 @@ def run_gemm(torch, name, wl, opt, steps, warmup):
     x0, g = workloads.make_inputs(wl, device="cuda")
     M, K = x0.shape
     N = opt["N"]
-    A, SA, _ = mxq.mxnorm(x0, None, 2.0)
+    elem = opt.get("elem", mxq.MXQ_E4M3)
+    fmt = "e2m1" if elem == mxq.MXQ_E2M1 else "e4m3"
+    row = K // 2 if elem == mxq.MXQ_E2M1 else K
+    A, SA, _ = mxq.mxnorm(x0, None, 2.0, fmt=fmt)
     w = workloads.random_rows(N, K, seed=11, device="cuda", scale=0.02)
-    B, SB = mxq.mxcast((w.float() * g.float()[None, :]).to(torch.bfloat16))
+    B, SB = mxq.mxcast((w.float() * g.float()[None, :]).to(torch.bfloat16), fmt=fmt)
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     L = mxq.lib()
     vp = ctypes.c_void_p
     stream = vp(torch.cuda.current_stream().cuda_stream)
-    args = (vp(A.data_ptr()), K, vp(SA.data_ptr()), K // 32, vp(B.data_ptr()), K, vp(SB.data_ptr()),
-            K // 32, M, N, K, mxq.MXQ_E4M3, mxq.MXQ_E4M3, vp(C.data_ptr()), N, mxq.MXQ_OUT_BF16,
+    args = (vp(A.data_ptr()), row, vp(SA.data_ptr()), K // 32, vp(B.data_ptr()), row,
+            vp(SB.data_ptr()), K // 32, M, N, K, elem, elem, vp(C.data_ptr()), N, mxq.MXQ_OUT_BF16,
             stream)
 
     def launch(i):
@@ -96,8 +104,10 @@ def run_gemm(torch, name, wl, opt, steps, warmup):
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / steps
     tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    peak, pname = ((PEAK_MXFP4_TFLOPS, "MXFP4") if elem == mxq.MXQ_E2M1
+                   else (PEAK_MXFP8_TFLOPS, "MXFP8"))
     print(f"{name:44s} M={M:6d} N={N:6d} K={K:5d} {us:9.2f} us/launch (events, back-to-back)  "
-          f"{tflops:8.1f} TFLOP/s  {100 * tflops / PEAK_MXFP8_TFLOPS:5.1f}% of MXFP8 peak",
+          f"{tflops:8.1f} TFLOP/s  {100 * tflops / peak:5.1f}% of {pname} peak",
           flush=True)
     del A, SA, B, SB, C
     torch.cuda.empty_cache()

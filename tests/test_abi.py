@@ -268,7 +268,11 @@ def test_gemm_argument_errors():
     assert gemm(ldc=100) == mxq.MXQ_ERR_SHAPE
     assert gemm(ea=3) == mxq.MXQ_ERR_ARG
     assert gemm(ct=2) == mxq.MXQ_ERR_ARG
-    assert gemm(ea=1) == mxq.MXQ_ERR_UNSUPPORTED           # E2M1 operands are reserved
+    # packed E2M1 rows hold K / 2 bytes: lda = 2048 passes the shape check
+    assert gemm(ea=1, lda=2047) == mxq.MXQ_ERR_SHAPE
+    assert gemm(ea=1, lda=2048, a=None) == mxq.MXQ_ERR_NULL
+    assert gemm(eb=1, ldb=2048, b=None) == mxq.MXQ_ERR_NULL
+    assert gemm(eb=1, ldb=2032) == mxq.MXQ_ERR_SHAPE
     assert gemm(K=160, lda=160, ldb=160, ldsa=8, ldsb=8) == mxq.MXQ_ERR_UNSUPPORTED  # K % 128
     assert gemm(a=None) == mxq.MXQ_ERR_NULL
     assert gemm(c=None) == mxq.MXQ_ERR_NULL

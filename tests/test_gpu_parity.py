@@ -446,12 +446,13 @@ def gemm_bound(ab, K, c64, bf16):
     return b
 
 
-def check_gemm(A, SA, B, SB, out_dtype=torch.float32, rows=None, what=""):
-    K = A.shape[1]
-    c = mxq.mx_matmul(A, SA, B, SB, out_dtype)
+def check_gemm(A, SA, B, SB, out_dtype=torch.float32, rows=None, what="", fa="e4m3", fb="e4m3"):
+    K = SA.shape[1] * 32
+    c = mxq.mx_matmul(A, SA, B, SB, out_dtype, fmt_a=fa, fmt_b=fb)
     torch.cuda.synchronize()
     r0, r1 = (0, A.shape[0]) if rows is None else rows
-    c64, ab = oracle.mx_gemm(np_(A[r0:r1]), np_(SA[r0:r1]), np_(B), np_(SB), K, threads=THREADS)
+    c64, ab = oracle.mx_gemm(np_(A[r0:r1]), np_(SA[r0:r1]), np_(B), np_(SB), K, fa, fb,
+                             threads=THREADS)
     got = c[r0:r1].double().cpu().numpy()
     bound = gemm_bound(ab, K, c64, out_dtype == torch.bfloat16)
     fin = np.isfinite(c64)
@@ -474,10 +475,12 @@ def test_gemm_exact_small_integers():
     assert np.array_equal(c.double().cpu().numpy(), c64)
 
 
-def random_mx_operand(rows, K, seed, scale_lo=115, scale_hi=135):
+def random_mx_operand(rows, K, seed, scale_lo=115, scale_hi=135, fmt="e4m3"):
     g = torch.Generator().manual_seed(seed)
-    codes = torch.randint(0, 256, (rows, K), generator=g, dtype=torch.int32).to(torch.uint8)
-    codes[(codes & 0x7F) == 0x7F] = 0x3C                   # no NaN codes
+    width = K // 2 if fmt == "e2m1" else K                 # packed E2M1: every byte is valid
+    codes = torch.randint(0, 256, (rows, width), generator=g, dtype=torch.int32).to(torch.uint8)
+    if fmt == "e4m3":
+        codes[(codes & 0x7F) == 0x7F] = 0x3C               # no NaN codes
     scales = torch.randint(scale_lo, scale_hi, (rows, K // 32), generator=g,
                            dtype=torch.int32).to(torch.uint8)
     return codes.to(DEV), scales.to(DEV)
@@ -528,6 +531,86 @@ def test_gemm_consumes_mxnorm_output():
     B, SB = mxq.mxcast(wg)
     for r0 in (0, 4096, x.shape[0] - 16):
         check_gemm(A, SA, B, SB, torch.bfloat16, rows=(r0, r0 + 16), what=f"mxnormlinear {r0}")
+
+
+FP4_PAIRS = [("e2m1", "e2m1"), ("e4m3", "e2m1"), ("e2m1", "e4m3")]
+
+
+@pytest.mark.parametrize("fa,fb", FP4_PAIRS)
+def test_gemm_fp4_exact_small_integers(fa, fb):
+    # every E2M1 value times another or one of {0, +-.5, +-1, +-2, +-4}, at
+    # scale 2^0: each product is a multiple of 1/4 of at most 36, each partial
+    # sum a multiple of 1/4 below 2^16, so the fp32 result is exact in any order
+    g = torch.Generator().manual_seed(509)
+    M, N, K = 256, 384, 1024
+
+    def operand(rows, fmt):
+        if fmt == "e2m1":
+            return torch.randint(0, 256, (rows, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+        return torch.from_numpy(E4M3_SMALL_INTS[torch.randint(0, 9, (rows, K), generator=g).numpy()])
+
+    A, B = operand(M, fa), operand(N, fb)
+    SA = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    SB = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    c = mxq.mx_matmul(A.to(DEV), SA.to(DEV), B.to(DEV), SB.to(DEV), fmt_a=fa, fmt_b=fb)
+    torch.cuda.synchronize()
+    c64, _ = oracle.mx_gemm(A.numpy(), SA.numpy(), B.numpy(), SB.numpy(), K, fa, fb)
+    assert np.array_equal(c.double().cpu().numpy(), c64)
+
+
+@pytest.mark.parametrize("fa,fb", FP4_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 200, 256), (513, 257, 384),
+                                   (1, 7, 4096)])
+def test_gemm_fp4_random_operands(fa, fb, M, N, K):
+    A, SA = random_mx_operand(M, K, 510 + M, fmt=fa)
+    B, SB = random_mx_operand(N, K, 511 + N, fmt=fb)
+    check_gemm(A, SA, B, SB, what=f"gemm {fa}x{fb} {M}x{N}x{K}", fa=fa, fb=fb)
+
+
+def test_gemm_fp4_bf16_output_and_strided():
+    A, SA = random_mx_operand(384, 512, 512, fmt="e2m1")
+    B, SB = random_mx_operand(320, 512, 513, fmt="e2m1")
+    c32, _ = check_gemm(A, SA, B, SB, what="gemm fp4 f32", fa="e2m1", fb="e2m1")
+    c16, _ = check_gemm(A, SA, B, SB, torch.bfloat16, what="gemm fp4 bf16", fa="e2m1", fb="e2m1")
+    assert torch.equal(c16, c32.to(torch.bfloat16))
+    # packed rows of 256 bytes inside rows of 320
+    Aw = torch.zeros(384, 320, dtype=torch.uint8, device=DEV)
+    Aw[:, :256] = A
+    c2 = mxq.mx_matmul(Aw[:, :256], SA, B, SB, fmt_a="e2m1", fmt_b="e2m1")
+    torch.cuda.synchronize()
+    assert torch.equal(c2, c32)
+
+
+def test_gemm_fp4_nan_scale():
+    A, SA = random_mx_operand(256, 256, 514, fmt="e2m1")
+    B, SB = random_mx_operand(256, 256, 515, fmt="e2m1")
+    SA[7, 3] = 255                                         # NaN scale: row 7
+    c, _ = check_gemm(A, SA, B, SB, what="gemm fp4 nan scale", fa="e2m1", fb="e2m1")
+    assert torch.isnan(c[7]).all() and not torch.isnan(c[:7]).any()
+
+
+def test_gemm_consumes_mxfp4_mxnorm_output():
+    # MXNormLinear in MXFP4: E2M1 activations of the mxfp4 workload through
+    # mxnorm_fwd, the gain-folded weight MX-cast to E2M1, then the MX GEMM;
+    # sampled rows against the oracle
+    x, g = workloads.make_inputs("mxfp4", device=DEV)
+    N = 512
+    w = workloads.random_rows(N, x.shape[1], seed=516, device=DEV, scale=0.02)
+    wg = (w.float() * g.float()[None, :]).to(torch.bfloat16)
+    A, SA, _ = mxq.mxnorm(x, None, 2.0, fmt="e2m1")
+    B, SB = mxq.mxcast(wg, fmt="e2m1")
+    for r0 in (0, 20000, x.shape[0] - 16):
+        check_gemm(A, SA, B, SB, torch.bfloat16, rows=(r0, r0 + 16), what=f"mxfp4 linear {r0}",
+                   fa="e2m1", fb="e2m1")
+
+
+def test_mx_matmul_checks_formats():
+    A, SA = random_mx_operand(64, 256, 517, fmt="e2m1")
+    B, SB = random_mx_operand(64, 256, 518)
+    with pytest.raises(ValueError):                        # [64, 128] codes are K = 128 as E4M3
+        mxq.mx_matmul(A, SA, B, SB)
+    with pytest.raises(ValueError):
+        mxq.mx_matmul(A, SA, B, SB, fmt_a="e5m2")
 
 
 # ---------------------------------------------------------------- E8M0 round-up scale rule
