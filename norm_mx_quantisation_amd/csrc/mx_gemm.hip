@@ -88,33 +88,81 @@ __device__ __forceinline__ int scale_row(int p) {
   return (p >> 7) * 128 + (p & 3) * 32 + ((p >> 2) & 31);
 }
 
+// The scales of kScaleSteps consecutive K steps: 16 E8M0 bytes of each row,
+// moved by one 16-byte DMA per row (entry r holds tile row r; word s of it is
+// step s's 4 blocks). One request per row brings four steps' scales, where
+// loading them step by step costs a whole L2 request for 4 bytes.
+constexpr int kScaleSteps = 4;
+struct ScaleGroup {
+  uint4 a[kBM];
+  uint4 b[kBN];
+};
+
+// Steps to spread one step's code DMA over (blocks of 4 MFMAs each), so that
+// the wave does not stall issuing it all at once.
+constexpr int kSpread = 4;
+
 // Direct-to-LDS loads of one operand's K step, CH chunks per row: a wave
 // instruction moves 64 x 16 bytes = 64 / CH rows; lane i lands at position
 // i, i.e. row i / CH, physical chunk i % CH, so it fetches logical chunk
 // (i % CH) ^ swz(row). Each wave moves CH such instructions. Rows past the
 // matrix end re-read its last row (their results are never stored).
 template <int CH>
+__device__ __forceinline__ void load_one(const uint8_t* base, int64_t ld, int rows_valid,
+                                         uint4* dst, int r0, int ks, int wave, int lane, int q) {
+  constexpr int kRows = kWave / CH;
+  const int blk = wave * CH + q;
+  const int r = blk * kRows + lane / CH;
+  const int c = (lane % CH) ^ swz<CH>(r);
+  __builtin_amdgcn_global_load_lds(
+      (const void*)(base + (int64_t)min(r0 + r, rows_valid - 1) * ld + ks * (16 * CH) + c * 16),
+      (lds_void*)&dst[blk * kWave], 16, 0, 0);
+}
+
+template <int CH>
 __device__ __forceinline__ void load_operand(const uint8_t* base, int64_t ld, int rows_valid,
                                              uint4* dst, int r0, int ks, int wave, int lane) {
-  constexpr int kRows = kWave / CH;
 #pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const int blk = wave * CH + q;
-    const int r = blk * kRows + lane / CH;
-    const int c = (lane % CH) ^ swz<CH>(r);
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(base + (int64_t)min(r0 + r, rows_valid - 1) * ld + ks * (16 * CH) + c * 16),
-        (lds_void*)&dst[blk * kWave], 16, 0, 0);
+  for (int q = 0; q < CH; ++q) load_one<CH>(base, ld, rows_valid, dst, r0, ks, wave, lane, q);
+}
+
+// Piece `piece` (of kSpread) of a step's code DMA: its share of the A then
+// B instructions.
+template <int FA, int FB>
+__device__ __forceinline__ void load_codes_piece(const GemmArgs& G, Stage* S, int m0, int n0,
+                                                 int ks, int wave, int lane, int piece) {
+  constexpr int CA = chunks_of<FA>(), CB = chunks_of<FB>();
+#pragma unroll
+  for (int t = 0; t < CA + CB; ++t) {
+    if (t * kSpread / (CA + CB) != piece) continue;
+    if (t < CA)
+      load_one<CA>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane, t);
+    else
+      load_one<CB>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane, t - CA);
   }
 }
 
-template <int FA, int FB>
+// Scale group gk (K steps kScaleSteps gk ...) of the tile's rows: lane i of
+// wave w moves row w * 64 + i's 16 bytes. Needs 16-byte aligned scale rows
+// with at least 16 (gk + 1) bytes.
+__device__ __forceinline__ void load_scale_group(const GemmArgs& G, ScaleGroup* SG, int m0, int n0,
+                                                 int gk, int wave, int lane) {
+  const int r = wave * kWave + lane;
+  __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + r, G.M - 1) * G.ldsa + gk * 16),
+                                   (lds_void*)&SG->a[wave * kWave], 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + r, G.N - 1) * G.ldsb + gk * 16),
+                                   (lds_void*)&SG->b[wave * kWave], 16, 0, 0);
+}
+
+// A whole step's codes and, step by step (GROUPED false), its scales: 4
+// bytes (the step's 4 blocks) per row; lane i of wave w fills position
+// w * 64 + i.
+template <int FA, int FB, bool GROUPED>
 __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage* S, int m0, int n0, int ks,
                                            int wave, int lane) {
   load_operand<chunks_of<FA>()>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane);
   load_operand<chunks_of<FB>()>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane);
-  // scales: 4 bytes (the step's 4 blocks) per row; lane i of wave w fills
-  // position w * 64 + i
+  if (GROUPED) return;
   const int rs = scale_row(wave * kWave + lane);
   __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + rs, G.M - 1) * G.ldsa + ks * 4),
                                    (lds_void*)&S->sa[wave * kWave], 4, 0, 0);
@@ -151,23 +199,41 @@ __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >
 // halves of 64 (the MX blocks 2 kk and 2 kk + 1 of the step). Per half, the
 // 4 B operands are read first and the A operand one 32-row block ahead of
 // the 4 MFMAs that use it, so the reads overlap the MFMAs. That `use` has
-// landed is the caller's wait and barrier. When `fill` and `use` are two
-// distinct LDS objects known at compile time, the compiler's alias analysis
-// tells the DMA's writes from these reads and the reads overlap the DMA;
-// with a stage chosen at run time it waits for the DMA before the first
-// read.
-template <int FA, int FB>
+// landed is the caller's wait and barrier.
+//
+// GROUPED: `fill` and `use` are two distinct LDS objects known at compile
+// time, so the compiler's alias analysis tells the DMA's writes from these
+// reads and the reads overlap the DMA in flight; the code DMA is spread over
+// the first K half's 4 blocks of MFMAs. The step's scales are word `sstep`
+// of the scale group `sg`; when `sg_fill` is set, the next group (group sgk
+// of the tile at sm0, sn0) goes out right after those reads.
+// Otherwise (stages chosen at run time) the whole DMA, scales included, goes
+// out first and the compiler waits for it before the first LDS read.
+template <int FA, int FB, bool GROUPED>
 __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Stage* use, int fm0,
                                        int fn0, int fks, int wave, int lane, int wm, int wn,
-                                       v16f (&acc)[4][4]) {
+                                       v16f (&acc)[4][4], const ScaleGroup* sg, int sstep,
+                                       ScaleGroup* sg_fill, int sm0, int sn0, int sgk) {
   constexpr int CA = chunks_of<FA>(), CB = chunks_of<FB>();
-  load_stage<FA, FB>(G, fill, fm0, fn0, fks, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);  // the DMA goes out first: it has the whole step to land
+  if (!GROUPED) {
+    load_stage<FA, FB, false>(G, fill, fm0, fn0, fks, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const int g = lane >> 5, rl = lane & 31;
-  const uint4 sbw = scale_words(use->sb, wn, rl);
-  const uint4 saw = scale_words(use->sa, wm, rl);
-  const uint32_t sbw4[4] = {sbw.x, sbw.y, sbw.z, sbw.w};
-  const uint32_t saw4[4] = {saw.x, saw.y, saw.z, saw.w};
+  uint32_t sbw4[4], saw4[4];
+  if (GROUPED) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sbw4[j] = reinterpret_cast<const uint32_t*>(&sg->b[wn * 128 + j * 32 + rl])[sstep];
+      saw4[j] = reinterpret_cast<const uint32_t*>(&sg->a[wm * 128 + j * 32 + rl])[sstep];
+    }
+    if (sg_fill) load_scale_group(G, sg_fill, sm0, sn0, sgk, wave, lane);
+  } else {
+    const uint4 sbw = scale_words(use->sb, wn, rl);
+    const uint4 saw = scale_words(use->sa, wm, rl);
+    sbw4[0] = sbw.x, sbw4[1] = sbw.y, sbw4[2] = sbw.z, sbw4[3] = sbw.w;
+    saw4[0] = saw.x, saw4[1] = saw.y, saw4[2] = saw.z, saw4[3] = saw.w;
+  }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     v8i bo[4];
@@ -182,6 +248,7 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
     for (int i = 0; i < 4; ++i) {
       v8i ao_next;
       if (i + 1 < 4) ao_next = operand<CA>(use->a, wm * 128 + (i + 1) * 32 + rl, kk, g);
+      if (GROUPED && kk == 0) load_codes_piece<FA, FB>(G, fill, fm0, fn0, fks, wave, lane, i);
       const int sav = scale_byte(saw4[i], 2 * kk + g);
       // B is the first operand, so each lane's results are consecutive columns of C
 #pragma unroll
@@ -309,15 +376,21 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& G, int t, int& m0, i
 // other stage after every wave's reads of it in the previous step. The step
 // issues the next step's DMA, then computes.
 //
-// PAIRS (the number of K steps per tile is even): the loop body is two steps,
-// the first reading S0 and filling S1, the second the reverse, so both stages
-// are named at compile time and the LDS reads overlap the DMA in flight.
-// Otherwise the stage alternates at run time and each step's reads wait for
-// the DMA it issued (correct, slower).
-template <bool OUT_BF16, bool PAIRS, int FA, int FB>
+// GROUPED (K a multiple of kScaleSteps steps, 16-byte aligned scale rows):
+// the loop body is two steps, the first reading S0 and filling S1, the
+// second the reverse, so both stages are named at compile time and the LDS
+// reads overlap the DMA in flight. The scales come in groups of kScaleSteps
+// steps, double-buffered in SG0 / SG1 (group number, counted across tiles,
+// even: SG0): a group's first step issues the next group's DMA into the
+// other buffer, whose last reads (the previous group's) the step's barrier
+// has ordered before it, and the next step's wait and barrier see it landed.
+// Otherwise the stage alternates at run time, scales come step by step, and
+// each step's reads wait for the DMA it issued (correct, slower).
+template <bool OUT_BF16, bool GROUPED, int FA, int FB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mx_gemm_kernel(GemmArgs G) {
   __shared__ Stage S0, S1;
+  __shared__ ScaleGroup SG0, SG1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;   // wave's 128 x 128 quarter of the tile
@@ -334,20 +407,30 @@ void mx_gemm_kernel(GemmArgs G) {
 
   int m0, n0;
   tile_origin(G, blockIdx.x, m0, n0);
-  load_stage<FA, FB>(G, &S0, m0, n0, 0, wave, lane);
+  load_stage<FA, FB, GROUPED>(G, &S0, m0, n0, 0, wave, lane);
+  if (GROUPED) load_scale_group(G, &SG0, m0, n0, 0, wave, lane);
   for (int jt = 0; jt < my_tiles; ++jt) {
     // the tile after this one (past the last: this one again; its DMA then
     // fills a stage no later step reads)
     int nm0 = m0, nn0 = n0;
     if (jt + 1 < my_tiles) tile_origin(G, blockIdx.x + (jt + 1) * gridDim.x, nm0, nn0);
-    if (PAIRS) {
+    if (GROUPED) {
+      const int ng = nk / kScaleSteps;
       for (int ks = 0; ks < nk; ks += 2) {
+        const int gi = jt * ng + ks / kScaleSteps;
+        const ScaleGroup* sg = (gi & 1) ? &SG1 : &SG0;
+        ScaleGroup* sg_next = (gi & 1) ? &SG0 : &SG1;
+        const bool gstart = ks % kScaleSteps == 0;
+        const bool glast = ks + kScaleSteps >= nk;   // next group: the next tile's first
         step_barrier();
-        k_step<FA, FB>(G, &S1, &S0, m0, n0, ks + 1, wave, lane, wm, wn, acc);
+        k_step<FA, FB, true>(G, &S1, &S0, m0, n0, ks + 1, wave, lane, wm, wn, acc, sg,
+                             ks % kScaleSteps, gstart ? sg_next : nullptr, glast ? nm0 : m0,
+                             glast ? nn0 : n0, glast ? 0 : ks / kScaleSteps + 1);
         const bool last = ks + 2 == nk;
         step_barrier();
-        k_step<FA, FB>(G, &S0, &S1, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 2, wave,
-                       lane, wm, wn, acc);
+        k_step<FA, FB, true>(G, &S0, &S1, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 2,
+                             wave, lane, wm, wn, acc, sg, (ks + 1) % kScaleSteps, nullptr, 0, 0,
+                             0);
       }
     } else {
       for (int ks = 0; ks < nk; ++ks) {
@@ -356,8 +439,8 @@ void mx_gemm_kernel(GemmArgs G) {
         step_barrier();
         Stage* fill = (step & 1) ? &S0 : &S1;
         const Stage* use = (step & 1) ? &S1 : &S0;
-        k_step<FA, FB>(G, fill, use, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 1, wave,
-                       lane, wm, wn, acc);
+        k_step<FA, FB, false>(G, fill, use, last ? nm0 : m0, last ? nn0 : n0, last ? 0 : ks + 1,
+                              wave, lane, wm, wn, acc, nullptr, 0, nullptr, 0, 0, 0);
       }
     }
     store_tile<OUT_BF16>(G, m0, n0, wm, wn, lane, acc);
@@ -389,14 +472,14 @@ int cu_count() {
 }  // namespace
 
 template <int FA, int FB>
-void launch_gemm(const GemmArgs& G, bool bf16, bool pairs, unsigned grid, hipStream_t s) {
+void launch_gemm(const GemmArgs& G, bool bf16, bool grouped, unsigned grid, hipStream_t s) {
   if (bf16) {
-    if (pairs)
+    if (grouped)
       hipLaunchKernelGGL((mx_gemm_kernel<true, true, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
     else
       hipLaunchKernelGGL((mx_gemm_kernel<true, false, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
   } else {
-    if (pairs)
+    if (grouped)
       hipLaunchKernelGGL((mx_gemm_kernel<false, true, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
     else
       hipLaunchKernelGGL((mx_gemm_kernel<false, false, FA, FB>), dim3(grid), dim3(kThreads), 0, s, G);
@@ -448,16 +531,19 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   if (grid_i >= 8) grid_i -= grid_i % 8;
   const unsigned grid = (unsigned)grid_i;
   hipStream_t s = (hipStream_t)stream;
-  const bool pairs = (K / kBK) % 2 == 0;
+  // the fast loop: whole scale groups (16 bytes of each scale row per
+  // kScaleSteps steps, so 16-byte aligned rows) and an even step count
+  const bool grouped = K % (kBK * kScaleSteps) == 0 && aligned(a_scales, 16) &&
+                       aligned(b_scales, 16) && ldsa % 16 == 0 && ldsb % 16 == 0;
   const bool bf16 = c_type == MXQ_OUT_BF16;
   if (elem_a == MXQ_E4M3 && elem_b == MXQ_E4M3)
-    launch_gemm<kFmtE4M3, kFmtE4M3>(G, bf16, pairs, grid, s);
+    launch_gemm<kFmtE4M3, kFmtE4M3>(G, bf16, grouped, grid, s);
   else if (elem_a == MXQ_E4M3)
-    launch_gemm<kFmtE4M3, kFmtE2M1>(G, bf16, pairs, grid, s);
+    launch_gemm<kFmtE4M3, kFmtE2M1>(G, bf16, grouped, grid, s);
   else if (elem_b == MXQ_E4M3)
-    launch_gemm<kFmtE2M1, kFmtE4M3>(G, bf16, pairs, grid, s);
+    launch_gemm<kFmtE2M1, kFmtE4M3>(G, bf16, grouped, grid, s);
   else
-    launch_gemm<kFmtE2M1, kFmtE2M1>(G, bf16, pairs, grid, s);
+    launch_gemm<kFmtE2M1, kFmtE2M1>(G, bf16, grouped, grid, s);
   if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP;
   return MXQ_OK;
 }
