@@ -53,11 +53,15 @@ constexpr int kChunks = kBK / 16;   // 16-byte chunks per row and step (8-bit co
 constexpr int kFmtE4M3 = 0, kFmtE2M1 = 4;
 template <int F> constexpr int chunks_of() { return F == kFmtE2M1 ? 4 : 8; }
 
-// Chunk c of row r sits at position c ^ swz(r): conflict-free for the 8
-// consecutive rows a quarter-wave reads (rows of 128 bytes: r & 7; rows of 64
-// bytes: (r >> 1) & 3, so two rows share the 32 banks and the 8 land apart).
+// Chunk c of row r sits at position c ^ swz(r). gfx950's LDS serves a
+// 16-byte read 16 lanes at a time over 64 banks (256 bytes), so the 16
+// consecutive rows such a group reads must land on 16 distinct 16-byte bank
+// slots: rows of 128 bytes fill 2 rows per 256 bytes, and (r >> 1) & 7 sets
+// rows of equal parity apart; rows of 64 bytes fill 4, and (r >> 2) & 3 sets
+// rows of equal r % 4 apart. (The r & 7 pattern, conflict-free on a 32-bank
+// LDS, measures 4 conflict cycles per read here.)
 template <int CH> __device__ __forceinline__ int swz(int r) {
-  return CH == 8 ? (r & 7) : ((r >> 1) & 3);
+  return CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 struct GemmArgs {
