@@ -52,6 +52,11 @@ CASES = (
     # times an E2M1 weight
     ("mxfp4 mx_gemm e2m1 qkv N=6144", "mxfp4", "gemm", {"N": 6144, "elem": mxq.MXQ_E2M1}),
     ("mxfp4 mx_gemm e2m1 ffn-up N=14336", "mxfp4", "gemm", {"N": 14336, "elem": mxq.MXQ_E2M1}),
+    # reference points from the vendor library (hipBLASLt through torch._scaled_mm) at
+    # the QKV shape: a plain FP8 GEMM with one scale per tensor, and with 32-element
+    # E8M0 block scales
+    ("library fp8 per-tensor scaled_mm qkv N=6144", "llama3_8b_preattn", "libgemm", {"N": 6144, "mx": False}),
+    ("library mxfp8 block-scaled scaled_mm qkv N=6144", "llama3_8b_preattn", "libgemm", {"N": 6144, "mx": True}),
 )
 
 PEAK_MXFP8_TFLOPS = 5000.0    # MI355X dense FP8 / MXFP8 matrix peak
@@ -113,9 +118,43 @@ def run_gemm(torch, name, wl, opt, steps, warmup):
     torch.cuda.empty_cache()
 
 
+def run_libgemm(torch, name, wl, opt, steps, warmup):
+    w = workloads.WORKLOADS[wl]
+    M, K, N = w.T, w.D, opt["N"]
+    g = torch.Generator().manual_seed(12)
+    a = (torch.randn(M, K, generator=g) * 0.5).to(torch.float8_e4m3fn).to("cuda")
+    b = (torch.randn(N, K, generator=g) * 0.5).to(torch.float8_e4m3fn).to("cuda")
+    if opt["mx"]:
+        sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+        sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+    else:
+        sa = sb = torch.tensor(1.0, device="cuda")
+    try:
+        f = lambda: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError) as e:
+        print(f"{name:44s} not available in this torch build: {str(e)[:120]}", flush=True)
+        return
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        f()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    print(f"{name:44s} M={M:6d} N={N:6d} K={K:5d} {us:9.2f} us/launch (events, back-to-back)  "
+          f"{tflops:8.1f} TFLOP/s  {100 * tflops / PEAK_MXFP8_TFLOPS:5.1f}% of MXFP8 peak", flush=True)
+
+
 def run_case(torch, name, wl, op, opt, steps, warmup):
     if op == "gemm":
         return run_gemm(torch, name, wl, opt, steps, warmup)
+    if op == "libgemm":
+        return run_libgemm(torch, name, wl, opt, steps, warmup)
     w = workloads.WORKLOADS[wl]
     x0, g = workloads.make_inputs(wl, device="cuda")
     T, D = x0.shape
