@@ -78,9 +78,11 @@ struct GemmArgs {
 
 // One K step of both operands in LDS. Code rows hold 8 (E4M3) or 4 (E2M1)
 // chunks of 16 bytes, swizzled as swz above.
-// The scale words (the step's 4 E8M0 bytes of a row) are stored in the order
-// the MFMA lanes consume them: position h * 128 + rl * 4 + blk holds row
-// h * 128 + blk * 32 + rl, so a lane's 4 words are contiguous.
+// sa / sb serve the loop that loads scales step by step (the grouped loop
+// reads ScaleGroup below): the step's scale words (its 4 E8M0 bytes of a
+// row), stored in the order the MFMA lanes consume them: position
+// h * 128 + rl * 4 + blk holds row h * 128 + blk * 32 + rl, so a lane's 4
+// words are contiguous.
 struct Stage {
   uint4 a[kBM * kChunks];
   uint4 b[kBN * kChunks];
