@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+        print("bench.py measures one GPU: the hot path runs on a single MI355X "
               "(rows shard over GPUs with no exchange); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
