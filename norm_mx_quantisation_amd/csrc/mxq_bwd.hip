@@ -202,66 +202,64 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
   }
 }
 
-// out[s][d] = sum of in[r][d] over the rows r of segment s ([s * seg,
-// s * seg + seg) clipped to rows). A workgroup covers 64 float4 columns of one
-// segment; wave w adds rows [w * q, w * q + q) of the segment in row order
-// (q = ceil(seg / 4); loads batched 8 deep), and the four wave sums combine as
-// (w0 + w1) + (w2 + w3). With rows == 0 it writes zeros.
-__global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int rows, int D4, int seg,
+// dgamma[d] = sum of in[r][d] over the rows r < rows (rows <= kBwdMaxGroups;
+// rows == 0 writes zeros and reads nothing). A workgroup covers 4 float4
+// columns. Wave w adds rows [w q, w q + q) (q = ceil(rows / 4)): lane l takes
+// float4 column l % 4 of rows w q + l / 4 + 16 k, k = 0..7, in that order,
+// so that one load instruction reads 16 rows of 64 contiguous bytes and the
+// eight loads go out together (one memory round trip). The 16 lanes of a
+// column then combine by a butterfly over lane bits 2..5 (every lane ends
+// with the same sum), and the four wave sums as (w0 + w1) + (w2 + w3).
+__global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int rows, int D4,
                                                            float* out) {
-  __shared__ float4 part[3][kWave];
+  __shared__ float4 part[3][4];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int q = blockIdx.x * kWave + lane;
-  const int qc = min(q, D4 - 1);  // lanes past the last column stay in bounds, store nothing
-  const int per = (seg + 3) / 4;
-  const int r0 = blockIdx.y * seg + wave * per;
-  const int r1 = min(min(rows, blockIdx.y * seg + seg), r0 + per);
-  const float4* src = reinterpret_cast<const float4*>(in);
+  const int c = lane & 3, rs = lane >> 2;
+  const int q = blockIdx.x * 4 + c;  // float4 column, < D4 (D4 % 4 == 0)
   float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  int r = r0;
-  for (; r + 8 <= r1; r += 8) {  // 8 loads in flight, then added in row order
+  if (rows > 0) {
+    const int per = (rows + 3) / 4;
+    const int r0 = wave * per;
+    const int r1 = min(rows, r0 + per);
+    const float4* src = reinterpret_cast<const float4*>(in);
     float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(r + u) * D4 + qc];
+    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(r0 + rs + 16 * k, rows - 1) * D4 + q];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
-    }
-  }
-  {  // the last < 8 rows: every load in flight first, then the adds in row order
-    const int n = r1 - r;
-    float4 v[7];
-#pragma unroll
-    for (int u = 0; u < 7; ++u)
-      if (u < n) v[u] = src[(size_t)(r + u) * D4 + qc];
-#pragma unroll
-    for (int u = 0; u < 7; ++u)
-      if (u < n) {
-        a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+    for (int k = 0; k < 8; ++k)
+      if (r0 + rs + 16 * k < r1) {
+        a.x += v[k].x; a.y += v[k].y; a.z += v[k].z; a.w += v[k].w;
       }
   }
-  if (wave > 0) part[wave - 1][lane] = a;
+#pragma unroll
+  for (int m = 4; m < kWave; m <<= 1) {
+    a.x += __shfl_xor(a.x, m);
+    a.y += __shfl_xor(a.y, m);
+    a.z += __shfl_xor(a.z, m);
+    a.w += __shfl_xor(a.w, m);
+  }
+  if (wave > 0 && rs == 0) part[wave - 1][c] = a;
   __syncthreads();
-  if (wave == 0 && q < D4) {
-    const float4 b = part[0][lane], c = part[1][lane], d = part[2][lane];
+  if (wave == 0 && rs == 0) {
+    const float4 b = part[0][c], d = part[1][c], e = part[2][c];
     float4 o;
-    o.x = (a.x + b.x) + (c.x + d.x);
-    o.y = (a.y + b.y) + (c.y + d.y);
-    o.z = (a.z + b.z) + (c.z + d.z);
-    o.w = (a.w + b.w) + (c.w + d.w);
-    reinterpret_cast<float4*>(out)[(size_t)blockIdx.y * D4 + q] = o;
+    o.x = (a.x + b.x) + (d.x + e.x);
+    o.y = (a.y + b.y) + (d.y + e.y);
+    o.z = (a.z + b.z) + (d.z + e.z);
+    o.w = (a.w + b.w) + (d.w + e.w);
+    reinterpret_cast<float4*>(out)[q] = o;
   }
 }
 
 // Backward launch geometry: rows per workgroup, a multiple of 4, so that at
-// most kBwdMaxGroups partial rows are written; the partials are then summed
-// in segments of kBwdSegment rows, then the segments.
+// most kBwdMaxGroups partial rows are written; one column-sum launch then
+// adds them (each wave of it covers at most 128 rows: 16 per load, 8 loads).
 constexpr int64_t kBwdMaxGroups = 512;
-constexpr int kBwdSegment = 16;
+static_assert(kBwdMaxGroups <= 4 * 16 * 8, "the column sum reads at most 512 rows");
 
 struct BwdPlan {
-  int64_t rows_per_group, groups, segments;
+  int64_t rows_per_group, groups;
   size_t workspace_bytes;
 };
 
@@ -272,8 +270,7 @@ BwdPlan bwd_plan(int64_t T, int64_t D, bool dgamma = true) {
   r = ((r + kRowsPerBlock - 1) / kRowsPerBlock) * kRowsPerBlock;
   p.rows_per_group = r < kRowsPerBlock ? kRowsPerBlock : r;
   p.groups = (T + p.rows_per_group - 1) / p.rows_per_group;
-  p.segments = (p.groups + kBwdSegment - 1) / kBwdSegment;
-  p.workspace_bytes = (size_t)(p.groups + p.segments) * (size_t)D * sizeof(float);
+  p.workspace_bytes = (size_t)p.groups * (size_t)D * sizeof(float);
   return p;
 }
 
@@ -300,11 +297,9 @@ mxq_status dispatch_bwd(const BwdArgs& A, int nc, unsigned groups, hipStream_t s
   }
 }
 
-mxq_status launch_col_sum(const float* in, int rows, int D, int seg, int nseg, float* out,
-                          hipStream_t s) {
-  const int D4 = D / 4;
-  hipLaunchKernelGGL(col_sum_kernel, dim3((D4 + kWave - 1) / kWave, nseg), dim3(kThreads), 0, s,
-                     in, rows, D4, seg, out);
+mxq_status launch_col_sum(const float* in, int rows, int D, float* out, hipStream_t s) {
+  const int D4 = D / 4;  // a multiple of 8 (D % 32 == 0)
+  hipLaunchKernelGGL(col_sum_kernel, dim3(D4 / 4), dim3(kThreads), 0, s, in, rows, D4, out);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
@@ -334,7 +329,7 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     // nothing to read; the gain's gradient of an empty batch is zero
-    return dgamma ? launch_col_sum(nullptr, 0, (int)D, 1, 1, dgamma, s) : MXQ_OK;
+    return dgamma ? launch_col_sum(nullptr, 0, (int)D, dgamma, s) : MXQ_OK;
   }
   if (x == nullptr || dy == nullptr || inv_norm == nullptr || dx == nullptr) return MXQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || ldx % 8 != 0 || lddy % 8 != 0)
@@ -365,11 +360,8 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
   else
     st = g ? dispatch_bwd<true, false>(A, nc, groups, s) : dispatch_bwd<false, false>(A, nc, groups, s);
   if (st != MXQ_OK || dgamma == nullptr) return st;
-  // partials [groups][D] -> segment sums [segments][D] -> dgamma [D]
-  float* seg = static_cast<float*>(workspace) + (size_t)plan.groups * (size_t)D;
-  st = launch_col_sum(A.partial, (int)plan.groups, (int)D, kBwdSegment, (int)plan.segments, seg, s);
-  if (st != MXQ_OK) return st;
-  return launch_col_sum(seg, (int)plan.segments, (int)D, (int)plan.segments, 1, dgamma, s);
+  // partials [groups][D] -> dgamma [D]
+  return launch_col_sum(A.partial, (int)plan.groups, (int)D, dgamma, s);
 }
 
 }  // extern "C"

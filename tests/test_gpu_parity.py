@@ -366,10 +366,12 @@ def check_backward(x, g, dy, inv, what="", dgamma=True):
     assert (np.abs(got - ref) <= 2 * ulp + bound).all(), what
     if dgamma:
         dg64, absum = oracle.mxnorm_bwd_dgamma(xs, dys, iv)
-        # per column: each term rounds twice, each wave adds its rows in order,
-        # then 2 combine levels, then up to 16 + 32 sequential partial sums
+        # per column: each term rounds twice; in the main kernel each wave adds
+        # its rows in order and the 4 wave sums combine in 2 levels; the column
+        # sum then adds up to 8 partial rows per lane in order, a 4-level
+        # butterfly and 2 levels over its waves
         per_wave = -(-T // 4)
-        n = min(per_wave, 64) + 2 + 16 + 32 + 2
+        n = min(per_wave, 64) + 2 + 8 + 4 + 2 + 2
         assert (np.abs(np_(dg) - dg64) <= n * U24 * absum + 1e-30).all(), what
     return dx, row_dot, dg
 
