@@ -274,6 +274,22 @@ def test_two_pass_formats(elem, rnd):
                    what=f"two-pass {elem} {rnd}")
 
 
+@pytest.mark.parametrize("D", [mxq.MXQ_MAX_D, mxq.MXQ_MAX_D - 32])
+def test_widest_rows(D):
+    # the largest rows the C ABI accepts: the LDS-staged kernels with one row
+    # (and its bf16 gains) filling most of a workgroup's LDS; D - 32 leaves a
+    # ragged last chunk
+    x = workloads.random_rows(5, D, seed=97 + D, device=DEV)
+    x[3, :64] *= 30.0
+    g = workloads.random_gamma(D, seed=98, device=DEV)
+    check_mxnorm(x, g, 2.0, what=f"widest D={D}")
+    check_mxnorm(x, None, math.inf, what=f"widest D={D} p=inf no gamma")
+    check_mxnorm(x, g, 2.0, "e2m1", "sr", what=f"widest D={D} e2m1 sr")
+    check_rms_fused(x, g, what=f"widest D={D} rms-fused")
+    check_two_pass(x, g, what=f"widest D={D} two-pass")
+    check_mxcast(x, "e4m3", "sr", what=f"widest D={D} mxcast sr")
+
+
 # ---------------------------------------------------------------- single-pass exact-RMS comparator
 
 @pytest.mark.parametrize("D", [32, 96, 4096, 8192, 8224, 14336])
