@@ -6,9 +6,10 @@
 // next linear layer's weight [N, K], gain folded and MX-cast along K (§2.3,
 // MXNormLinear). The products run on the gfx950 block-scaled matrix cores
 // (v_mfma_scale_f32_32x32x64_f8f6f4), which apply both operands' E8M0 scales
-// and accumulate in fp32. (Its 16 x 16 x 128 sibling measures at less than
-// half its rate with 8-bit operands on MI355X, the 32 x 32 x 64 form near the
-// 5 PFLOP/s MXFP8 peak.)
+// and accumulate in fp32. (With register operands it and its 16 x 16 x 128
+// sibling both issue at about 4.5 PFLOP/s with 8-bit operands; the 32 x 32 x
+// 64 form needs a quarter of the accumulators and half the instructions and
+// scale operands for a 128 x 128 wave tile.)
 //
 // Either operand may be E2M1 (FP4, packed two to a byte, element 2j in the
 // low nibble): the same instruction with format code 4 runs FP4 operands at
