@@ -40,6 +40,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
@@ -74,7 +75,8 @@ struct GemmArgs {
   int64_t lda, ldsa, ldb, ldsb, ldc;  // code bytes, scale bytes, C elements per row
   int M, N, K;
   int tiles_m, tiles_n;
-  int vec;  // C rows allow 4-element vector stores (aligned base, ldc % 4 == 0)
+  int vec;    // C rows allow 4-element vector stores (aligned base, ldc % 4 == 0)
+  int vec16;  // bf16 C rows allow 16-byte stores (16-byte aligned base, ldc % 8 == 0)
 };
 
 // One K step of both operands in LDS. Code rows hold 8 (E4M3) or 4 (E2M1)
@@ -357,6 +359,53 @@ __device__ __forceinline__ void store_tile(const GemmArgs& G, int m0, int n0, in
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 }
 
+// Epilogue of a whole bf16 tile through LDS. Stored straight from the
+// accumulators, each store instruction writes 8 bytes to each of 32 rows, so
+// every 128-byte line of C is assembled from 8 partial writes. Instead each
+// wave writes its 128 x 128 quarter, 64 rows at a time, into its own 16 KB
+// slot of a stage no wave reads any more (256 bytes per row; 16-byte group c
+// of slot row r at c ^ (r & 15), so the 16 rows a write instruction touches
+// land on distinct banks), then reads it back 16 contiguous bytes per lane
+// and stores whole lines: 4 rows of 256 bytes per instruction, non-temporal
+// (C is written once; streaming it keeps the operand panels in L2). A wave
+// reads back only what it wrote, and its LDS accesses complete in order.
+__device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& G, int m0, int n0, int wm,
+                                                    int wn, int wave, int lane, v16f (&acc)[4][4],
+                                                    uint4* stage) {
+  uint8_t* slot = reinterpret_cast<uint8_t*>(stage) + wave * 16384;
+  const int g = lane >> 5, rl = lane & 31;
+  uint16_t* C = static_cast<uint16_t*>(G.c);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int r = ii * 32 + rl;  // slot row; quarter row 64 h + r
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v16f& a = acc[2 * h + ii][j];
+          const u32x2 w = {(uint32_t)bf16_rne(a[4 * q]) | ((uint32_t)bf16_rne(a[4 * q + 1]) << 16),
+                           (uint32_t)bf16_rne(a[4 * q + 2]) | ((uint32_t)bf16_rne(a[4 * q + 3]) << 16)};
+          // columns j * 32 + 8 q + 4 g .. + 3: 16-byte group 4 j + q, half g
+          *reinterpret_cast<u32x2*>(slot + r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + g * 8) = w;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 4 * k + (lane >> 4), c16 = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(slot + r * 256 + ((c16 ^ (r & 15)) << 4));
+      const int64_t row = m0 + wm * 128 + h * 64 + r;
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<u32x4*>(C + row * G.ldc + n0 + wn * 128 + c16 * 8));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+}
+
 // Tile order: the 8 XCDs take workgroup ids round robin, so tile t is first
 // mapped to slot (t % 8) * (n / 8) + t / 8, giving each XCD (and its L2) a
 // contiguous run of the sequence (tiles b + j G stay on b's XCD); the
@@ -450,7 +499,17 @@ void mx_gemm_kernel(GemmArgs G) {
                               wave, lane, wm, wn, acc, nullptr, 0, nullptr, 0, 0, 0);
       }
     }
-    store_tile<OUT_BF16>(G, m0, n0, wm, wn, lane, acc);
+    if (GROUPED && OUT_BF16 && G.vec16 && m0 + kBM <= G.M && n0 + kBN <= G.N) {
+      // the tile's last step read S1 (the next tile's first DMA fills S0):
+      // once every wave's reads of it are complete, S1 stages the epilogue;
+      // the next tile's first wait and barrier order its refill after
+      // every wave's epilogue reads (s_waitcnt lgkmcnt(0) alone: 0xC07F)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      store_tile_bf16_lds(G, m0, n0, wm, wn, wave, lane, acc, S1.a);
+    } else {
+      store_tile<OUT_BF16>(G, m0, n0, wm, wn, lane, acc);
+    }
     m0 = nm0;
     n0 = nn0;
   }
@@ -529,6 +588,7 @@ extern "C" mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_sc
   G.tiles_m = (int)((M + kBM - 1) / kBM);
   G.tiles_n = (int)((N + kBN - 1) / kBN);
   G.vec = (ldc % 4 == 0) && aligned(c, c_type == MXQ_OUT_BF16 ? 8 : 16);
+  G.vec16 = c_type == MXQ_OUT_BF16 && ldc % 8 == 0 && aligned(c, 16);
   // persistent grid: one workgroup per CU, a multiple of 8 (one per XCD
   // round-robin slot), at most one per tile
   const int nb = G.tiles_m * G.tiles_n;
