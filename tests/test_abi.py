@@ -281,3 +281,13 @@ def test_gemm_argument_errors():
     assert gemm(ldsa=130) == mxq.MXQ_ERR_ALIGN
     assert gemm(c=A16 + 2) == mxq.MXQ_ERR_ALIGN            # fp32 output needs 4-byte alignment
     assert gemm(M=0, a=None, sa=None, b=None, sb=None, c=None) == mxq.MXQ_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU fallback: without the built library every call raises
+    monkeypatch.setattr(mxq, "_lib", None)
+    monkeypatch.setattr(mxq, "LIB_PATH", str(tmp_path / "libmxq.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mxq.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        mxq.mxq_abi_version()
