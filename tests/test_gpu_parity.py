@@ -528,6 +528,24 @@ def test_gemm_bf16_output_and_strided():
     assert torch.equal(c2, c32)
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1")])
+def test_gemm_bf16_into_strided_output(fa, fb):
+    # whole 256 x 256 tiles of a bf16 result go out through LDS as whole rows
+    # when C's row stride allows 16-byte stores (here 520 elements), directly
+    # otherwise (518); both must equal the contiguous result and leave the
+    # padding columns alone
+    M, N, K = 512, 512, 1024
+    A, SA = random_mx_operand(M, K, 519, fmt=fa)
+    B, SB = random_mx_operand(N, K, 520, fmt=fb)
+    ref, _ = check_gemm(A, SA, B, SB, torch.bfloat16, what=f"gemm {fa} bf16", fa=fa, fb=fb)
+    for ld in (520, 518):
+        wide = torch.full((M, ld), 7.0, dtype=torch.bfloat16, device=DEV)
+        mxq.mx_matmul(A, SA, B, SB, out=wide[:, :N], fmt_a=fa, fmt_b=fb)
+        torch.cuda.synchronize()
+        assert torch.equal(wide[:, :N], ref), ld
+        assert (wide[:, N:] == 7.0).all(), ld
+
+
 def test_gemm_nonfinite_operands():
     A, SA = random_mx_operand(256, 256, 506)
     B, SB = random_mx_operand(256, 256, 507)
