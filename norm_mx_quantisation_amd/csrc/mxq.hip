@@ -122,19 +122,31 @@ __device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, LaneMa
 // into the exponent field in exactly those cases (a finite a stays below
 // 0x7F800000 + 0x7FFFFF, so the carry never reaches the sign). adj is 0 for
 // the floor rule and scale_adjust<ELEM>() for the round-up rule. The code is
-// s + 127 clamped at 0; NaN / Inf give 0xFF. a >= 0 here.
+// s + 127 clamped at 0; NaN / Inf give 0xFF.
 template <int ELEM>
 __host__ __device__ constexpr uint32_t scale_adjust() {
   return 0x7FFFFFu - ((ELEM == MXQ_E4M3) ? 0x600000u : 0x400000u);
 }
 
+// A block's E8M0 byte (the low byte of code), and whether the block holds NaN
+// or Inf (then code is all ones, so the byte is 0xFF, and every element of
+// the block is encoded as NaN).
+struct BlockScale {
+  uint32_t code;
+  bool bad;
+};
+
+// a is the block's absolute maximum: +0 or more, or NaN (a NaN with its sign
+// bit set also counts as bad). Taking emax (and the round-up adjustment) off
+// the bits in one clamped unsigned subtract, ahead of the shift, gives the
+// biased exponent less emax, saturated at 0.
 template <int ELEM>
-__device__ __forceinline__ uint32_t e8m0_code(float amax, uint32_t adj) {
-  constexpr int kEmax = (ELEM == MXQ_E4M3) ? 8 : 2;
-  const uint32_t b = __float_as_uint(amax) & 0x7FFFFFFFu;
-  if (b >= 0x7F800000u) return 0xFFu;
-  const uint32_t e = (b + adj) >> 23;
-  return e > (uint32_t)kEmax ? e - kEmax : 0u;
+__device__ __forceinline__ BlockScale e8m0_scale(float amax, uint32_t adj) {
+  constexpr uint32_t kEmax = (ELEM == MXQ_E4M3) ? 8u : 2u;
+  const uint32_t b = __float_as_uint(amax);
+  const bool bad = b >= 0x7F800000u;
+  const uint32_t code = __builtin_elementwise_sub_sat(b, (kEmax << 23) - adj) >> 23;
+  return {bad ? ~0u : code, bad};  // all ones is an inline constant: no literal move
 }
 
 // ------------------------------------------------------------------ Philox
@@ -179,12 +191,12 @@ struct SrStream {
 // ------------------------------------------------------------------ encode
 
 // 8 values y (not yet divided by the scale) -> 8 E4M3 codes, RNE, saturating.
-// A non-finite block (code 0xFF) is encoded with a harmless stand-in scale
-// and then replaced by NaN codes with a select, so the common path has no
-// branch.
-__device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], uint32_t code_in) {
-  const bool bad = code_in == 0xFFu;
-  const uint32_t code = bad ? 127u : code_in;
+// A non-finite block is encoded like any other (its scale and limit are then
+// meaningless values that fault nothing) and its codes are replaced by NaN
+// with a select, so the common path has no branch.
+__device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], BlockScale s) {
+  const uint32_t code = s.code;
+  const bool bad = s.bad;
   const float scale = __uint_as_float(code << 23);                  // 2^(code-127)
   const float lim = __uint_as_float(((code + 8u) << 23) | 0x00600000u); // 448 * 2^(code-127)
   float w[8];
@@ -202,10 +214,9 @@ __device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], uint32_t cod
 }
 
 // 8 values -> 8 E2M1 codes packed in one word (element 2j in the low nibble).
-__device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], uint32_t code_in) {
-  const bool bad = code_in == 0xFFu;  // as for E4M3: select, no branch
-  const uint32_t code = bad ? 127u : code_in;
-  const float scale = __uint_as_float(code << 23);
+__device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], BlockScale s) {
+  const bool bad = s.bad;  // as for E4M3: select, no branch
+  const float scale = __uint_as_float(s.code << 23);
   uint32_t q = __float_as_uint(y[0]);  // all four bytes are written below
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[0], y[1], scale, 0);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[2], y[3], scale, 1);
@@ -242,9 +253,9 @@ __device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
   return code | ((u >> 31) << kSignBit);
 }
 
-__device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], uint32_t code, const uint32_t r[8]) {
-  if (code == 0xFFu) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  const float inv_scale = __uint_as_float((254u - code) << 23);  // 2^-(code-127), a normal float
+__device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
+  if (s.bad) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const float inv_scale = __uint_as_float((254u - s.code) << 23);  // 2^-(code-127), a normal float
   uint32_t c[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) c[j] = sr_code<MXQ_E4M3>(y[j] * inv_scale, r[j]);
@@ -252,9 +263,9 @@ __device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], uint32_t code
                     c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
 }
 
-__device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], uint32_t code, const uint32_t r[8]) {
-  if (code == 0xFFu) return 0x77777777u;
-  const float inv_scale = __uint_as_float((254u - code) << 23);
+__device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
+  if (s.bad) return 0x77777777u;
+  const float inv_scale = __uint_as_float((254u - s.code) << 23);
   uint32_t q = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) q |= sr_code<MXQ_E2M1>(y[j] * inv_scale, r[j]) << (4 * j);
@@ -278,7 +289,7 @@ __device__ __forceinline__ void store4_stream(uint8_t* p, uint32_t v) {
 // element index that keys the stochastic-rounding stream.
 template <int ELEM, int RND>
 __device__ __forceinline__ void encode_store8(uint8_t* codes_row, uint32_t d, uint64_t n,
-                                              const float y[8], uint32_t code,
+                                              const float y[8], BlockScale code,
                                               const SrStream& rng) {
   if (RND == MXQ_SR) {
     uint32_t r[8];
@@ -378,6 +389,8 @@ __device__ __forceinline__ uint32_t chunk_products(const uint4& xb, const float 
 
 // Second half: y = RN(v * inv), E8M0 code from max |y| = RN(max |v| * inv)
 // (rounding is monotone), codes stored. Returns the code of the lane's block.
+// vmax_bits has its sign bit clear and inv is +0 or more, or NaN, so the
+// maximum is +0 or more, or NaN, as e8m0_scale expects.
 template <int ELEM, int RND>
 __device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* codes_row,
                                                  uint64_t nrow, uint32_t d, float v[8],
@@ -385,9 +398,9 @@ __device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* cod
   const float amax = __uint_as_float(vmax_bits) * inv;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
-  const uint32_t code = e8m0_code<ELEM>(amax, A.ceil_rule ? scale_adjust<ELEM>() : 0u);
-  encode_store8<ELEM, RND>(codes_row, d, nrow + d, v, code, A.rng);
-  return code;
+  const BlockScale s = e8m0_scale<ELEM>(amax, A.ceil_rule ? scale_adjust<ELEM>() : 0u);
+  encode_store8<ELEM, RND>(codes_row, d, nrow + d, v, s, A.rng);
+  return s.code;
 }
 
 // Both halves of the chunk at column d of row nrow / D.
@@ -405,12 +418,18 @@ __device__ __forceinline__ uint4 nan_group() {
   return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
 }
 
-// Whether any of 8 bf16 values is NaN or Inf (exponent field all ones).
+// Whether any of 8 bf16 values is NaN or Inf (exponent field all ones): the
+// exponent fields alone, as 16-bit lanes, reach their largest value 0x7F80
+// exactly then.
 __device__ __forceinline__ bool nonfinite_bf16x8(const uint4& r) {
-  auto bad = [](uint32_t w) {
-    return ((w & 0x7F80u) == 0x7F80u) || (((w >> 16) & 0x7F80u) == 0x7F80u);
-  };
-  return bad(r.x) | bad(r.y) | bad(r.z) | bad(r.w);  // no short-circuit branches
+  const uint32_t k = 0x7F807F80u;
+  const u16x2 a = __builtin_bit_cast(u16x2, r.x & k), b = __builtin_bit_cast(u16x2, r.y & k);
+  const u16x2 c = __builtin_bit_cast(u16x2, r.z & k), d = __builtin_bit_cast(u16x2, r.w & k);
+  const uint32_t m = __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                          __builtin_elementwise_max(c, d)));
+  const u16x2 h = __builtin_bit_cast(u16x2, m);
+  return __builtin_elementwise_max(h.x, h.y) == 0x7F80u;
 }
 
 // gamma [D] goes to LDS as fp32, laid out [chunk][half][lane] (float4 each),
@@ -426,23 +445,26 @@ struct GammaStage {
   uint4 r[kItems];
 
   __device__ __forceinline__ void load(const uint16_t* gamma, int D) {
+    const RangeLoader g(gamma, D);
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-      const int i = min((int)threadIdx.x + k * NT, NC * kWave - 1);
-      r[k] = load16(gamma + min(i * 8, D - 8));  // always in bounds; masked in store()
-    }
+    for (int k = 0; k < kItems; ++k) r[k] = g.load8(((int)threadIdx.x + k * NT) * 8);
   }
 
   // Writes the gains to LDS (a group of 8 holding a NaN or Inf becomes 8
-  // NaNs, see G_GAIN) and waits for the whole workgroup.
-  __device__ __forceinline__ void store(int D, float4* g_lds) {
+  // NaNs, see G_GAIN; the replacement is skipped by the whole wavefront when
+  // none of its groups needs it) and waits for the whole workgroup. Items
+  // past the row end read zeros; the chunks they belong to are never
+  // encoded, so their gains are never read.
+  __device__ __forceinline__ void store(float4* g_lds) {
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
       const int i = (int)threadIdx.x + k * NT;
       if (i < NC * kWave) {
-        const uint4 q = i * 8 < D ? r[k] : make_uint4(0, 0, 0, 0);
+        uint4 q = r[k];
+        const bool bad = nonfinite_bf16x8(q);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) q = bad ? nan_group() : q;
         float v[8];
-        unpack8(nonfinite_bf16x8(q) ? nan_group() : q, v);
+        unpack8(q, v);
         const int c = i / kWave, l = i % kWave;
         g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
         g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
@@ -501,7 +523,8 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
     if (d < A.D) {
       if (GM != G_NONE) gains(g_lds, c, lane, g);
       const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, crow, nrow, d, raw[c], g, mb[c], inv);
-      if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
+      // block d / 32 = 16 c + lane / 4: the chunk's part is an immediate offset
+      if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);
     }
   }
   flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K, A.K, A.sc_vec != 0, lane);
@@ -528,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
   __builtin_amdgcn_sched_barrier(0);
-  if (GAMMA) gs.store(A.D, g_lds);  // the row loads stay in flight meanwhile
+  if (GAMMA) gs.store(g_lds);  // the row loads stay in flight meanwhile
   if (!live) return;
   uint32_t* sc = sc_lds[wave];
   if (!GAMMA)
@@ -736,13 +759,14 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
   for (int u = 0; u < kCastChunksPerWave; ++u) {
     if (g0 + u < A.total_chunks && ds[u] < A.D) {
       const uint32_t mbits = quad_max_u32(absmax_bits8(raw[u]));
-      const uint32_t code = e8m0_code<ELEM>(__uint_as_float(mbits << 16),
+      const BlockScale s = e8m0_scale<ELEM>(__uint_as_float(mbits << 16),
                                             A.ceil_rule ? scale_adjust<ELEM>() : 0u);
+      const uint32_t code = s.code;
       float v[8];
       unpack8(raw[u], v);
       const uint64_t nrow = (uint64_t)rows[u] * (uint64_t)A.D;
       encode_store8<ELEM, RND>(code_row<ELEM>(A.codes, nrow), (uint32_t)ds[u], nrow + ds[u], v,
-                               code, A.rng);
+                               s, A.rng);
       if ((lane & 3) == 0) {
         if (A.sc_vec)
           put_scale(sc, u * 16 + (lane >> 2), code);

@@ -35,8 +35,7 @@ __device__ __forceinline__ uint32_t absmax_bits8(const uint4& r) {
   u16x2 d = __builtin_bit_cast(u16x2, r.w & k);
   u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
                                       __builtin_elementwise_max(c, d));
-  uint32_t mm = __builtin_bit_cast(uint32_t, m);
-  return max(mm & 0xFFFFu, mm >> 16);
+  return (uint32_t)__builtin_elementwise_max(m.x, m.y);  // one 16-bit max of the halves
 }
 
 // Cross-lane moves that stay in the VALU (no LDS round trip): DPP within a
@@ -139,6 +138,22 @@ __device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* xr, int c, int dl, int D) {
   return load16_stream(xr + min(c * kChunk + dl, D - 8));
 }
+
+// Loads from one wave-uniform range (gamma) through a buffer resource whose
+// size is the range's bytes: a lane's 16 bytes past the end read as zeros
+// (the resource's range check), so the loads need no clamp. Word 3 is the
+// gfx9 raw-buffer format.
+struct RangeLoader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ RangeLoader(const uint16_t* base, int elems)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, elems * 2,
+                                               0x00020000)) {}
+  // 8 elements from element e
+  __device__ __forceinline__ uint4 load8(int e) const {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, e * 2, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+};
 
 // Gains of chunk c for this lane, from the fp32 LDS copy laid out
 // [chunk][half][lane] (two conflict-free 16-byte reads).
