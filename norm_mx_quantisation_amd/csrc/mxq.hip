@@ -232,35 +232,55 @@ __device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], BlockScal
 //     and the discarded mantissa bits shifted to the top are frac32;
 //   below the smallest normal the quantum is fixed (2^-9, E2M1 2^-1): q = |v| /
 //     quantum is exact, n = trunc(q), and (q - n) * 2^32 is exact as well.
+//   The magnitude goes through abs source modifiers and a bit-field extract
+//   (no masking instruction); q - n is the hardware fraction of q (exact for
+//   q >= 0). The sign is left to the caller.
 template <int ELEM>
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
+__device__ __forceinline__ uint32_t sr_mag_code(float v, uint32_t r) {
   constexpr int kSh = (ELEM == MXQ_E4M3) ? 20 : 22;                // fp32 mantissa bits dropped
   constexpr uint32_t kBias = (ELEM == MXQ_E4M3) ? 960u : 252u;     // (120 << 3), (126 << 1)
-  constexpr uint32_t kMinNormal = (ELEM == MXQ_E4M3) ? 0x3C800000u : 0x3F800000u;  // 2^-6, 1
+  constexpr float kMinNormal = (ELEM == MXQ_E4M3) ? 0x1p-6f : 1.0f;
   constexpr float kInvQuantum = (ELEM == MXQ_E4M3) ? 512.0f : 2.0f;
   constexpr uint32_t kMaxCode = (ELEM == MXQ_E4M3) ? 0x7Eu : 0x7u;
-  constexpr int kSignBit = (ELEM == MXQ_E4M3) ? 7 : 3;
   const uint32_t u = __float_as_uint(v);
-  const uint32_t a = u & 0x7FFFFFFFu;
   // both forms, then a select per lane (no divergent branch); q < 2^18 always
-  const float q = __uint_as_float(a) * kInvQuantum;
+  const float q = fabsf(v) * kInvQuantum;
   const uint32_t n_sub = (uint32_t)q;
-  const uint32_t f_sub = (uint32_t)((q - (float)n_sub) * 4294967296.0f);
-  const bool normal = a >= kMinNormal;
-  uint32_t code = normal ? (a >> kSh) - kBias : n_sub;
-  const uint32_t frac = normal ? a << (32 - kSh) : f_sub;
-  code = min(code + (r < frac ? 1u : 0u), kMaxCode);
-  return code | ((u >> 31) << kSignBit);
+  const uint32_t f_sub = (uint32_t)(__builtin_amdgcn_fractf(q) * 4294967296.0f);
+  const bool normal = fabsf(v) >= kMinNormal;
+  const uint32_t code = normal ? __builtin_amdgcn_ubfe(u, kSh, 31 - kSh) - kBias : n_sub;
+  const uint32_t frac = normal ? u << (32 - kSh) : f_sub;  // the sign bit shifts out
+  return min(code + (r < frac ? 1u : 0u), kMaxCode);
+}
+
+template <int ELEM>
+__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
+  constexpr int kSignBit = (ELEM == MXQ_E4M3) ? 7 : 3;
+  return sr_mag_code<ELEM>(v, r) | ((__float_as_uint(v) >> 31) << kSignBit);
+}
+
+// Sign bits of four values as bit 7 of four bytes: byte permutes gather each
+// value's top byte, then one and-or merges them into the packed magnitudes
+// (whose bit 7 is clear).
+__device__ __forceinline__ uint32_t with_signs4(uint32_t mags, float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0C0C0703u);
+  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07030C0Cu);
+  const uint32_t top = __builtin_amdgcn_perm(hi, lo, 0x07060100u);
+  return (top & 0x80808080u) | mags;
 }
 
 __device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
   if (s.bad) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   const float inv_scale = __uint_as_float((254u - s.code) << 23);  // 2^-(code-127), a normal float
   uint32_t c[8];
+  float w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) c[j] = sr_code<MXQ_E4M3>(y[j] * inv_scale, r[j]);
-  return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                    c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+  for (int j = 0; j < 8; ++j) {
+    w[j] = y[j] * inv_scale;
+    c[j] = sr_mag_code<MXQ_E4M3>(w[j], r[j]);
+  }
+  return make_uint2(with_signs4(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, w[0], w[1], w[2], w[3]),
+                    with_signs4(c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24, w[4], w[5], w[6], w[7]));
 }
 
 __device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
