@@ -44,7 +44,8 @@ struct BwdArgs {
 // sums are combined as (w0 + w2) + (w1 + w3) through LDS into the group's
 // partial row. KEEP holds the row's x and dy in registers between the two
 // passes (D <= 4096); otherwise the second pass loads them again (from L2).
-template <int NC, bool GAMMA, bool DGAMMA, bool KEEP>
+// NT: dx leaves through non-temporal stores.
+template <int NC, bool GAMMA, bool DGAMMA, bool KEEP, bool NT>
 __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
   __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
   __shared__ float red[DGAMMA ? 2 * NC * 8 * kWave : 1];
@@ -54,13 +55,48 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
   const int64_t row0 = (int64_t)blockIdx.x * A.rows_per_group;
   const int64_t row_end = min(A.T, row0 + A.rows_per_group);
 
+  // Gains and the wave's first row go out before the gains are staged to
+  // LDS: gains first (loads retire in order, so staging waits for them
+  // alone), then the row, whose loads stay in flight across the staging and
+  // its barrier. Item i of the gains is chunk i / 64, lane i % 64; a load past
+  // the row end is clamped in bounds and its item never read.
+  constexpr int kGItems = (NC * kWave + kThreads - 1) / kThreads;
+  uint4 gr[GAMMA ? kGItems : 1];
   if (GAMMA) {
-    for (int i = threadIdx.x; i < NC * kWave; i += kThreads) {
-      float v[8];
-      unpack8(i * 8 < A.D ? load16(A.gamma + i * 8) : make_uint4(0, 0, 0, 0), v);
-      const int c = i / kWave, l = i % kWave;
-      g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
-      g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+    for (int k = 0; k < kGItems; ++k) {
+      const int i = min((int)threadIdx.x + k * kThreads, NC * kWave - 1);
+      gr[k] = load16(A.gamma + min(i * 8, A.D - 8));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // KEEP: the row's packed x and dy in registers. The next row goes into
+  // xn / dn: the first one here, later ones (with dgamma a wave walks
+  // several rows) while the current row is processed; without dgamma each
+  // wave has one row.
+  constexpr bool PREFETCH = KEEP && DGAMMA;
+  uint4 xk[KEEP ? NC : 1], dk[KEEP ? NC : 1], xn[KEEP ? NC : 1], dn[KEEP ? NC : 1];
+  if (KEEP && row0 + wave < row_end) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      xn[c] = load_chunk(A.x + (row0 + wave) * A.ldx, c, dl, A.D);
+      dn[c] = load_chunk(A.dy + (row0 + wave) * A.lddy, c, dl, A.D);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (GAMMA) {
+#pragma unroll
+    for (int k = 0; k < kGItems; ++k) {
+      const int i = (int)threadIdx.x + k * kThreads;
+      if (i < NC * kWave) {
+        float v[8];
+        unpack8(gr[k], v);
+        const int c = i / kWave, l = i % kWave;
+        g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
+        g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
+      }
     }
     __syncthreads();
   }
@@ -73,38 +109,19 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
       for (int j = 0; j < 8; ++j) acc[c][j] = 0.0f;
   }
 
-  // KEEP: the row's packed x and dy in registers. With dgamma a wave walks
-  // several rows, and its next row is prefetched into xn / dn while this one
-  // is processed; without, each wave has one row.
-  constexpr bool PREFETCH = KEEP && DGAMMA;
-  uint4 xk[KEEP ? NC : 1], dk[KEEP ? NC : 1], xn[PREFETCH ? NC : 1], dn[PREFETCH ? NC : 1];
-  if (PREFETCH && row0 + wave < row_end) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      xn[c] = load_chunk(A.x + (row0 + wave) * A.ldx, c, dl, A.D);
-      dn[c] = load_chunk(A.dy + (row0 + wave) * A.lddy, c, dl, A.D);
-    }
-  }
   for (int64_t row = row0 + wave; row < row_end; row += kRowsPerBlock) {
     const uint16_t* xr = A.x + row * A.ldx;
     const uint16_t* dr = A.dy + row * A.lddy;
     float s = 0.0f;
     float g[8] = {1, 1, 1, 1, 1, 1, 1, 1};
-    if (KEEP && !PREFETCH) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        xk[c] = load_chunk(xr, c, dl, A.D);
-        dk[c] = load_chunk(dr, c, dl, A.D);
-      }
-    }
-    if (PREFETCH) {
+    const int64_t next = row + kRowsPerBlock;
+    if (KEEP) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         xk[c] = xn[c];
         dk[c] = dn[c];
       }
-      const int64_t next = row + kRowsPerBlock;
-      if (next < row_end) {
+      if (PREFETCH && next < row_end) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           xn[c] = load_chunk(A.x + next * A.ldx, c, dl, A.D);
@@ -147,16 +164,26 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
         if (GAMMA) gains(g_lds, c, lane, g);
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[j] = a * (g[j] * dv[j]) - cf * xv[j];
-        uint4 w;
-        w.x = pack_bf16x2(o[0], o[1]);
-        w.y = pack_bf16x2(o[2], o[3]);
-        w.z = pack_bf16x2(o[4], o[5]);
-        w.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4*>(A.dx + (uint64_t)row * (uint64_t)A.D + (uint64_t)d) = w;
+        const u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                         pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+        u32x4* dst = reinterpret_cast<u32x4*>(A.dx + (uint64_t)row * (uint64_t)A.D + (uint64_t)d);
+        if constexpr (NT)
+          __builtin_nontemporal_store(w, dst);
+        else
+          *dst = w;
         if (DGAMMA) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[c][j] += (dv[j] * xv[j]) * a;
         }
+      }
+    }
+    // a wave with several rows and no prefetch loads its next row once this
+    // one is done with (the current plan gives such waves a single row)
+    if (KEEP && !PREFETCH && next < row_end) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        xn[c] = load_chunk(A.x + next * A.ldx, c, dl, A.D);
+        dn[c] = load_chunk(A.dy + next * A.lddy, c, dl, A.D);
       }
     }
   }
@@ -274,10 +301,20 @@ BwdPlan bwd_plan(int64_t T, int64_t D, bool dgamma = true) {
   return p;
 }
 
+// Non-temporal dx stores measured faster without dgamma (34.6 against
+// 34.8 us on [8192, 4096], 128 against 136 us on [32768, 4096]) and with it at
+// 64 rows per workgroup ([32768, 4096]: 157 against 163 us), but slower at 16
+// rows per workgroup ([8192, 4096]: 45.7 against 43.4 us); the dgamma kernel
+// takes them from 32 rows per workgroup on.
 template <int NC, bool GAMMA, bool DGAMMA>
 mxq_status launch_bwd(const BwdArgs& A, unsigned groups, hipStream_t s) {
-  hipLaunchKernelGGL((mxnorm_bwd_kernel<NC, GAMMA, DGAMMA, (NC <= 8)>), dim3(groups), dim3(kThreads), 0,
-                     s, A);
+  constexpr bool kKeep = NC <= 8;
+  if (!DGAMMA || A.rows_per_group >= 32)
+    hipLaunchKernelGGL((mxnorm_bwd_kernel<NC, GAMMA, DGAMMA, kKeep, true>), dim3(groups),
+                       dim3(kThreads), 0, s, A);
+  else
+    hipLaunchKernelGGL((mxnorm_bwd_kernel<NC, GAMMA, true, kKeep, false>), dim3(groups),
+                       dim3(kThreads), 0, s, A);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
