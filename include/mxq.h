@@ -78,7 +78,7 @@ typedef enum {
   MXQ_ERR_SHAPE = 2,       /* T < 0, D <= 0, D % 32 != 0, or ldx < D             */
   MXQ_ERR_ALIGN = 3,       /* a pointer or ldx breaks the alignment rules above  */
   MXQ_ERR_ARG = 4,         /* bad p / eps / element / rounding / flags / rng     */
-  MXQ_ERR_UNSUPPORTED = 5, /* D beyond the largest row the kernels hold         */
+  MXQ_ERR_UNSUPPORTED = 5, /* a size beyond what the kernels take (see each call) */
   MXQ_ERR_HIP = 6          /* the HIP runtime refused the launch                 */
 } mxq_status;
 
@@ -120,7 +120,8 @@ enum {
  *            bit-identical results), optionally or-ed with MXQ_FLAG_SCALE_CEIL.
  *   codes, scales  outputs; inv_norm [T] fp32 output, may be NULL.
  * Errors: NULL (x, codes, scales), SHAPE, ALIGN, ARG (p <= 0 or NaN, unknown
- * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large), HIP.
+ * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large for the path,
+ * T * D >= 2^40, or more than 2^31 - 1 workgroups of rows), HIP.
  */
 mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
                       int64_t D, float p, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
@@ -133,7 +134,9 @@ mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int
  *   eps      >= 0 and finite.
  *   flags    0 or MXQ_FLAG_SCALE_CEIL (the scale rule of the cast).
  *   inv_rms  [T] fp32 output, may be NULL.
- * Other arguments and errors as for mxnorm_fwd (y_workspace NULL -> NULL).
+ * Other arguments and errors as for mxnorm_fwd (y_workspace NULL -> NULL;
+ * also UNSUPPORTED when T * ceil(D / 512) >= 2^32 - 256, the cast pass's
+ * 32-bit count of 512-element chunks).
  */
 mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
                               int64_t T, int64_t D, float eps, mxq_elem elem, mxq_round rnd,
@@ -160,7 +163,8 @@ mxq_status rmsnorm_mxcast_fused_fwd(const uint16_t* x, int64_t ldx, const uint16
  * MXCast of a bf16 activation (MXNorm page, §1.2 and §2.1): block absmax,
  * E8M0 scale and element cast, with no normalisation.
  *   flags    0 or MXQ_FLAG_SCALE_CEIL (the scale rule).
- * Other arguments and errors as for mxnorm_fwd (no gamma, p or inv_norm).
+ * Other arguments and errors as for mxnorm_fwd (no gamma, p or inv_norm;
+ * UNSUPPORTED when T * ceil(D / 512) >= 2^32 - 256, its 32-bit chunk count).
  */
 mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_elem elem,
                       mxq_round rnd, const mxq_rng* rng, uint32_t flags, uint8_t* codes,

@@ -806,8 +806,12 @@ __global__ __launch_bounds__(kThreads) void mxcast_kernel(CastArgs A) {
 
 
 
+// Workgroup counts above this are refused (the x dimension of a grid).
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
 template <int NC, int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_reg(const NormArgs& A, hipStream_t s) {
+  if ((A.T + kRowsPerBlock - 1) / kRowsPerBlock > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
   const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL((mxnorm_reg_kernel<NC, ELEM, RND, GAMMA, STAT>), dim3(grid), dim3(kThreads), 0, s, A);
   MXQ_LAUNCH_CHECK();
@@ -851,6 +855,7 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
     }
   }
   const size_t bytes = per_row * rows + g_bytes;
+  if ((A.T + rows - 1) / rows > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
   auto kern = mxnorm_lds_kernel<ELEM, RND, GAMMA, STAT>;
   if (bytes > 64 * 1024 &&
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -883,6 +888,7 @@ mxq_status dispatch_norm_cast(const NormArgs& A, mxq_elem elem, mxq_round rnd, b
 
 template <int NC, bool GAMMA>
 mxq_status launch_rms_reg(const RmsArgs& A, hipStream_t s) {
+  if ((A.T + kRowsPerBlock - 1) / kRowsPerBlock > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
   const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL((rmsnorm_reg_kernel<NC, GAMMA>), dim3(grid), dim3(kThreads), 0, s, A);
   MXQ_LAUNCH_CHECK();
@@ -900,6 +906,7 @@ mxq_status dispatch_rms(const RmsArgs& A, int nc, hipStream_t s) {
     MXQ_CASE(15) MXQ_CASE(16)
 #undef MXQ_CASE
     default: {
+      if ((A.T + kRowsPerBlock - 1) / kRowsPerBlock > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
       const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
       hipLaunchKernelGGL((rmsnorm_wide_kernel<GAMMA>), dim3(grid), dim3(kThreads), 0, s, A, nc);
       MXQ_LAUNCH_CHECK();
@@ -1029,6 +1036,9 @@ mxq_status rmsnorm_mxcast_fwd(const uint16_t* x, int64_t ldx, const uint16_t* ga
   if (flags & ~(uint32_t)MXQ_FLAG_SCALE_CEIL) return MXQ_ERR_ARG;
   if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
   if (T == 0) return MXQ_OK;
+  // the cast pass counts 512-element chunks in 32 bits, as mxcast_fwd does
+  if ((uint64_t)T * (uint64_t)((D + kChunk - 1) / kChunk) >= (1ull << 32) - kThreads)
+    return MXQ_ERR_UNSUPPORTED;
   if (y_workspace == nullptr) return MXQ_ERR_NULL;
   if (!aligned(y_workspace, 16)) return MXQ_ERR_ALIGN;
   if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;

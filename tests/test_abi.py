@@ -108,6 +108,19 @@ def test_format_rounding_rng_errors(call):
     assert call(rnd=1, rng=None) == mxq.MXQ_ERR_ARG     # SR needs a stream
 
 
+def test_sizes_past_the_launch_limits():
+    # Refused on the host before any HIP call (the pointers are never used).
+    # 32-element rows keep T * D below the 2^40 element limit.
+    huge = 1 << 34   # 2^32 workgroups of 4 rows: past the grid limit
+    assert norm(T=huge, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+    assert rms_fused(T=huge, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+    # 2^32 chunks of 512 elements: past the cast pass's 32-bit chunk count
+    assert rms(T=1 << 32, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+    assert cast(T=1 << 32, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+    # past the element limit
+    assert norm(T=1 << 35, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+
+
 def test_mxnorm_argument_errors():
     assert norm(p=0.0) == mxq.MXQ_ERR_ARG
     assert norm(p=-1.0) == mxq.MXQ_ERR_ARG
