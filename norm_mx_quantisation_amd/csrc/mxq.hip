@@ -253,20 +253,18 @@ __device__ __forceinline__ uint32_t sr_mag_code(float v, uint32_t r) {
   return min(code + (r < frac ? 1u : 0u), kMaxCode);
 }
 
-template <int ELEM>
-__device__ __forceinline__ uint32_t sr_code(float v, uint32_t r) {
-  constexpr int kSignBit = (ELEM == MXQ_E4M3) ? 7 : 3;
-  return sr_mag_code<ELEM>(v, r) | ((__float_as_uint(v) >> 31) << kSignBit);
-}
-
-// Sign bits of four values as bit 7 of four bytes: byte permutes gather each
-// value's top byte, then one and-or merges them into the packed magnitudes
-// (whose bit 7 is clear).
-__device__ __forceinline__ uint32_t with_signs4(uint32_t mags, float a, float b, float c, float d) {
+// The top bytes of four values (a in byte 0 ... d in byte 3), so each sign
+// is bit 7 of its byte: three byte permutes.
+__device__ __forceinline__ uint32_t top_bytes4(float a, float b, float c, float d) {
   const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0C0C0703u);
   const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07030C0Cu);
-  const uint32_t top = __builtin_amdgcn_perm(hi, lo, 0x07060100u);
-  return (top & 0x80808080u) | mags;
+  return __builtin_amdgcn_perm(hi, lo, 0x07060100u);
+}
+
+// Four E4M3 magnitudes packed in bytes (bit 7 clear) with the signs of the
+// four values merged in by one and-or.
+__device__ __forceinline__ uint32_t with_signs4(uint32_t mags, float a, float b, float c, float d) {
+  return (top_bytes4(a, b, c, d) & 0x80808080u) | mags;
 }
 
 __device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
@@ -287,9 +285,17 @@ __device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], BlockScale
   if (s.bad) return 0x77777777u;
   const float inv_scale = __uint_as_float((254u - s.code) << 23);
   uint32_t q = 0;
+  float w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) q |= sr_code<MXQ_E2M1>(y[j] * inv_scale, r[j]) << (4 * j);
-  return q;
+  for (int j = 0; j < 8; ++j) {
+    w[j] = y[j] * inv_scale;
+    q |= sr_mag_code<MXQ_E2M1>(w[j], r[j]) << (4 * j);
+  }
+  // sign of element j is bit 3 of its nibble: bit 7 of byte j / 2 for odd j,
+  // bit 3 of that byte for even j (the even top bytes shifted down a nibble)
+  const uint32_t odd = top_bytes4(w[1], w[3], w[5], w[7]) & 0x80808080u;
+  const uint32_t even = (top_bytes4(w[0], w[2], w[4], w[6]) >> 4) & 0x08080808u;
+  return q | odd | even;
 }
 
 // ------------------------------------------------------------------ memory
