@@ -845,6 +845,80 @@ def test_helpers_refuse_mismatched_buffers_before_launching():
     torch.cuda.synchronize()
 
 
+# ---------------------------------------------------------------- concurrency
+
+def test_concurrent_calls_from_threads_on_their_own_streams():
+    # Every call keeps its state in its arguments: four host threads, each with
+    # its own stream and output buffers, run the fused forward, the SR cast,
+    # the backward with dgamma and the MX GEMM at the same time, 20 times each,
+    # and reproduce the results of the same calls made one after another.
+    import threading
+    gen = torch.Generator(DEV).manual_seed(1234)
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV, rows=2048)
+    T, D = x.shape
+    dy = torch.randn(T, D, device=DEV, generator=gen).to(torch.bfloat16)
+    w = torch.randn(512, D, device=DEV, generator=gen).to(torch.bfloat16)
+    codes, scales, inv = mxq.mxnorm(x, g, 2.0)
+    wc, wsc = mxq.mxcast(w)
+    torch.cuda.synchronize()
+
+    def fwd_out():
+        return (torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(inv))
+
+    def bwd_out():
+        nb = mxq.mxnorm_bwd_workspace_size(T, D)
+        return (torch.empty(T, D, dtype=torch.bfloat16, device=DEV),
+                torch.empty(T, dtype=torch.float32, device=DEV),
+                torch.empty(D, dtype=torch.float32, device=DEV),
+                torch.empty(nb // 4, dtype=torch.float32, device=DEV))
+
+    jobs = {
+        "mxnorm": (fwd_out, lambda s, o: mxq.mxnorm(x, g, 2.0, stream=s, out=o)),
+        "mxcast_sr": (lambda: fwd_out()[:2] + (None,),
+                      lambda s, o: mxq.mxcast(x, "e4m3", "sr", 7, 3, stream=s, out=o)),
+        "backward": (bwd_out, lambda s, o: mxq.mxnorm_backward(x, g, dy, inv, True, stream=s,
+                                                               out=o)),
+        "gemm": (lambda: (torch.empty(T, 512, dtype=torch.float32, device=DEV),),
+                 lambda s, o: mxq.mx_matmul(codes, scales, wc, wsc, stream=s, out=o[0])),
+    }
+    def results(name, o):  # every output but the backward's scratch workspace
+        return tuple(t.clone() for t in (o[:3] if name == "backward" else o) if t is not None)
+
+    want = {}
+    for name, (make, run) in jobs.items():
+        o = make()
+        run(torch.cuda.current_stream(), o)
+        torch.cuda.synchronize()
+        want[name] = results(name, o)
+    got, errors = {}, []
+
+    def worker(name):
+        try:
+            make, run = jobs[name]
+            o = make()
+            s = torch.cuda.Stream()
+            for _ in range(20):
+                run(s, o)
+            s.synchronize()
+            with torch.cuda.stream(s):
+                got[name] = results(name, o)
+            s.synchronize()
+        except Exception as e:  # surfaced below, in the test's own thread
+            errors.append((name, e))
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for name in jobs:
+        assert len(got[name]) == len(want[name]), name
+        for a, b in zip(got[name], want[name]):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
 # ---------------------------------------------------------------- graph capture
 
 def test_graph_replays_match_eager():
