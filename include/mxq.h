@@ -37,7 +37,11 @@
  *   - MXNorm normaliser: inv = RN32(1 / G) with G computed in fp32 from the
  *     exact block maxima (no epsilon, no c(p,B) factor); G == 0 gives inv = 0;
  *     a row holding NaN/Inf gives inv = NaN. y = RN32(RN32(x * gamma) * inv).
- *     inv is accurate to 1e-5 relative while G lies in [2^-126, 2^126].
+ *     When 1/G exceeds the fp32 range (a finite row whose block maxima are all
+ *     below about 2^-128), inv_norm reports +Inf and y applies the same fp32
+ *     mantissa at its true exponent: y = RN32(RN32(x * gamma) * 2^64 *
+ *     (RN32(1/G) * 2^-64)), both power-of-two scalings exact.
+ *   - A NaN in the bf16 y of the two-pass path has no defined sign or payload.
  *   - RMSNorm: inv = 1 / sqrt(sum(x^2) / D + eps) in fp32 and
  *     y = bf16_rne(RN32(RN32(x * gamma) * inv)).
  *   - Stochastic rounding: element n = t * D + d draws word (n & 3) of

@@ -86,31 +86,61 @@ __device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift,
   return lane_terms_p<NCT, P_GEN>(nchunks, mb, shift, p);
 }
 
+// A row's normaliser. The products v = x * gamma are multiplied by `apply`
+// after an exact power-of-two pre-scaling by `pre`: y = RN32((v * pre) * apply).
+// `inv` is RN32(1/G), the value reported per row. While 1/G fits fp32, pre = 1
+// and apply = inv, so y = RN32(v * inv). When 1/G exceeds the fp32 range (a
+// finite row whose block maxima are all below about 2^-128), inv is +Inf,
+// pre = 2^64 and apply = RN32(1/G) * 2^-64: the same fp32 mantissa applied at
+// an exponent fp32 can hold, so y is what RN32(v * RN32(1/G)) would be with an
+// unbounded exponent.
+struct Normaliser {
+  float inv;
+  float apply;
+  float pre;
+};
+
+__device__ __forceinline__ Normaliser plain_normaliser(float inv) { return {inv, inv, 1.0f}; }
+
 // Normaliser 1/G of a row from its block maxima (bf16 bit patterns, one per
 // chunk for this lane's quad, zero for blocks past the row end). lane_max()
 // gives this lane's maximum of the patterns. Terms are added chunk by chunk in
 // each lane, then over the quads; every variant uses exactly this order.
 // A sum inside [2^-96, 2^96] is finite and nonzero, so the row holds no NaN
-// or Inf (either would make the sum non-finite) and is not all zero: the row
-// maximum is only needed outside that range, and for p = inf.
+// or Inf (either would make the sum non-finite) and is not all zero; if G is
+// also a normal fp32 value, inv = 1/G. Otherwise the row maximum decides: NaN
+// or Inf in the row gives NaN, an all-zero row 0; else the maxima are rescaled
+// by 2^-E, E = floor(log2 of the row maximum) (exact also for bf16
+// subnormals), so the largest lies in [1, 2), and G = G' * 2^E. p = inf takes
+// this path always.
 template <int NCT, class BlockMax, class LaneMax>
-__device__ __forceinline__ float row_normaliser(int nchunks, BlockMax mb, LaneMax lane_max,
-                                                int pmode, float p, float K) {
+__device__ __forceinline__ Normaliser row_normaliser(int nchunks, BlockMax mb, LaneMax lane_max,
+                                                     int pmode, float p, float K) {
   if (pmode != P_INF) {
     const float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, 0, pmode, p));
-    if (s >= 0x1p-96f && s <= 0x1p96f) return 1.0f / pmean_finish(s, pmode, p, K);
+    if (s >= 0x1p-96f && s <= 0x1p96f) {
+      const float G = pmean_finish(s, pmode, p, K);
+      if (G >= 0x1p-126f) return plain_normaliser(1.0f / G);
+    }
   }
   const uint32_t rmax = max_over_quads(lane_max());
-  if (rmax >= 0x7F80u) return __builtin_nanf("");  // the row holds NaN or Inf
-  if (rmax == 0u) return 0.0f;                      // all-zero row
-  if (pmode == P_INF) return 1.0f / __uint_as_float(rmax << 16);
-  // The p-th powers left the range where fp32 holds them accurately (an
-  // underflowing or overflowing sum): rescale the maxima by 2^-E, E the
-  // exponent of the row maximum, and undo it on G.
-  int E = (int)((rmax >> 7) & 0xFFu) - 127;
-  if (E < -126) E = -126;
-  const float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p));
-  return 1.0f / ldexpf(pmean_finish(s, pmode, p, K), E);
+  if (rmax >= 0x7F80u) return plain_normaliser(__builtin_nanf(""));  // the row holds NaN or Inf
+  if (rmax == 0u) return plain_normaliser(0.0f);                      // all-zero row
+  // bf16 bits 0x0001 .. 0x7F7F: the biased exponent, or for a subnormal the
+  // position of its leading mantissa bit (value = mantissa * 2^-133)
+  const int ef = (int)(rmax >> 7);
+  const int E = ef ? ef - 127 : -133 + (31 - __builtin_clz(rmax));
+  const float Gs = (pmode == P_INF)
+                       ? ldexpf(__uint_as_float(rmax << 16), -E)
+                       : pmean_finish(sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p)),
+                                      pmode, p, K);
+  const float G = ldexpf(Gs, E);
+  if (G >= 0x1p-126f) return plain_normaliser(1.0f / G);
+  // G below the normal range: scale RN32(1/G') instead of forming a subnormal G
+  const float r = 1.0f / Gs;
+  const float inv = ldexpf(r, -E);  // exact, or +Inf past the fp32 range
+  if (inv <= 0x1.fffffep127f) return plain_normaliser(inv);
+  return {inv, ldexpf(r, -E - 64), 0x1p64f};
 }
 
 // ------------------------------------------------------------------ scales
@@ -416,12 +446,21 @@ __device__ __forceinline__ uint32_t chunk_products(const uint4& xb, const float 
 // Second half: y = RN(v * inv), E8M0 code from max |y| = RN(max |v| * inv)
 // (rounding is monotone), codes stored. Returns the code of the lane's block.
 // vmax_bits has its sign bit clear and inv is +0 or more, or NaN, so the
-// maximum is +0 or more, or NaN, as e8m0_scale expects.
+// maximum is +0 or more, or NaN, as e8m0_scale expects. A normaliser past the
+// fp32 range first scales v and its maximum by N.pre (exact; the branch is
+// uniform over the wavefront and taken only by such rows).
 template <int ELEM, int RND>
 __device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* codes_row,
                                                  uint64_t nrow, uint32_t d, float v[8],
-                                                 uint32_t vmax_bits, float inv) {
-  const float amax = __uint_as_float(vmax_bits) * inv;
+                                                 uint32_t vmax_bits, const Normaliser& N) {
+  float vmax = __uint_as_float(vmax_bits);
+  if (N.pre != 1.0f) {
+    vmax = vmax * N.pre;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * N.pre;
+  }
+  const float inv = N.apply;
+  const float amax = vmax * inv;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * inv;
   const BlockScale s = e8m0_scale<ELEM>(amax, A.ceil_rule ? scale_adjust<ELEM>() : 0u);
@@ -433,10 +472,11 @@ __device__ __forceinline__ uint32_t chunk_finish(const NormArgs& A, uint8_t* cod
 template <int ELEM, int RND, int GM>
 __device__ __forceinline__ uint32_t mxnorm_chunk(const NormArgs& A, uint8_t* codes_row,
                                                  uint64_t nrow, uint32_t d, const uint4& xb,
-                                                 const float g[8], uint32_t mbits, float inv) {
+                                                 const float g[8], uint32_t mbits,
+                                                 const Normaliser& N) {
   float v[8];
   const uint32_t vm = chunk_products<GM>(xb, g, mbits, v);
-  return chunk_finish<ELEM, RND>(A, codes_row, nrow, d, v, vm, inv);
+  return chunk_finish<ELEM, RND>(A, codes_row, nrow, d, v, vm, N);
 }
 
 // 8 bf16 quiet NaNs.
@@ -516,13 +556,13 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
     const uint32_t valid = 0u - (uint32_t)(c * kChunk + dl < A.D);
     mb[c] = quad_max_u32(absmax_bits8(raw[c]) & valid);
   }
-  float inv;
+  Normaliser N;
   if constexpr (STAT == S_RMS) {
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
-    inv = rms_normaliser(s, A.Df, A.eps);
+    N = plain_normaliser(rms_normaliser(s, A.Df, A.eps));
   } else {
     auto lane_max = [&]() {
       uint32_t m = 0;
@@ -530,9 +570,9 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
       for (int c = 0; c < NC; ++c) m = max(m, mb[c]);
       return m;
     };
-    inv = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, lane_max, A.pmode, A.p, A.Kf);
+    N = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, lane_max, A.pmode, A.p, A.Kf);
   }
-  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  if (lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
   // The empty asm claims to rewrite the packed row, so the compiler widens
   // each chunk to fp32 where it is used below instead of ahead of the row
   // reduction, where all widened chunks would be live at once.
@@ -548,7 +588,7 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
     const int d = c * kChunk + dl;
     if (d < A.D) {
       if (GM != G_NONE) gains(g_lds, c, lane, g);
-      const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, crow, nrow, d, raw[c], g, mb[c], inv);
+      const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, crow, nrow, d, raw[c], g, mb[c], N);
       // block d / 32 = 16 c + lane / 4: the chunk's part is an immediate offset
       if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);
     }
@@ -630,21 +670,21 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   auto mb = [&](int c) { return quad_max_u32(absmax_bits8(slice[c * kWave + lane])); };
-  float inv;
+  Normaliser N;
   if constexpr (STAT == S_RMS) {
     float s = 0.0f;
     for (int c = 0; c < nchunks; ++c)
       if (c * kChunk + dl < A.D) s = sumsq8(slice[c * kWave + lane], s);
-    inv = rms_normaliser(s, A.Df, A.eps);
+    N = plain_normaliser(rms_normaliser(s, A.Df, A.eps));
   } else {
     auto lane_max = [&]() {
       uint32_t m = 0;
       for (int c = 0; c < nchunks; ++c) m = max(m, mb(c));
       return m;
     };
-    inv = row_normaliser<0>(nchunks, mb, lane_max, A.pmode, A.p, A.Kf);
+    N = row_normaliser<0>(nchunks, mb, lane_max, A.pmode, A.p, A.Kf);
   }
-  if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  if (lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
 
   const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
   uint8_t* crow = code_row<ELEM>(A.codes, nrow);
@@ -655,10 +695,10 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
       const uint4 xb = slice[c * kWave + lane];
       uint32_t code;
       if (!GAMMA) {
-        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, xb, g, mb(c), inv);
+        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, xb, g, mb(c), N);
       } else {
         unpack8(g_lds[c * kWave + lane], g);
-        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, xb, g, 0u, inv);
+        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, xb, g, 0u, N);
       }
       if ((lane & 3) == 0) put_scale(sc, d >> 5, code);
     }

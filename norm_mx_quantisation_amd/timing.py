@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import os
 import sys
 
 import norm_mx_quantisation_amd as mxq
@@ -25,6 +26,16 @@ HBM_PEAK_GBS = 8000.0
 # (case, workload, operation, options)
 CASES = (
     ("llama3_8b_preattn mxnorm p=2", "llama3_8b_preattn", "mxnorm", {"p": 2.0}),
+    # bytes-only reference kernels with the fused call's traffic and layout
+    # (libmxq_floor.so): what moving these bytes alone reaches at this size,
+    # then with the normaliser's row dependency and the gain staging added
+    ("llama3_8b_preattn floor plain", "llama3_8b_preattn", "floor", {"variant": 0}),
+    ("llama3_8b_preattn floor nt loads", "llama3_8b_preattn", "floor", {"variant": 1}),
+    ("llama3_8b_preattn floor nt stores", "llama3_8b_preattn", "floor", {"variant": 2}),
+    ("llama3_8b_preattn floor nt", "llama3_8b_preattn", "floor", {"variant": 3}),
+    ("llama3_8b_preattn floor nt row-gated", "llama3_8b_preattn", "floor", {"variant": 7}),
+    ("llama3_8b_preattn floor nt row-gated staged", "llama3_8b_preattn", "floor",
+     {"variant": 15}),
     ("llama3_8b_preattn mxnorm p=1", "llama3_8b_preattn", "mxnorm", {"p": 1.0}),
     ("llama3_8b_preattn mxnorm p=2 gamma folded", "llama3_8b_preattn", "mxnorm",
      {"p": 2.0, "gamma": False}),
@@ -150,6 +161,24 @@ def run_libgemm(torch, name, wl, opt, steps, warmup):
           f"{tflops:8.1f} TFLOP/s  {100 * tflops / PEAK_MXFP8_TFLOPS:5.1f}% of MXFP8 peak", flush=True)
 
 
+_floor = None
+
+
+def floor_lib():
+    """libmxq_floor.so, the bytes-only reference kernels (built with libmxq.so)."""
+    global _floor
+    if _floor is None:
+        path = os.path.join(os.path.dirname(mxq.LIB_PATH), "libmxq_floor.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run norm_mx_quantisation_amd.build")
+        L = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.mxq_floor_stream.argtypes = [vp, vp, i64, i64, vp, vp, ctypes.c_int, vp]
+        L.mxq_floor_stream.restype = ctypes.c_int
+        _floor = L
+    return _floor
+
+
 def run_case(torch, name, wl, op, opt, steps, warmup):
     if op == "gemm":
         return run_gemm(torch, name, wl, opt, steps, warmup)
@@ -208,6 +237,8 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
             st = L.rmsnorm_mxcast_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
                                       opt.get("flags", 0), vp(ys[k].data_ptr()), cp, sp, ip,
                                       stream)
+        elif op == "floor":
+            st = floor_lib().mxq_floor_stream(xp, gp, T, D, cp, sp, opt["variant"], stream)
         else:
             st = L.mxcast_fwd(xp, D, T, D, elem, rnd, rngp, opt.get("flags", 0), cp, sp, stream)
         if st != mxq.MXQ_OK:

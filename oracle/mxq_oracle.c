@@ -103,10 +103,14 @@ static double rne_on_grid(double a, int qe) {
   return ldexp(n + up, qe);
 }
 
-/* bf16 round-to-nearest-even of a double (NaN -> 0x7FC0 with the sign kept). */
+/* bf16 round-to-nearest-even of a double. Every NaN becomes the canonical
+ * quiet NaN 0x7FC0: the pages give a NaN in the normalised tensor no sign or
+ * payload, and the sign of a NaN made by arithmetic (Inf * 0 in RMSNorm of a
+ * row holding an Inf) depends on the machine (x86 gives a negative one), so
+ * the oracle fixes one pattern and comparisons treat all NaN patterns alike. */
 uint16_t orc_bf16_rne(double v) {
+  if (isnan(v)) return 0x7FC0;
   uint16_t sign = signbit(v) ? 0x8000 : 0;
-  if (isnan(v)) return sign | 0x7FC0;
   double a = fabs(v);
   if (isinf(a)) return sign | 0x7F80;
   if (a == 0) return sign;

@@ -16,7 +16,8 @@ import torch
 import norm_mx_quantisation_amd as mxq
 import oracle
 from norm_mx_quantisation_amd import workloads
-from parity_util import (assert_bits, check_normaliser, compare_reference, host, np_)
+from parity_util import (assert_bf16_bits, assert_bits, check_normaliser, compare_reference, host,
+                         np_)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -44,16 +45,21 @@ def same_outputs(a, b):
 
 
 def check_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, rows=None, what="", ref=True,
-                 rule="floor"):
-    """Run the kernel on x (device) and check rows [r0, r1) (default all)."""
-    codes, scales, inv = gpu_mxnorm(x, g, p, elem, rnd, flags, rule=rule)
+                 rule="floor", out=None):
+    """Run the kernel on x (device), or take its outputs `out`, and check rows
+    [r0, r1) (default all). Mode (I) applies to rows whose reported normaliser
+    is finite; a row whose 1/G lies past the fp32 range reports +Inf, and its
+    codes are checked against mode (R) here and by scale invariance in
+    test_mxnorm_normaliser_past_fp32_range."""
+    codes, scales, inv = gpu_mxnorm(x, g, p, elem, rnd, flags, rule=rule) if out is None else out
     r0, r1 = (0, x.shape[0]) if rows is None else rows
     xs, gs = host(x[r0:r1]), host(g)
     c, s, i = np_(codes[r0:r1]), np_(scales[r0:r1]), np_(inv[r0:r1])
     oc, os_, _ = oracle.mxnorm(xs, gs, p, elem, rnd, SEED, OFFSET, inv_inject=i, row_base=r0,
                                threads=THREADS, rule=rule)
-    assert_bits(s, os_, f"{what} scales (I)")
-    assert_bits(c, oc, f"{what} codes (I)")
+    inj = ~np.isposinf(i)
+    assert_bits(s[inj], os_[inj], f"{what} scales (I)")
+    assert_bits(c[inj], oc[inj], f"{what} codes (I)")
     if ref:
         rc, rs, rinv = oracle.mxnorm(xs, gs, p, elem, rnd, SEED, OFFSET, row_base=r0,
                                      threads=THREADS, rule=rule)
@@ -62,9 +68,12 @@ def check_mxnorm(x, g, p, elem="e4m3", rnd="rne", flags=0, rows=None, what="", r
     return c, s, i
 
 
-def check_mxcast(x, elem="e4m3", rnd="rne", rows=None, what="", rule="floor"):
-    codes, scales = mxq.mxcast(x, elem, rnd, SEED, OFFSET, scale_rule=rule)
-    torch.cuda.synchronize()
+def check_mxcast(x, elem="e4m3", rnd="rne", rows=None, what="", rule="floor", out=None):
+    if out is None:
+        codes, scales = mxq.mxcast(x, elem, rnd, SEED, OFFSET, scale_rule=rule)
+        torch.cuda.synchronize()
+    else:
+        codes, scales = out
     r0, r1 = (0, x.shape[0]) if rows is None else rows
     oc, os_ = oracle.mxcast(host(x[r0:r1]), elem, rnd, SEED, OFFSET, row_base=r0, threads=THREADS,
                             rule=rule)
@@ -73,7 +82,10 @@ def check_mxcast(x, elem="e4m3", rnd="rne", rows=None, what="", rule="floor"):
     return codes, scales
 
 
-def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what="", rule="floor"):
+def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what="", rule="floor",
+                   ref=True):
+    """The bf16 intermediate y is compared bit for bit, every NaN pattern
+    counting as one value (a NaN in y has no defined sign or payload)."""
     codes, scales, inv, y = mxq.rmsnorm_mxcast(x, g, eps, elem, rnd, SEED, OFFSET, scale_rule=rule)
     torch.cuda.synchronize()
     r0, r1 = (0, x.shape[0]) if rows is None else rows
@@ -81,13 +93,15 @@ def check_two_pass(x, g, eps=1e-5, elem="e4m3", rnd="rne", rows=None, what="", r
     i = np_(inv[r0:r1])
     oy, oc, os_, _ = oracle.rmsnorm_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, inv_inject=i,
                                            row_base=r0, threads=THREADS, rule=rule)
-    assert_bits(np_(y[r0:r1].view(torch.int16)).view(np.uint16), oy, f"{what} y (I)")
+    assert_bf16_bits(np_(y[r0:r1].view(torch.int16)).view(np.uint16), oy, f"{what} y (I)")
     assert_bits(np_(scales[r0:r1]), os_, f"{what} scales (I)")
     assert_bits(np_(codes[r0:r1]), oc, f"{what} codes (I)")
-    ry, rc, rs, rinv = oracle.rmsnorm_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET, row_base=r0,
-                                             threads=THREADS, rule=rule)
-    check_normaliser(i, rinv, what)
-    compare_reference(np_(codes[r0:r1]), np_(scales[r0:r1]), rc, rs, elem, what)
+    if ref:
+        ry, rc, rs, rinv = oracle.rmsnorm_mxcast(xs, gs, eps, elem, rnd, SEED, OFFSET,
+                                                 row_base=r0, threads=THREADS, rule=rule)
+        check_normaliser(i, rinv, what)
+        compare_reference(np_(codes[r0:r1]), np_(scales[r0:r1]), rc, rs, elem, what)
+    return codes, scales, inv, y
 
 
 def check_rms_fused(x, g, eps=1e-5, elem="e4m3", rnd="rne", flags=0, rows=None, what="",
@@ -217,6 +231,52 @@ def test_mxnorm_special_rows(p):
     check_mxnorm(xg, g, p, what=f"special gamma p={p}")
 
 
+def _tiny_rows(D):
+    """Finite rows whose block maxima are bf16 subnormals (each row label says
+    where its normaliser 1/G lands), plus one ordinary row."""
+    x = workloads.random_rows(6, D, seed=79).clone().float()
+    x[0] = x[0] * 2.0**-131              # max |x| ~ 2^-129: 1/G past the fp32 range
+    x[1] = x[1] * 2.0**-126              # G normal, reached through the rescaled sum
+    x[2] = x[2] * 2.0**-128              # G subnormal, 1/G still inside fp32
+    x[3] = 0.0
+    x[3, 77] = 2.0**-133                 # one smallest subnormal: 1/G = K * 2^133
+    # one magnitude per block, (k % 3 + 1) * 2^-133 in block k, random signs:
+    # the block maxima differ, so no element lands on y = +-1, the E8M0
+    # boundary where any rounding of G would flip every block's scale
+    mag = (torch.arange(D) // 32 % 3 + 1).float() * 2.0**-133
+    x[4] = torch.where(x[4] > 0, mag, -mag)
+    return x.to(torch.bfloat16)          # row 5 stays N(0, 1)
+
+
+@pytest.mark.parametrize("flags", [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS])
+@pytest.mark.parametrize("p", [1.0, 2.0, 3.5, math.inf])
+def test_mxnorm_normaliser_past_fp32_range(p, flags):
+    # Rows of bf16 subnormals: G can fall below 2^-128, where 1/G exceeds fp32.
+    # The kernel then reports inv_norm = +Inf and applies RN32(1/G) at a
+    # representable exponent after scaling the products by 2^64. Checks:
+    # mode (R) (normaliser: +Inf exactly where 1/G is past FLT_MAX, finite
+    # values within 1e-5; codes within the dequantised tolerance), and, since
+    # MXNorm is invariant under x -> 2^64 x, the tiny rows' codes and scales
+    # bit-equal to the kernel's on the scaled rows, which have finite
+    # normalisers and pass mode (I) bit-exactly.
+    D = 512
+    x = _tiny_rows(D)
+    g = workloads.random_gamma(D, seed=80)
+    for gam in (None, g):
+        gd = None if gam is None else gam.to(DEV)
+        what = f"tiny rows p={p} flags={flags} gamma={gam is not None}"
+        c, sc, i = check_mxnorm(x.to(DEV), gd, p, flags=flags, what=what)   # host arrays
+        assert np.isposinf(i[0]) and np.isposinf(i[3]) and np.isposinf(i[4]), i
+        assert np.isfinite(i[[1, 2, 5]]).all() and i[2] > 2.0**126, i
+        assert (sc != 255).all()               # no row of finite values is poisoned
+        xs = (x[:5].float() * 2.0**64).to(torch.bfloat16)        # exact: subnormals widen
+        assert torch.equal(xs.float(), x[:5].float() * 2.0**64)
+        c2, s2, i2 = check_mxnorm(xs.to(DEV), gd, p, flags=flags, what=what + " x 2^64")
+        assert np.isfinite(i2).all()
+        assert_bits(sc[:5], s2, what + " scale invariance (scales)")
+        assert_bits(c[:5], c2, what + " scale invariance (codes)")
+
+
 @pytest.mark.parametrize("flags", [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS])
 def test_mxnorm_nonfinite_gains(flags):
     # a NaN or Inf gain makes its products non-finite: those blocks get scale
@@ -241,13 +301,40 @@ def test_mxnorm_nonfinite_gains(flags):
 
 @pytest.mark.parametrize("D", [256, 4096, 8192])
 @pytest.mark.parametrize("gamma", [False, True])
-def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma):
+@pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e4m3", "sr"), ("e2m1", "rne"),
+                                      ("e2m1", "sr")])
+def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma, elem, rnd):
     x = workloads.random_rows(37, D, seed=79 + D, device=DEV)
+    x[5, :64] *= 40.0
     g = workloads.random_gamma(D, seed=80, device=DEV) if gamma else None
-    for p in (1.0, 2.0, 3.5):
-        a = gpu_mxnorm(x, g, p, flags=mxq.MXQ_FLAG_FORCE_REG)
-        b = gpu_mxnorm(x, g, p, flags=mxq.MXQ_FLAG_FORCE_LDS)
+    for p in (1.0, 2.0, 3.5, math.inf):
+        a = gpu_mxnorm(x, g, p, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_REG)
+        b = gpu_mxnorm(x, g, p, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_LDS)
         assert same_outputs(a, b), p
+
+
+@pytest.mark.parametrize("elem,rnd", [("e2m1", "rne"), ("e4m3", "rne"), ("e2m1", "sr")])
+@pytest.mark.parametrize("D", [1024, 8192, 8224])
+def test_mxnorm_lds_variant_against_the_oracle(elem, rnd, D):
+    # the LDS-staged kernel on its own, with gains, every format and rounding
+    x = workloads.random_rows(9, D, seed=81 + D, device=DEV)
+    x[2, :96] *= 25.0
+    g = workloads.random_gamma(D, seed=82, device=DEV)
+    check_mxnorm(x, g, 2.0, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_LDS, what=f"lds {elem} {rnd} D={D}")
+    check_mxnorm(x, None, 1.0, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_LDS,
+                 what=f"lds {elem} {rnd} D={D} no gamma")
+
+
+@pytest.mark.parametrize("flags", [0, mxq.MXQ_FLAG_FORCE_LDS])
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_mxnorm_strided_rows_both_variants(flags, elem):
+    # rows inside a wider buffer (ldx > D) through either kernel
+    x = workloads.random_rows(11, 1024, seed=83, device=DEV, ldx=1056)
+    assert x.stride(0) == 1056
+    g = workloads.random_gamma(1024, seed=84, device=DEV)
+    c1, s1, i1 = check_mxnorm(x, g, 2.0, elem, flags=flags, what=f"strided {elem} flags={flags}")
+    c2, s2, i2 = gpu_mxnorm(x.contiguous(), g, 2.0, elem, flags=flags)
+    assert np.array_equal(c1, np_(c2)) and np.array_equal(s1, np_(s2)) and np.array_equal(i1, np_(i2))
 
 
 def test_mxnorm_empty_input():
@@ -272,6 +359,40 @@ def test_two_pass_formats(elem, rnd):
     x = workloads.random_rows(16, 1024, seed=83, device=DEV)
     check_two_pass(x, workloads.random_gamma(1024, seed=84, device=DEV), elem=elem, rnd=rnd,
                    what=f"two-pass {elem} {rnd}")
+
+
+@pytest.mark.parametrize("gamma", [False, True])
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_two_pass_special_rows(gamma, elem):
+    # zero, -0, NaN, +-Inf, bf16 subnormal and 1e+-30 rows through the two-pass
+    # path. A NaN makes the sum of squares NaN (whole row NaN); an Inf makes it
+    # Inf, so inv_rms = 0 and the Inf element's y = Inf * 0 is NaN (its block
+    # 0xFF, the others signed zeros). Mode (I) covers every row; mode (R) the
+    # rows whose fp32 statistic stays in range (1e30^2 overflows fp32).
+    D = 512
+    x = workloads.random_rows(10, D, seed=85).clone()
+    x[0] = 0.0
+    x[1] = -0.0
+    x[1, 3] = 0.0
+    x[2, 100] = float("nan")
+    x[3, 7] = float("inf")
+    x[4, 300] = float("-inf")
+    x[5] = x[5] * 2.0**-128          # bf16 subnormals: the sum of squares underflows
+    x[6] = x[6] * 1e-30
+    x[7, :32] = 0.0                  # a zero block in an ordinary row
+    x[8] = x[8] * 1e30               # the sum of squares overflows fp32: (I) only
+    xg = x.to(DEV)
+    g = workloads.random_gamma(D, seed=86, device=DEV) if gamma else None
+    what = f"two-pass special gamma={gamma} {elem}"
+    codes, scales, inv, y = check_two_pass(xg, g, elem=elem, rows=(0, 8), what=what)
+    check_two_pass(xg, g, elem=elem, rows=(8, 10), what=what + " (I)", ref=False)
+    i, sc, yb = np_(inv), np_(scales), np_(y.view(torch.int16)).view(np.uint16)
+    assert math.isnan(i[2]) and (sc[2] == 255).all()
+    assert i[3] == 0 and i[4] == 0
+    assert sc[3, 0] == 255 and (sc[3, 1:] == 0).all() and sc[4, 300 // 32] == 255
+    assert (yb[3, 7] & 0x7FFF) > 0x7F80                       # NaN
+    assert (yb[0] == 0).all() and (yb[1] & 0x7FFF == 0).all() and (sc[:2] == 0).all()
+    assert i[8] == 0 and (sc[8] == 0).all()                   # sum of squares overflowed
 
 
 @pytest.mark.parametrize("D", [mxq.MXQ_MAX_D, mxq.MXQ_MAX_D - 32])
@@ -766,7 +887,14 @@ def test_workload_llama3_8b_full():
     check_rms_fused(x, g, what="llama3-8b rms-fused")
 
 
-def test_workload_longseq_sampled_and_variants_identical():
+def _batches(T, rows):
+    return [(r0, min(T, r0 + rows)) for r0 in range(0, T, rows)]
+
+
+def test_workload_longseq_full_and_variants_identical():
+    # every row of [65536, 8192] against the oracle, in row batches: the
+    # register and LDS-staged kernels give the same bits on the whole tensor,
+    # so the oracle comparison covers both
     x, g = workloads.make_inputs("longseq_t3", device=DEV)
     T = x.shape[0]
     reg = gpu_mxnorm(x, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_REG)
@@ -775,17 +903,22 @@ def test_workload_longseq_sampled_and_variants_identical():
     del lds
     auto = gpu_mxnorm(x, g, 2.0)
     assert same_outputs(reg, auto)
-    del reg, auto
-    for r0 in (0, T // 2, T - 256):
-        check_mxnorm(x, g, 2.0, rows=(r0, r0 + 256), what=f"longseq rows {r0}")
+    del auto
+    for r0, r1 in _batches(T, 4096):
+        check_mxnorm(x, g, 2.0, rows=(r0, r1), out=reg, what=f"longseq rows {r0}")
 
 
-def test_workload_swiglu_sampled_and_sr_unbiased():
+def test_workload_swiglu_full_and_sr_unbiased():
+    # MXCast of every row of [16384, 14336], RNE and Philox stochastic
+    # rounding, bit-exact against the oracle (the 16 rows scaled x100 included)
     x, _ = workloads.make_inputs("swiglu_downproj", device=DEV)
     T = x.shape[0]
-    for r0 in (0, T - 128):
-        check_mxcast(x, "e4m3", "rne", rows=(r0, r0 + 128), what=f"swiglu rne {r0}")
-        check_mxcast(x, "e4m3", "sr", rows=(r0, r0 + 128), what=f"swiglu sr {r0}")
+    for rnd in ("rne", "sr"):
+        out = mxq.mxcast(x, "e4m3", rnd, SEED, OFFSET)
+        torch.cuda.synchronize()
+        for r0, r1 in _batches(T, 2048):
+            check_mxcast(x, "e4m3", rnd, rows=(r0, r1), out=out, what=f"swiglu {rnd} {r0}")
+        del out
     # mean stochastic-rounding error over the whole tensor, in element ulps, ~ 0
     codes, scales = mxq.mxcast(x, "e4m3", "sr", SEED, OFFSET)
     tab = torch.tensor(oracle.decode_table("e4m3"), dtype=torch.float64, device=DEV)
@@ -807,11 +940,12 @@ def test_workload_swiglu_sampled_and_sr_unbiased():
     assert abs(mean) < 5 * sd / math.sqrt(n_sum) + 1e-6, (mean, sd, n_sum)
 
 
-def test_workload_mxfp4_sampled():
+def test_workload_mxfp4_full():
+    # every row of [32768, 4096], MXNorm p = 2 -> packed E2M1, against the oracle
     x, g = workloads.make_inputs("mxfp4", device=DEV)
-    T = x.shape[0]
-    for r0 in (0, T // 3, T - 512):
-        check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r0 + 512), what=f"mxfp4 rows {r0}")
+    out = gpu_mxnorm(x, g, 2.0, "e2m1")
+    for r0, r1 in _batches(x.shape[0], 8192):
+        check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r1), out=out, what=f"mxfp4 rows {r0}")
 
 
 # ---------------------------------------------------------------- caller buffers

@@ -7,6 +7,7 @@ whole code table, and defining inequalities of the scale rule.
 """
 
 import math
+import struct
 import os
 
 import numpy as np
@@ -81,6 +82,23 @@ def test_bf16_rne_matches_torch_on_fp32(orc):
     ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = np.array([orc.bf16_rne(float(v)) for v in f], np.uint16)
     assert (got == ref).all()
+
+
+def test_bf16_rne_nan_is_canonical(orc):
+    # a NaN in the bf16 intermediate carries no sign or payload: whatever NaN
+    # fp64 arithmetic made (x86 makes Inf * 0 a negative one), the result is
+    # the canonical quiet NaN
+    inf_times_zero = np.float64(np.inf) * np.float64(0.0)
+    neg_nan = -np.float64(np.nan)
+    assert np.isnan(inf_times_zero) and np.signbit(neg_nan)
+    for v in (float("nan"), float(neg_nan), float(inf_times_zero),
+              struct.unpack("<d", struct.pack("<Q", 0x7FF0000000000001))[0],   # signalling
+              struct.unpack("<d", struct.pack("<Q", 0xFFF8DEADBEEF0000))[0]):  # payload, negative
+        assert math.isnan(v)
+        assert orc.bf16_rne(v) == 0x7FC0
+    # infinities and zeros keep their signs
+    assert orc.bf16_rne(math.inf) == 0x7F80 and orc.bf16_rne(-math.inf) == 0xFF80
+    assert orc.bf16_rne(0.0) == 0x0000 and orc.bf16_rne(-0.0) == 0x8000
 
 
 def test_bf16_rne_ties_from_fp64(orc):
