@@ -62,7 +62,8 @@
  *     HIP call; a launch failure returns MXQ_ERR_HIP; a device fault shows at
  *     the caller's next synchronisation.
  *   - T == 0 is a valid empty call (pointers are not read).
- *   - no global mutable state: calls are thread-safe.
+ *   - no global mutable state (except the scratch array of
+ *     mxnorm_bwd_noalloc, described there): calls are thread-safe.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -205,6 +206,26 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
 
 /* Workspace bytes mxnorm_bwd needs to produce dgamma (0 for a bad shape). */
 size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D);
+
+/*
+ * mxnorm_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It computes exactly what mxnorm_bwd computes, with
+ * the same kernels and summation order (bit-identical results), and allocates
+ * nothing: the dgamma partial sums live in a 16 MiB array that the library
+ * holds on each GPU it runs on until the process ends (every shape this entry
+ * point accepts fits it; a larger one would return UNSUPPORTED). That array is
+ * shared by every call on the GPU, so calls that overlap on one GPU (two
+ * streams, two threads) race on it and must be serialised by the caller. The
+ * current device must be the stream's device. The first call on a device
+ * looks up the array's address on it.
+ * Arguments and errors as for mxnorm_bwd without workspace and
+ * workspace_bytes (HIP also when the array's address cannot be looked up).
+ */
+mxq_status mxnorm_bwd_noalloc(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                              const uint16_t* dy, int64_t lddy, const float* inv_norm, int64_t T,
+                              int64_t D, uint16_t* dx, float* row_dot, float* dgamma,
+                              void* stream);
 
 /* Element type of a GEMM result. */
 typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;

@@ -30,8 +30,8 @@ MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
 ABI_VERSION = 2
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
-           "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mx_gemm", "mxq_strerror",
-           "mxq_abi_version")
+           "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mxnorm_bwd_noalloc", "mx_gemm",
+           "mxq_strerror", "mxq_abi_version")
 
 
 class mxq_rng(ctypes.Structure):
@@ -74,6 +74,8 @@ def lib():
             L.mxnorm_bwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
             L.mxnorm_bwd.restype = i32
+            L.mxnorm_bwd_noalloc.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp]
+            L.mxnorm_bwd_noalloc.restype = i32
             L.mxnorm_bwd_workspace_size.argtypes = [i64, i64]
             L.mxnorm_bwd_workspace_size.restype = ctypes.c_size_t
             L.mx_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, i32, vp,
@@ -126,6 +128,12 @@ def mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, wor
                workspace_bytes, stream) -> int:
     return lib().mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma,
                             workspace, workspace_bytes, stream)
+
+
+def mxnorm_bwd_noalloc(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma,
+                       stream) -> int:
+    return lib().mxnorm_bwd_noalloc(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma,
+                                    stream)
 
 
 def mxnorm_bwd_workspace_size(T, D) -> int:

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mxq.h"
 
 namespace {
@@ -341,39 +343,34 @@ mxq_status launch_col_sum(const float* in, int rows, int D, float* out, hipStrea
   return MXQ_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D) {
-  if (T < 0 || D <= 0 || D % 32 != 0) return 0;
-  return bwd_plan(T, D).workspace_bytes;
-}
-
-mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
-                      int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
-                      float* row_dot, float* dgamma, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+// Argument checks shared by both entry points (the workspace is checked by
+// the caller).
+mxq_status check_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
+                     int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
+                     const float* row_dot, const float* dgamma) {
   if (T < 0 || D <= 0 || D % 32 != 0 || ldx < D || lddy < D) return MXQ_ERR_SHAPE;
   if (D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
   if ((uint64_t)T * (uint64_t)D >= (1ull << 40)) return MXQ_ERR_UNSUPPORTED;
-  const BwdPlan plan = bwd_plan(T, D, dgamma != nullptr);
-  if (dgamma != nullptr) {
-    if (workspace == nullptr) return MXQ_ERR_NULL;
-    if (workspace_bytes < plan.workspace_bytes) return MXQ_ERR_ARG;
-    if (!aligned(dgamma, 16) || !aligned(workspace, 16)) return MXQ_ERR_ALIGN;
-  }
-  hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {
-    // nothing to read; the gain's gradient of an empty batch is zero
-    return dgamma ? launch_col_sum(nullptr, 0, (int)D, dgamma, s) : MXQ_OK;
-  }
+  if (dgamma != nullptr && !aligned(dgamma, 16)) return MXQ_ERR_ALIGN;
+  if (T == 0) return MXQ_OK;
   if (x == nullptr || dy == nullptr || inv_norm == nullptr || dx == nullptr) return MXQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || ldx % 8 != 0 || lddy % 8 != 0)
     return MXQ_ERR_ALIGN;
   if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
   if (!aligned(inv_norm, 4) || (row_dot != nullptr && !aligned(row_dot, 4))) return MXQ_ERR_ALIGN;
+  return MXQ_OK;
+}
 
+// Launches after validation; partial holds the dgamma partial rows (at least
+// bwd_plan(T, D).workspace_bytes) when dgamma is wanted.
+mxq_status run_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
+                   int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
+                   float* row_dot, float* dgamma, float* partial, hipStream_t s) {
+  if (T == 0) {
+    // nothing to read; the gain's gradient of an empty batch is zero
+    return dgamma ? launch_col_sum(nullptr, 0, (int)D, dgamma, s) : MXQ_OK;
+  }
+  const BwdPlan plan = bwd_plan(T, D, dgamma != nullptr);
   BwdArgs A;
   A.x = x;
   A.dy = dy;
@@ -381,7 +378,7 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
   A.inv = inv_norm;
   A.dx = dx;
   A.row_dot = row_dot;
-  A.partial = dgamma ? static_cast<float*>(workspace) : nullptr;
+  A.partial = dgamma ? partial : nullptr;
   A.ldx = ldx;
   A.lddy = lddy;
   A.T = T;
@@ -399,6 +396,83 @@ mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, con
   if (st != MXQ_OK || dgamma == nullptr) return st;
   // partials [groups][D] -> dgamma [D]
   return launch_col_sum(A.partial, (int)plan.groups, (int)D, dgamma, s);
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+
+// The dgamma partial rows of mxnorm_bwd_noalloc: every partial row the
+// backward can write (at most kBwdMaxGroups rows of MXQ_MAX_D_REG floats,
+// 16 MiB), in one array per GPU that the library holds until the process
+// ends. Each call writes every partial row it later reads, so nothing needs
+// clearing between calls; calls that overlap on one GPU race on it.
+constexpr size_t kScratchBytes = (size_t)kBwdMaxGroups * MXQ_MAX_D_REG * sizeof(float);
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The array's device address on the current device. In host code `scratch`
+// is only a handle for the runtime, never an address a kernel may use: the
+// address is looked up once per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+mxq_status device_scratch(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MXQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MXQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MXQ_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch[dev]);
+  return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mxnorm_bwd_workspace_size(int64_t T, int64_t D) {
+  if (T < 0 || D <= 0 || D % 32 != 0) return 0;
+  return bwd_plan(T, D).workspace_bytes;
+}
+
+mxq_status mxnorm_bwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, const uint16_t* dy,
+                      int64_t lddy, const float* inv_norm, int64_t T, int64_t D, uint16_t* dx,
+                      float* row_dot, float* dgamma, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  mxq_status st = check_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma);
+  if (st != MXQ_OK) return st;
+  if (dgamma != nullptr) {
+    if (workspace == nullptr) return MXQ_ERR_NULL;
+    if (workspace_bytes < bwd_plan(T, D).workspace_bytes) return MXQ_ERR_ARG;
+    if (!aligned(workspace, 16)) return MXQ_ERR_ALIGN;
+  }
+  return run_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma,
+                 static_cast<float*>(workspace), (hipStream_t)stream);
+}
+
+mxq_status mxnorm_bwd_noalloc(const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                              const uint16_t* dy, int64_t lddy, const float* inv_norm, int64_t T,
+                              int64_t D, uint16_t* dx, float* row_dot, float* dgamma,
+                              void* stream) {
+  mxq_status st = check_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma);
+  if (st != MXQ_OK) return st;
+  float* partial = nullptr;
+  if (dgamma != nullptr) {
+    if (bwd_plan(T, D).workspace_bytes > kScratchBytes) return MXQ_ERR_UNSUPPORTED;
+    st = device_scratch(&partial);
+    if (st != MXQ_OK) return st;
+  }
+  return run_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, partial,
+                 (hipStream_t)stream);
 }
 
 }  // extern "C"

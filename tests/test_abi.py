@@ -255,6 +255,29 @@ def test_backward_argument_errors():
     assert bwd(T=0, x=None, dy=None, inv=None, dx=None) == mxq.MXQ_OK
 
 
+def nbwd(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, dy=A16, lddy=4096, inv=A16, T=8, D=4096, dx=A16,
+             row_dot=None, dgamma=None, stream=None)
+    a.update(kw)
+    return mxq.mxnorm_bwd_noalloc(a["x"], a["ldx"], a["gamma"], a["dy"], a["lddy"], a["inv"],
+                                  a["T"], a["D"], a["dx"], a["row_dot"], a["dgamma"], a["stream"])
+
+
+def test_noalloc_backward_argument_errors():
+    # the same checks as mxnorm_bwd, before any HIP call (these never reach the
+    # scratch array's lookup or a launch)
+    assert nbwd(D=0) == mxq.MXQ_ERR_SHAPE
+    assert nbwd(T=-1) == mxq.MXQ_ERR_SHAPE
+    assert nbwd(ldx=2048) == mxq.MXQ_ERR_SHAPE
+    assert nbwd(D=8224, ldx=8224, lddy=8224) == mxq.MXQ_ERR_UNSUPPORTED
+    assert nbwd(x=None) == mxq.MXQ_ERR_NULL
+    assert nbwd(dx=None, dgamma=A16) == mxq.MXQ_ERR_NULL
+    assert nbwd(x=A8) == mxq.MXQ_ERR_ALIGN
+    assert nbwd(dgamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert nbwd(gamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert nbwd(lddy=4100) == mxq.MXQ_ERR_ALIGN
+
+
 def test_backward_workspace_grows_slowly_with_rows():
     # one partial row of D floats per workgroup, at most 512 workgroups
     D = 4096
