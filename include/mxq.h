@@ -44,11 +44,13 @@
  *   - A NaN in the bf16 y of the two-pass path has no defined sign or payload.
  *   - RMSNorm: inv = 1 / sqrt(sum(x^2) / D + eps) in fp32 and
  *     y = bf16_rne(RN32(RN32(x * gamma) * inv)).
- *   - Stochastic rounding: element n = t * D + d draws word (n & 3) of
- *     Philox4x32-10 (Salmon et al., SC'11) with key = seed (low word first)
- *     and counter = (n >> 2 as two words, offset as two words); it rounds up
- *     iff word < floor(frac * 2^32), frac the distance above the lower
- *     neighbour in units of the local quantum.
+ *   - Stochastic rounding: element n = t * D + d draws word r = word (n & 3)
+ *     of Philox4x32-10 (Salmon et al., SC'11) with key = seed (low word first)
+ *     and counter = (n >> 2 as two words, offset as two words); with frac the
+ *     distance above the lower neighbour in units of the local quantum, it
+ *     rounds up iff r < 2^(32-B) * floor(frac * 2^B): the top B bits of r
+ *     against the top B bits of frac, B = 20 for E4M3 and 22 for E2M1 (the
+ *     fp32 mantissa bits the format drops).
  *
  * Memory and execution:
  *   - every pointer is a device pointer owned by the caller; the library

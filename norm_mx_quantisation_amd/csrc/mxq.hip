@@ -23,8 +23,9 @@
 //   * Element casts use the gfx950 scaled converts (the E8M0 code is the
 //     exponent field of the fp32 scale operand, which divides). The FP8
 //     convert does not saturate, so values are clamped to +-448 * 2^s first;
-//     the FP4 convert saturates by itself. Stochastic rounding is integer
-//     code on Philox4x32-10 words.
+//     the FP4 convert saturates by itself. Stochastic rounding uses the
+//     gfx950 stochastic-rounding converts fed the complement of each
+//     element's Philox4x32-10 word (see encode8_e4m3_sr).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -188,11 +189,14 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53
-// and 0xCD9E8D57, key increments 0x9E3779B9 and 0xBB67AE85.
-__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                               uint32_t k0, uint32_t k1) {
+// and 0xCD9E8D57, key increments 0x9E3779B9 and 0xBB67AE85. Returns the
+// bitwise complement of the four output words (what the stochastic-rounding
+// converts take, see encode8_e4m3_sr): the last round's xors become xnors
+// (truth table 0x69) and its two low products are inverted.
+__device__ __forceinline__ uint4 philox4x32_10_not(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                   uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 9; ++i) {
     // one 32x32 -> 64-bit multiply each (v_mad_u64_u32 gives both halves)
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
@@ -203,16 +207,19 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
-  return make_uint4(c0, c1, c2, c3);
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  return make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x69), ~(uint32_t)p1,
+                    __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x69), ~(uint32_t)p0);
 }
 
 struct SrStream {
   uint32_t k0, k1, o0, o1;
-  // Words for logical elements n0 .. n0+7 (n0 % 8 == 0).
-  __device__ __forceinline__ void words8(uint64_t n0, uint32_t r[8]) const {
+  // Complemented words for logical elements n0 .. n0+7 (n0 % 8 == 0).
+  __device__ __forceinline__ void words8_not(uint64_t n0, uint32_t r[8]) const {
     const uint64_t b = n0 >> 2;
-    const uint4 a = philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), o0, o1, k0, k1);
-    const uint4 c = philox4x32_10((uint32_t)(b + 1), (uint32_t)((b + 1) >> 32), o0, o1, k0, k1);
+    const uint4 a = philox4x32_10_not((uint32_t)b, (uint32_t)(b >> 32), o0, o1, k0, k1);
+    const uint4 c = philox4x32_10_not((uint32_t)(b + 1), (uint32_t)((b + 1) >> 32), o0, o1, k0, k1);
     r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
     r[4] = c.x; r[5] = c.y; r[6] = c.z; r[7] = c.w;
   }
@@ -255,77 +262,81 @@ __device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], BlockScal
   return bad ? 0x77777777u : q;
 }
 
-// Stochastic rounding of v (already divided by the scale, |v| < 2^(emax+1)):
-// with n the magnitude in units of the local quantum, truncated, and frac32 =
-// floor(frac * 2^32) the part below it, round up iff r < frac32; saturating.
-//   normal binades: n and the exponent form the code directly, (a >> sh) - bias,
-//     and the discarded mantissa bits shifted to the top are frac32;
-//   below the smallest normal the quantum is fixed (2^-9, E2M1 2^-1): q = |v| /
-//     quantum is exact, n = trunc(q), and (q - n) * 2^32 is exact as well.
-//   The magnitude goes through abs source modifiers and a bit-field extract
-//   (no masking instruction); q - n is the hardware fraction of q (exact for
-//   q >= 0). The sign is left to the caller.
-template <int ELEM>
-__device__ __forceinline__ uint32_t sr_mag_code(float v, uint32_t r) {
-  constexpr int kSh = (ELEM == MXQ_E4M3) ? 20 : 22;                // fp32 mantissa bits dropped
-  constexpr uint32_t kBias = (ELEM == MXQ_E4M3) ? 960u : 252u;     // (120 << 3), (126 << 1)
-  constexpr float kMinNormal = (ELEM == MXQ_E4M3) ? 0x1p-6f : 1.0f;
-  constexpr float kInvQuantum = (ELEM == MXQ_E4M3) ? 512.0f : 2.0f;
-  constexpr uint32_t kMaxCode = (ELEM == MXQ_E4M3) ? 0x7Eu : 0x7u;
-  const uint32_t u = __float_as_uint(v);
-  // both forms, then a select per lane (no divergent branch); q < 2^18 always
-  const float q = fabsf(v) * kInvQuantum;
-  const uint32_t n_sub = (uint32_t)q;
-  const uint32_t f_sub = (uint32_t)(__builtin_amdgcn_fractf(q) * 4294967296.0f);
-  const bool normal = fabsf(v) >= kMinNormal;
-  const uint32_t code = normal ? __builtin_amdgcn_ubfe(u, kSh, 31 - kSh) - kBias : n_sub;
-  const uint32_t frac = normal ? u << (32 - kSh) : f_sub;  // the sign bit shifts out
-  return min(code + (r < frac ? 1u : 0u), kMaxCode);
-}
-
-// The top bytes of four values (a in byte 0 ... d in byte 3), so each sign
-// is bit 7 of its byte: three byte permutes.
-__device__ __forceinline__ uint32_t top_bytes4(float a, float b, float c, float d) {
-  const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0C0C0703u);
-  const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07030C0Cu);
-  return __builtin_amdgcn_perm(hi, lo, 0x07060100u);
-}
-
-// Four E4M3 magnitudes packed in bytes (bit 7 clear) with the signs of the
-// four values merged in by one and-or.
-__device__ __forceinline__ uint32_t with_signs4(uint32_t mags, float a, float b, float c, float d) {
-  return (top_bytes4(a, b, c, d) & 0x80808080u) | mags;
-}
-
-__device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
-  if (s.bad) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  const float inv_scale = __uint_as_float((254u - s.code) << 23);  // 2^-(code-127), a normal float
-  uint32_t c[8];
+// Stochastic rounding: with q = |y| / 2^s in units of the local quantum,
+// n = floor(q) and f = q - n, round up iff r < 2^(32-B) * floor(f * 2^B), where
+// r is the element's Philox word and B = 23 - (stored mantissa bits) is the
+// number of fp32 mantissa bits the format drops (20 for E4M3, 22 for E2M1);
+// saturating. The gfx950 stochastic-rounding converts take exactly this
+// decision when fed ~r: they add the top B bits of their random operand to the
+// top B bits of the fraction and round up on the carry, and
+// f_B + (2^B - 1 - r_B) >= 2^B  <=>  r_B < f_B  (r_B, f_B the top B bits).
+// Probed on the device against the rule over random values from 2^-45 to the
+// format maximum (subnormal targets included) and at every threshold +- 1 and
+// +- one step of the low bits; the FP4 convert is given one value per
+// instruction (its pair partner zero), because it draws the second value's
+// bits differently. Both converts are clamped first, like the FP8 RNE path
+// (the FP8 convert does not saturate; 448 and 6 are on the grid, so a clamped
+// value's fraction is zero and it stays put).
+__device__ __forceinline__ uint2 encode8_e4m3_sr(const float y[8], BlockScale s, const uint32_t nr[8]) {
+  const uint32_t code = s.code;
+  const float scale = __uint_as_float(code << 23);
+  const float lim = __uint_as_float(((code + 8u) << 23) | 0x00600000u);  // 448 * 2^(code-127)
   float w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w[j] = y[j] * inv_scale;
-    c[j] = sr_mag_code<MXQ_E4M3>(w[j], r[j]);
-  }
-  return make_uint2(with_signs4(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, w[0], w[1], w[2], w[3]),
-                    with_signs4(c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24, w[4], w[5], w[6], w[7]));
+  for (int j = 0; j < 8; ++j) w[j] = __builtin_amdgcn_fmed3f(y[j], -lim, lim);
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(lo, w[0], nr[0], scale, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(lo, w[1], nr[1], scale, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(lo, w[2], nr[2], scale, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(lo, w[3], nr[3], scale, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(hi, w[4], nr[4], scale, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(hi, w[5], nr[5], scale, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(hi, w[6], nr[6], scale, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(hi, w[7], nr[7], scale, 3);
+  return make_uint2(s.bad ? 0x7F7F7F7Fu : (uint32_t)lo, s.bad ? 0x7F7F7F7Fu : (uint32_t)hi);
 }
 
-__device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], BlockScale s, const uint32_t r[8]) {
-  if (s.bad) return 0x77777777u;
-  const float inv_scale = __uint_as_float((254u - s.code) << 23);
-  uint32_t q = 0;
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// One value through the FP4 stochastic-rounding convert into byte SEL of acc
+// (low nibble; the pair partner is zero, so the high nibble is 0). Written as
+// assembly because the compiler does not carry the destination's other bytes
+// from one call of this convert's builtin to the next; here the destination
+// is an input and output of every instruction, as the hardware treats it.
+template <int SEL>
+__device__ __forceinline__ void cvt_sr_fp4_into(uint32_t& acc, float w, uint32_t nr, float scale) {
+  const float2_t pair = {w, 0.0f};
+  if constexpr (SEL == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(pair), "v"(nr), "v"(scale));
+  else if constexpr (SEL == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]"
+        : "+v"(acc) : "v"(pair), "v"(nr), "v"(scale));
+  else if constexpr (SEL == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]"
+        : "+v"(acc) : "v"(pair), "v"(nr), "v"(scale));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]"
+        : "+v"(acc) : "v"(pair), "v"(nr), "v"(scale));
+}
+
+__device__ __forceinline__ uint32_t encode8_e2m1_sr(const float y[8], BlockScale s, const uint32_t nr[8]) {
+  const uint32_t code = s.code;
+  const float scale = __uint_as_float(code << 23);
+  const float lim = __uint_as_float(((code + 2u) << 23) | 0x00400000u);  // 6 * 2^(code-127)
   float w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w[j] = y[j] * inv_scale;
-    q |= sr_mag_code<MXQ_E2M1>(w[j], r[j]) << (4 * j);
-  }
-  // sign of element j is bit 3 of its nibble: bit 7 of byte j / 2 for odd j,
-  // bit 3 of that byte for even j (the even top bytes shifted down a nibble)
-  const uint32_t odd = top_bytes4(w[1], w[3], w[5], w[7]) & 0x80808080u;
-  const uint32_t even = (top_bytes4(w[0], w[2], w[4], w[6]) >> 4) & 0x08080808u;
-  return q | odd | even;
+  for (int j = 0; j < 8; ++j) w[j] = __builtin_amdgcn_fmed3f(y[j], -lim, lim);
+  // byte j of `even` holds element 2j in its low nibble, of `odd` element 2j+1
+  uint32_t even = 0, odd = 0;
+  cvt_sr_fp4_into<0>(even, w[0], nr[0], scale);
+  cvt_sr_fp4_into<1>(even, w[2], nr[2], scale);
+  cvt_sr_fp4_into<2>(even, w[4], nr[4], scale);
+  cvt_sr_fp4_into<3>(even, w[6], nr[6], scale);
+  cvt_sr_fp4_into<0>(odd, w[1], nr[1], scale);
+  cvt_sr_fp4_into<1>(odd, w[3], nr[3], scale);
+  cvt_sr_fp4_into<2>(odd, w[5], nr[5], scale);
+  cvt_sr_fp4_into<3>(odd, w[7], nr[7], scale);
+  return s.bad ? 0x77777777u : (even | (odd << 4));
 }
 
 // ------------------------------------------------------------------ memory
@@ -349,7 +360,7 @@ __device__ __forceinline__ void encode_store8(uint8_t* codes_row, uint32_t d, ui
                                               const SrStream& rng) {
   if (RND == MXQ_SR) {
     uint32_t r[8];
-    rng.words8(n, r);
+    rng.words8_not(n, r);
     if (ELEM == MXQ_E4M3)
       store8_stream(codes_row + d, encode8_e4m3_sr(y, code, r));
     else

@@ -40,11 +40,15 @@
  *  - element rounding: round to nearest, ties to even, saturating at the
  *    format's largest finite value; the sign of zero is kept.
  *  - stochastic rounding: with q the value in units of the local quantum,
- *    n = floor(q), f = q - n, round up iff r < floor(f * 2^32) for a 32-bit
- *    random word r; saturating; r comes from Philox4x32-10 (Salmon, Moraes,
- *    Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) keyed
- *    by the 64-bit seed, counter (n>>2 as two words, offset as two words),
- *    word (n & 3), n = t*D + d the logical element index.
+ *    n = floor(q), f = q - n, round up iff the top B bits of a 32-bit random
+ *    word r are below the top B bits of f, i.e. r < 2^(32-B) * floor(f * 2^B),
+ *    where B = 23 - (stored mantissa bits) is the number of fp32 mantissa bits
+ *    the format drops at a normal target (20 for E4M3, 22 for E2M1);
+ *    saturating; r comes from Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ *    "Parallel random numbers: as easy as 1, 2, 3", SC'11) keyed by the
+ *    64-bit seed, counter (n>>2 as two words, offset as two words), word
+ *    (n & 3), n = t*D + d the logical element index. P(up) is f to within
+ *    2^-B: unbiased to that precision.
  *  - MXNorm divides by G itself (no c(p,B) correction) and has no epsilon;
  *    G == 0 gives a zero normaliser; a row holding a NaN or Inf gives a NaN
  *    normaliser.
@@ -170,7 +174,8 @@ static uint8_t magnitude_bits(const fmt_t* F, double mag) {
 
 /* Encode a finite value already divided by the block scale.
  * RNE: nearest on the format grid, ties to the even code, saturating.
- * SR : round up iff r < floor(f * 2^32), saturating. */
+ * SR : round up iff r < 2^(32-B) * floor(f * 2^B), B = 23 - mbits (the top B
+ *      bits of r against the top B bits of the fraction), saturating. */
 static uint8_t encode_value(const fmt_t* F, int rnd, double v, uint32_t r) {
   uint8_t sign = signbit(v) ? (uint8_t)(1 << (F->ebits + F->mbits)) : 0;
   double a = fabs(v);
@@ -185,7 +190,8 @@ static uint8_t encode_value(const fmt_t* F, int rnd, double v, uint32_t r) {
     double q = ldexp(a, -qe);
     double n = floor(q);
     double f = q - n;
-    double thr = floor(ldexp(f, 32)); /* exact: f has at most 53 significant bits */
+    int B = 23 - F->mbits;
+    double thr = ldexp(floor(ldexp(f, B)), 32 - B); /* exact: power-of-two scalings */
     int up = (double)r < thr;
     mag = ldexp(n + up, qe);
   }

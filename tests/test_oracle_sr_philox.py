@@ -152,3 +152,95 @@ def test_sr_saturates(orc):
     assert (got == 0x7E).all()
     got = orc.encode_array("e2m1", "sr", np.full(3, -7.5), r)
     assert (got == 0xF).all()
+
+
+# ---------------------------------------------------------------- the B-bit decision, exactly
+
+def _e2m1_table():
+    path = os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.txt")
+    tab = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            c, v = line.split()
+            tab[int(c, 0)] = float(v)
+    return np.array([tab[c] for c in range(16)])
+
+
+def _sr_by_definition(elem, v, r, table):
+    """Stochastic rounding written out with exact rationals: q = |v| in units of
+    the local quantum (binade of |v|, at least the smallest normal), n = floor(q),
+    f = q - n; round up iff r < 2^(32-B) * floor(f * 2^B), B the fp32 mantissa
+    bits the format drops (20 for E4M3, 22 for E2M1); saturate at the largest
+    value; then the code whose table value is the result, with v's sign."""
+    from fractions import Fraction
+    mbits, emin, maxval = (3, -6, 448.0) if elem == "e4m3" else (1, 0, 6.0)
+    B = 23 - mbits
+    a = Fraction(abs(v))
+    neg = np.signbit(v)
+    if a == 0:
+        mag = Fraction(0)
+    else:
+        e = a.numerator.bit_length() - a.denominator.bit_length()
+        if Fraction(2) ** e > a:
+            e -= 1
+        e = max(e, emin)
+        quantum = Fraction(2) ** (e - mbits)
+        q = a / quantum
+        n = q.numerator // q.denominator
+        f = q - n
+        thr = (f * 2 ** B).numerator // (f * 2 ** B).denominator * 2 ** (32 - B)
+        mag = min((n + (1 if r < thr else 0)) * quantum, Fraction(maxval))
+    half = len(table) // 2
+    pos = [c for c in range(half) if table[c] == float(mag)]
+    assert len(pos) == 1, (v, mag)
+    return pos[0] | (half if neg else 0)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_sr_decision_is_the_b_bit_rule(orc, elem):
+    # random values over every binade that reaches subnormal targets and far
+    # below them, random words and words at the B-bit threshold +- 1 and +- one
+    # step of the dropped low bits
+    table = torch_e4m3_table() if elem == "e4m3" else _e2m1_table()
+    mbits, emin, top = (3, -6, 8) if elem == "e4m3" else (1, 0, 2)
+    B = 23 - mbits
+    rng = np.random.default_rng(31 if elem == "e4m3" else 32)
+    n = 3000
+    e = rng.integers(-40, top + 1, n)
+    v = np.ldexp(rng.uniform(1, 2, n), e).astype(np.float32).astype(np.float64)
+    v = np.minimum(v, 448.0 if elem == "e4m3" else 6.0) * np.where(rng.random(n) < 0.5, -1, 1)
+    a = np.abs(v)
+    ee = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1))), emin)
+    q = np.ldexp(a, (-(ee - mbits)).astype(np.int64))
+    thr = np.ldexp(np.floor(np.ldexp(q - np.floor(q), B)), 32 - B)
+    step = 2.0 ** (32 - B)
+    words = [rng.integers(0, 1 << 32, n, dtype=np.uint64)]
+    for d in (-step - 1, -1, 0, step - 1, step):
+        words.append(np.clip(thr + d, 0, 2 ** 32 - 1).astype(np.uint64))
+    for r in words:
+        r = r.astype(np.uint32)
+        got = orc.encode_array(elem, "sr", v, r)
+        want = [_sr_by_definition(elem, float(v[i]), int(r[i]), table) for i in range(n)]
+        assert (got == np.array(want)).all()
+
+
+def test_sr_b_bit_rule_differs_from_a_full_word_rule_only_below_the_dropped_bits(orc):
+    # Mutation guard on the rule itself: a value whose fraction (in units of the
+    # quantum) has bits only below the top B rounds down under the B-bit rule
+    # for every word, where a 32-bit comparison would round up for small words.
+    # A subnormal E4M3 target (quantum 2^-9) and an fp64 value at a normal one.
+    for v, lo, hi in ((2.0 ** -8 + 2.0 ** -30, 2.0 ** -8, 3 * 2.0 ** -9),
+                      (1.25 + 2.0 ** -30, 1.25, 1.375)):
+        quantum = hi - lo
+        f = (v - lo) / quantum                  # exact: power-of-two quantum
+        assert 0 < f < 2.0 ** -20
+        full = int(np.floor(np.ldexp(f, 32)))
+        assert full >= 1
+        r = np.array([0, full - 1, full, 0xFFFFFFFF], np.uint32)
+        got = orc.encode_array("e4m3", "sr", np.full(4, v), r)
+        assert (got == orc.encode("e4m3", "rne", lo)).all(), (v, got)
+    # and at a fraction with bits at the top B, the threshold is 2^12 floor(f 2^20)
+    v = 1.25 + 2.0 ** -20                   # f = 2^-17: floor(f 2^20) = 8
+    got = orc.encode_array("e4m3", "sr", np.full(2, v), np.array([8 * 4096 - 1, 8 * 4096], np.uint32))
+    assert list(got) == [orc.encode("e4m3", "rne", 1.375), orc.encode("e4m3", "rne", 1.25)]
