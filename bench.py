@@ -75,7 +75,8 @@ def time_graph(torch, launch, steps, warmup, per_graph=GRAPH_LEN):
     launch i) in a HIP graph and replay it, plus one graph of the remainder, so
     that exactly `steps` launches are timed: the whole-job rate of back-to-back
     steps without host launch cost. Returns seconds per step between two
-    synchronisations, HIP-event seconds per launch, and the launch count."""
+    synchronisations, HIP-event seconds per launch, the launch count, and a
+    description of the graphs replayed."""
     steps = max(1, steps)
     per = min(per_graph, steps)
     reps, rem = divmod(steps, per)
@@ -111,8 +112,11 @@ def time_graph(torch, launch, steps, warmup, per_graph=GRAPH_LEN):
     ev1.record(stream)
     torch.cuda.synchronize()
     n = reps * per + rem
+    how = f"hip graph of {per} back-to-back C-ABI calls replayed {reps} time(s)"
+    if rem:
+        how += f", then one graph of the remaining {rem}"
     # wall seconds per step, and HIP-event seconds per launch on the replay stream
-    return (time.perf_counter() - t0) / n, ev0.elapsed_time(ev1) * 1e-3 / n, n
+    return (time.perf_counter() - t0) / n, ev0.elapsed_time(ev1) * 1e-3 / n, n, how
 
 
 def time_launches(torch, launch, steps, warmup):
@@ -140,6 +144,96 @@ def time_launches(torch, launch, steps, warmup):
         "kernel_p10_s": per[len(per) // 10],
         "kernel_p90_s": per[(9 * len(per)) // 10],
     }
+
+
+def tiny_latency(torch, mxq, workloads, steps):
+    """The 64 x 256 workload (gamma = 1, p = 2, E4M3): a launch-bound call, so
+    its latency per call: back-to-back in a graph (device time per call), and
+    eager through the C ABI with an event pair around each call."""
+    import ctypes
+    x, g = workloads.make_inputs("tiny", device="cuda")
+    T, D = x.shape
+    c = torch.empty((T, D), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((T, D // 32), dtype=torch.uint8, device="cuda")
+    inv = torch.empty((T,), dtype=torch.float32, device="cuda")
+    lib = mxq.lib()
+    vp = ctypes.c_void_p
+    args = (vp(x.data_ptr()), D, vp(g.data_ptr()), T, D, ctypes.c_float(2.0), mxq.MXQ_E4M3,
+            mxq.MXQ_RNE, None, 0, vp(c.data_ptr()), vp(sc.data_ptr()), vp(inv.data_ptr()))
+
+    def launch(i):
+        st = lib.mxnorm_fwd(*args, vp(torch.cuda.current_stream().cuda_stream))
+        if st != mxq.MXQ_OK:
+            raise mxq.MxqError(st, "mxnorm_fwd")
+
+    n = max(100, steps)
+    graph = time_graph(torch, launch, n, 100)
+    eager = time_launches(torch, launch, n, 20)
+    return {"shape": [T, D], "graph_us_per_call": round(graph[1] * 1e6, 3),
+            "eager_event_pair_median_us": round(eager["kernel_median_s"] * 1e6, 3),
+            "eager_wall_us_per_call": round(eager["s_per_step"] * 1e6, 3),
+            "launch": graph[3]}
+
+
+def mxnormlinear(torch, mxq, workloads, xs, outs, ys, g, steps):
+    """MXNormLinear (the MXNorm page, section 2.3): the normalised activation's
+    MX output feeds the next projection, whose weight has the gain folded in
+    and is MX-cast along K. One step: the norm of one [T, D] activation plus
+    the MX GEMM against the QKV (N = 6144) or FFN-up (N = 14336) weight, with
+    MXNorm (p = 2) or with the two-pass RMSNorm -> MXCast, the gain folded into
+    the weight for both. The pages' layer-level figure covers a whole
+    transformer layer; this is the norm and one projection."""
+    import ctypes
+    lib = mxq.lib()
+    vp = ctypes.c_void_p
+    T, D = xs[0].shape
+    res = {}
+    for name, N in (("qkv", 6144), ("ffn_up", 14336)):
+        w = workloads.random_rows(N, D, seed=11, device="cuda", scale=0.02)
+        B, SB = mxq.mxcast((w.float() * g.float()[None, :]).to(torch.bfloat16))
+        C = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        del w
+
+        def gemm(k, stream):
+            st = lib.mx_gemm(vp(outs[k][0].data_ptr()), D, vp(outs[k][1].data_ptr()), D // 32,
+                             vp(B.data_ptr()), D, vp(SB.data_ptr()), D // 32, T, N, D,
+                             mxq.MXQ_E4M3, mxq.MXQ_E4M3, vp(C.data_ptr()), N, mxq.MXQ_OUT_BF16,
+                             stream)
+            if st != mxq.MXQ_OK:
+                raise mxq.MxqError(st, "mx_gemm")
+
+        def with_mxnorm(i):
+            k, stream = i % ROTATE, vp(torch.cuda.current_stream().cuda_stream)
+            st = lib.mxnorm_fwd(vp(xs[k].data_ptr()), D, None, T, D, ctypes.c_float(2.0),
+                                mxq.MXQ_E4M3, mxq.MXQ_RNE, None, 0, vp(outs[k][0].data_ptr()),
+                                vp(outs[k][1].data_ptr()), vp(outs[k][2].data_ptr()), stream)
+            if st != mxq.MXQ_OK:
+                raise mxq.MxqError(st, "mxnorm_fwd")
+            gemm(k, stream)
+
+        def with_two_pass(i):
+            k, stream = i % ROTATE, vp(torch.cuda.current_stream().cuda_stream)
+            st = lib.rmsnorm_mxcast_fwd(vp(xs[k].data_ptr()), D, None, T, D, ctypes.c_float(1e-5),
+                                        mxq.MXQ_E4M3, mxq.MXQ_RNE, None, 0, vp(ys[k].data_ptr()),
+                                        vp(outs[k][0].data_ptr()), vp(outs[k][1].data_ptr()),
+                                        vp(outs[k][2].data_ptr()), stream)
+            if st != mxq.MXQ_OK:
+                raise mxq.MxqError(st, "rmsnorm_mxcast_fwd")
+            gemm(k, stream)
+
+        def gemm_only(i):
+            gemm(i % ROTATE, vp(torch.cuda.current_stream().cuda_stream))
+
+        a = time_graph(torch, with_mxnorm, steps, 4, per_graph=20)[0]
+        b = time_graph(torch, with_two_pass, steps, 4, per_graph=20)[0]
+        gm = time_graph(torch, gemm_only, steps, 4, per_graph=20)[0]
+        res[name] = {"N": N, "mxnorm_then_gemm_us": round(a * 1e6, 2),
+                     "rmsnorm_mxcast_then_gemm_us": round(b * 1e6, 2),
+                     "gemm_alone_us": round(gm * 1e6, 2),
+                     "speedup": round(b / a, 4),
+                     "gemm_TFLOP/s": round(2.0 * T * N * D / gm / 1e12, 1)}
+        del B, SB, C
+    return res
 
 
 def cpu_baseline(x_cpu, g_cpu, T, D, min_seconds=10.0):
@@ -282,15 +376,17 @@ def main():
         dst[i % ROTATE].copy_(src[i % ROTATE])
 
     K, W = args.steps, args.warmup
-    step_s, launch_s, graph_steps = time_graph(torch, fused_raw(2.0), K, W)  # headline: p = 2
+    step_s, launch_s, graph_steps, graph_how = time_graph(torch, fused_raw(2.0), K, W)  # headline: p = 2
     main_t = time_launches(torch, fused_raw(2.0), K, W)              # per-launch kernel time
     eager_t = time_launches(torch, fused(2.0), K, W)                 # through the torch helper
-    p1_step_s, _, _ = time_graph(torch, fused_raw(1.0), K, W)
+    p1_step_s = time_graph(torch, fused_raw(1.0), K, W)[0]
     tp_t = time_launches(torch, two_pass_raw, K, W)
-    tp_step_s, _, _ = time_graph(torch, two_pass_raw, K, W)
+    tp_step_s = time_graph(torch, two_pass_raw, K, W)[0]
     tp_hot = time_launches(torch, two_pass_hot, K, W)
-    rs_step_s, _, _ = time_graph(torch, rms_fused_raw, K, W)
+    rs_step_s = time_graph(torch, rms_fused_raw, K, W)[0]
     cp_t = time_launches(torch, copy, K, W)
+    tiny = tiny_latency(torch, mxq, workloads, K)
+    linear = mxnormlinear(torch, mxq, workloads, xs, outs, ys, g, min(K, 40))
 
     nbytes = fused_bytes(T, D)
     value = nbytes / step_s / 1e9
@@ -313,7 +409,7 @@ def main():
                    "rounding": "rne", "gamma": True, "block": 32,
                    "algorithmic_bytes_per_step": nbytes, "rotating_buffer_sets": ROTATE},
         "rows_per_s": round(T / step_s, 1),
-        "launch": "hip graph of 100 back-to-back C-ABI calls (10 passes over the buffer sets), replayed",
+        "launch": graph_how + f" (call i uses buffer set i % {ROTATE})",
         "eager_python_ms_per_step": round(eager_t["s_per_step"] * 1e3, 6),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -327,10 +423,12 @@ def main():
             "launch_us": round(launch_s * 1e6, 3),
             "launch_timing": "HIP events on the replay stream bracketing the timed graph "
                              "replays, divided by the launches (back-to-back kernels)",
+            # eager launches bracketed one by one by an event pair on the launch
+            # stream: each figure includes the pair's own overhead (about 2 us)
             "per_launch_event_pair_mean_us": round(main_t["kernel_mean_s"] * 1e6, 3),
-            "kernel_median_us": round(main_t["kernel_median_s"] * 1e6, 3),
-            "kernel_p10_us": round(main_t["kernel_p10_s"] * 1e6, 3),
-            "kernel_p90_us": round(main_t["kernel_p90_s"] * 1e6, 3),
+            "per_launch_event_pair_median_us": round(main_t["kernel_median_s"] * 1e6, 3),
+            "per_launch_event_pair_p10_us": round(main_t["kernel_p10_s"] * 1e6, 3),
+            "per_launch_event_pair_p90_us": round(main_t["kernel_p90_s"] * 1e6, 3),
             "bytes_per_launch": nbytes,
         },
         "comparison": {
@@ -352,6 +450,11 @@ def main():
             },
             "d2d_copy_same_bytes": {"kernel_mean_us": round(cp_t["kernel_mean_s"] * 1e6, 3),
                                     "GB/s": round(2 * copy_n / cp_t["kernel_mean_s"] / 1e9, 2)},
+            "tiny_64x256_latency": tiny,
+            # context: the MXNorm page reports +1.3% for a whole Llama 3 8B layer
+            # in MXFP8 on GB200 (section 3.2); these steps are the norm and one
+            # projection on this GPU
+            "mxnormlinear_llama3_8b": linear,
         },
         "cpu_baseline": None,
     }

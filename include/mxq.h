@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 2
+#define MXQ_ABI_VERSION 3
 
 typedef enum {
   MXQ_OK = 0,
@@ -99,17 +99,20 @@ typedef struct {
   uint64_t offset;
 } mxq_rng;
 
-/* Forward flags. FORCE_REG / FORCE_LDS select the variant of the single-pass
- * entry points (0 = automatic by D). SCALE_CEIL, accepted by every forward
+/* Forward flags. FORCE_REG / FORCE_LDS / FORCE_SPLIT select the variant of the
+ * single-pass entry points (0 = automatic by D: split rows for D a multiple of
+ * 512 above 4096, otherwise one wavefront per row up to 8192 and LDS staging
+ * beyond; all variants give bit-identical results). SCALE_CEIL, accepted by every forward
  * entry point, replaces the OCP floor rule for the E8M0 block scale,
  * s = floor(log2 amax) - emax, by the round-up rule: the smallest s with
  * amax <= maxval * 2^s (maxval 448 for E4M3, 6 for E2M1), so no element of
  * the block saturates. The MXFP8 recipes page names a scale conversion of its
  * own without printing it; this is the reading that rounds the scale up. */
 enum {
-  MXQ_FLAG_FORCE_REG = 1u, /* row held in registers (D <= 8192)               */
-  MXQ_FLAG_FORCE_LDS = 2u, /* row staged in LDS (D <= MXQ_MAX_D)              */
-  MXQ_FLAG_SCALE_CEIL = 4u /* round-up E8M0 scale rule                        */
+  MXQ_FLAG_FORCE_REG = 1u,   /* row held in one wavefront's registers (D <= 8192) */
+  MXQ_FLAG_FORCE_LDS = 2u,   /* row staged in LDS (D <= MXQ_MAX_D)                */
+  MXQ_FLAG_SCALE_CEIL = 4u,  /* round-up E8M0 scale rule                          */
+  MXQ_FLAG_FORCE_SPLIT = 8u  /* row split over wavefronts' registers (D % 512 == 0) */
 };
 
 /* Largest D of the register-resident MXNorm path and of any path. */
@@ -123,12 +126,14 @@ enum {
  *   p        power of the mean: > 0, or +INFINITY for the block-max maximum.
  *   elem     MXQ_E4M3 (codes [T, D]) or MXQ_E2M1 (codes [T, D/2]).
  *   rnd      MXQ_RNE, or MXQ_SR with rng != NULL.
- *   flags    0, MXQ_FLAG_FORCE_REG or MXQ_FLAG_FORCE_LDS (both variants give
- *            bit-identical results), optionally or-ed with MXQ_FLAG_SCALE_CEIL.
+ *   flags    0 (automatic), or one of MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS,
+ *            MXQ_FLAG_FORCE_SPLIT (all variants give bit-identical results),
+ *            optionally or-ed with MXQ_FLAG_SCALE_CEIL.
  *   codes, scales  outputs; inv_norm [T] fp32 output, may be NULL.
  * Errors: NULL (x, codes, scales), SHAPE, ALIGN, ARG (p <= 0 or NaN, unknown
  * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large for the path,
- * T * D >= 2^40, or more than 2^31 - 1 workgroups of rows), HIP.
+ * FORCE_SPLIT with D not a multiple of 512, T * D >= 2^40, or more than
+ * 2^31 - 1 workgroups of rows), HIP.
  */
 mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
                       int64_t D, float p, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,

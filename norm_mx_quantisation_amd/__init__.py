@@ -24,10 +24,10 @@ LIB_PATH = os.path.join(PKG, "libmxq.so")
 MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_HIP = range(7)
 MXQ_E4M3, MXQ_E2M1 = 0, 1
 MXQ_RNE, MXQ_SR = 0, 1
-MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS, MXQ_FLAG_SCALE_CEIL = 1, 2, 4
+MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS, MXQ_FLAG_SCALE_CEIL, MXQ_FLAG_FORCE_SPLIT = 1, 2, 4, 8
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
            "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mxnorm_bwd_noalloc", "mx_gemm",

@@ -49,6 +49,14 @@ typedef short short2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ p-mean
 
+// Every kernel adds a row's statistic in one canonical order, whatever its
+// work layout: the row is cut into groups of kGroupChunks chunks (2048
+// elements); within a group each lane adds its chunks' terms in chunk order,
+// the group total is the sum over the quads (or the wave, for the RMS) of
+// those lane sums, and the group totals are added in group order. Register,
+// LDS and split-row kernels therefore produce the same bits.
+constexpr int kGroupChunks = 4;
+
 // Term of the power mean for one block maximum m (m >= 0).
 __device__ __forceinline__ float pmean_add(float s, float m, int pmode, float p) {
   if (pmode == P_ONE) return s + m;
@@ -56,35 +64,77 @@ __device__ __forceinline__ float pmean_add(float s, float m, int pmode, float p)
   return s + exp2f(p * log2f(m));  // m == 0 -> exp2(-inf) == 0
 }
 
-__device__ __forceinline__ float pmean_finish(float s, int pmode, float p, float K) {
-  float q = s / K;
+// (s / K)^(1/p). Kinv is 1/K when K is a power of two (then s * Kinv is s / K
+// exactly) and 0 otherwise.
+__device__ __forceinline__ float pmean_finish(float s, int pmode, float p, float K, float Kinv) {
+  const float q = Kinv != 0.0f ? s * Kinv : s / K;
   if (pmode == P_ONE) return q;
   if (pmode == P_TWO) return sqrtf(q);
   return exp2f(log2f(q) / p);
 }
 
-// Sum of the power-mean terms of this lane's chunks, in chunk order, of the
-// block maxima scaled by 2^shift. NCT > 0 gives a compile-time (unrolled)
-// chunk count, NCT == 0 the runtime count.
-template <int NCT, int PM, class BlockMax>
-__device__ __forceinline__ float lane_terms_p(int nchunks, BlockMax mb, int shift, float p) {
+// One lane's sum of the power-mean terms of chunks [c0, c1) in chunk order, of
+// the block maxima scaled by 2^shift (mb(c): the lane's quad's maximum of chunk
+// c as bf16 bits, 0 past the row end). UNROLL > 0: c1 - c0 <= UNROLL, unrolled.
+template <int UNROLL, int PM, class BlockMax>
+__device__ __forceinline__ float lane_terms_p(int c0, int c1, BlockMax mb, int shift, float p) {
   float s = 0.0f;
-  if constexpr (NCT > 0) {
+  if constexpr (UNROLL > 0) {
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), PM, p);
+    for (int k = 0; k < UNROLL; ++k)
+      if (c0 + k < c1) s = pmean_add(s, ldexpf(__uint_as_float(mb(c0 + k) << 16), shift), PM, p);
   } else {
-    for (int c = 0; c < nchunks; ++c)
-      s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), PM, p);
+    for (int c = c0; c < c1; ++c) s = pmean_add(s, ldexpf(__uint_as_float(mb(c) << 16), shift), PM, p);
   }
   return s;
 }
 
+// Group total of chunks [c0, c1) (one group): lane sums, then over the quads.
 // The power mode is tested once, outside the term loop.
+template <int UNROLL, class BlockMax>
+__device__ __forceinline__ float group_terms(int c0, int c1, BlockMax mb, int shift, int pmode,
+                                             float p) {
+  float t;
+  if (pmode == P_TWO)
+    t = lane_terms_p<UNROLL, P_TWO>(c0, c1, mb, shift, p);
+  else if (pmode == P_ONE)
+    t = lane_terms_p<UNROLL, P_ONE>(c0, c1, mb, shift, p);
+  else
+    t = lane_terms_p<UNROLL, P_GEN>(c0, c1, mb, shift, p);
+  return sum_over_quads(t);
+}
+
+// The canonical total over a whole row held by one wave (nchunks chunks; NCT > 0
+// a compile-time count, unrolled).
 template <int NCT, class BlockMax>
-__device__ __forceinline__ float lane_terms(int nchunks, BlockMax mb, int shift, int pmode, float p) {
-  if (pmode == P_TWO) return lane_terms_p<NCT, P_TWO>(nchunks, mb, shift, p);
-  if (pmode == P_ONE) return lane_terms_p<NCT, P_ONE>(nchunks, mb, shift, p);
-  return lane_terms_p<NCT, P_GEN>(nchunks, mb, shift, p);
+__device__ __forceinline__ float row_terms(int nchunks, BlockMax mb, int shift, int pmode, float p) {
+  float total = 0.0f;
+  if constexpr (NCT > 0) {
+#pragma unroll
+    for (int g0 = 0; g0 < NCT; g0 += kGroupChunks)
+      total += group_terms<kGroupChunks>(g0, min(g0 + kGroupChunks, NCT), mb, shift, pmode, p);
+  } else {
+    for (int g0 = 0; g0 < nchunks; g0 += kGroupChunks)
+      total += group_terms<kGroupChunks>(g0, min(g0 + kGroupChunks, nchunks), mb, shift, pmode, p);
+  }
+  return total;
+}
+
+// floor(log2) of a nonzero finite bf16 magnitude given as bits 0x0001 .. 0x7F7F:
+// the unbiased exponent, or for a subnormal the position of its leading
+// mantissa bit (value = mantissa * 2^-133).
+__device__ __forceinline__ int bf16_exponent(uint32_t m) {
+  const int ef = (int)(m >> 7);
+  return ef ? ef - 127 : -133 + (31 - __builtin_clz(m));
+}
+
+// Whether a row whose direct total is s is finished without the rescaled total
+// (p = inf never needs a total). For p = 1 and 2 a total inside [2^-96, 2^96]
+// always gives G >= 2^-106 (K <= 1024), so only other p compute G here.
+__device__ __forceinline__ bool direct_total_suffices(float s, int pmode, float p, float K,
+                                                      float Kinv) {
+  return pmode != P_INF && s >= 0x1p-96f && s <= 0x1p96f &&
+         (pmode == P_ONE || pmode == P_TWO || pmean_finish(s, pmode, p, K, Kinv) >= 0x1p-126f);
 }
 
 // A row's normaliser. The products v = x * gamma are multiplied by `apply`
@@ -103,38 +153,31 @@ struct Normaliser {
 
 __device__ __forceinline__ Normaliser plain_normaliser(float inv) { return {inv, inv, 1.0f}; }
 
-// Normaliser 1/G of a row from its block maxima (bf16 bit patterns, one per
-// chunk for this lane's quad, zero for blocks past the row end). lane_max()
-// gives this lane's maximum of the patterns. Terms are added chunk by chunk in
-// each lane, then over the quads; every variant uses exactly this order.
-// A sum inside [2^-96, 2^96] is finite and nonzero, so the row holds no NaN
-// or Inf (either would make the sum non-finite) and is not all zero; if G is
-// also a normal fp32 value, inv = 1/G. Otherwise the row maximum decides: NaN
-// or Inf in the row gives NaN, an all-zero row 0; else the maxima are rescaled
-// by 2^-E, E = floor(log2 of the row maximum) (exact also for bf16
-// subnormals), so the largest lies in [1, 2), and G = G' * 2^E. p = inf takes
-// this path always.
-template <int NCT, class BlockMax, class LaneMax>
-__device__ __forceinline__ Normaliser row_normaliser(int nchunks, BlockMax mb, LaneMax lane_max,
-                                                     int pmode, float p, float K) {
+// Normaliser 1/G of a row from its statistic. total(shift) gives the row's
+// canonical total of the terms of the block maxima scaled by 2^shift;
+// row_max() the row's largest block maximum as bf16 bits. A direct total
+// inside [2^-96, 2^96] is finite and nonzero, so the row holds no NaN or Inf
+// (either would make it non-finite) and is not all zero; if G is also a normal
+// fp32 value, inv = 1/G. Otherwise the row maximum decides: NaN or Inf in the
+// row gives NaN, an all-zero row 0; else the maxima are rescaled by 2^-E,
+// E = floor(log2 of the row maximum), so the largest lies in [1, 2), and
+// G = G' * 2^E. p = inf takes this path always.
+template <class Total, class RowMax>
+__device__ __forceinline__ Normaliser row_normaliser(Total total, RowMax row_max, int pmode, float p,
+                                                     float K, float Kinv) {
   if (pmode != P_INF) {
-    const float s = sum_over_quads(lane_terms<NCT>(nchunks, mb, 0, pmode, p));
+    const float s = total(0);
     if (s >= 0x1p-96f && s <= 0x1p96f) {
-      const float G = pmean_finish(s, pmode, p, K);
+      const float G = pmean_finish(s, pmode, p, K, Kinv);
       if (G >= 0x1p-126f) return plain_normaliser(1.0f / G);
     }
   }
-  const uint32_t rmax = max_over_quads(lane_max());
+  const uint32_t rmax = row_max();
   if (rmax >= 0x7F80u) return plain_normaliser(__builtin_nanf(""));  // the row holds NaN or Inf
   if (rmax == 0u) return plain_normaliser(0.0f);                      // all-zero row
-  // bf16 bits 0x0001 .. 0x7F7F: the biased exponent, or for a subnormal the
-  // position of its leading mantissa bit (value = mantissa * 2^-133)
-  const int ef = (int)(rmax >> 7);
-  const int E = ef ? ef - 127 : -133 + (31 - __builtin_clz(rmax));
-  const float Gs = (pmode == P_INF)
-                       ? ldexpf(__uint_as_float(rmax << 16), -E)
-                       : pmean_finish(sum_over_quads(lane_terms<NCT>(nchunks, mb, -E, pmode, p)),
-                                      pmode, p, K);
+  const int E = bf16_exponent(rmax);
+  const float Gs = (pmode == P_INF) ? ldexpf(__uint_as_float(rmax << 16), -E)
+                                    : pmean_finish(total(-E), pmode, p, K, Kinv);
   const float G = ldexpf(Gs, E);
   if (G >= 0x1p-126f) return plain_normaliser(1.0f / G);
   // G below the normal range: scale RN32(1/G') instead of forming a subnormal G
@@ -142,6 +185,44 @@ __device__ __forceinline__ Normaliser row_normaliser(int nchunks, BlockMax mb, L
   const float inv = ldexpf(r, -E);  // exact, or +Inf past the fp32 range
   if (inv <= 0x1.fffffep127f) return plain_normaliser(inv);
   return {inv, ldexpf(r, -E - 64), 0x1p64f};
+}
+
+// ------------------------------------------------------------------ RMS
+
+// The RMS statistic's group total of chunks [c0, c1): each lane adds the
+// squares of its chunks in chunk order, then the wave adds the lane sums.
+template <int UNROLL, class Chunk>
+__device__ __forceinline__ float group_sumsq(int c0, int c1, Chunk chunk) {
+  float s = 0.0f;
+  if constexpr (UNROLL > 0) {
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k)
+      if (c0 + k < c1) s = chunk(c0 + k, s);
+  } else {
+    for (int c = c0; c < c1; ++c) s = chunk(c, s);
+  }
+  return sum_over_wave(s);
+}
+
+// The canonical sum of squares of a row held by one wave. chunk(c, s) adds
+// chunk c's squares (zero for lanes past the row end) to the lane sum s.
+template <int NCT, class Chunk>
+__device__ __forceinline__ float row_sumsq(int nchunks, Chunk chunk) {
+  float total = 0.0f;
+  if constexpr (NCT > 0) {
+#pragma unroll
+    for (int g0 = 0; g0 < NCT; g0 += kGroupChunks)
+      total += group_sumsq<kGroupChunks>(g0, min(g0 + kGroupChunks, NCT), chunk);
+  } else {
+    for (int g0 = 0; g0 < nchunks; g0 += kGroupChunks)
+      total += group_sumsq<kGroupChunks>(g0, min(g0 + kGroupChunks, nchunks), chunk);
+  }
+  return total;
+}
+
+// RMSNorm's normaliser from the canonical sum of squares.
+__device__ __forceinline__ float rms_inv(float total, float Df, float eps) {
+  return 1.0f / sqrtf(total / Df + eps);
 }
 
 // ------------------------------------------------------------------ scales
@@ -229,8 +310,8 @@ struct SrStream {
 
 // 8 values y (not yet divided by the scale) -> 8 E4M3 codes, RNE, saturating.
 // A non-finite block is encoded like any other (its scale and limit are then
-// meaningless values that fault nothing) and its codes are replaced by NaN
-// with a select, so the common path has no branch.
+// meaningless values that fault nothing) and its codes are then replaced by
+// NaN, behind a branch that a wavefront with no such block skips.
 __device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], BlockScale s) {
   const uint32_t code = s.code;
   const bool bad = s.bad;
@@ -246,8 +327,12 @@ __device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], BlockScale s
   a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, w[2], w[3], scale, true);
   b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[4], w[5], scale, false);
   b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(b, w[6], w[7], scale, true);
-  const uint32_t lo = __builtin_bit_cast(uint32_t, a), hi = __builtin_bit_cast(uint32_t, b);
-  return make_uint2(bad ? 0x7F7F7F7Fu : lo, bad ? 0x7F7F7F7Fu : hi);
+  uint32_t lo = __builtin_bit_cast(uint32_t, a), hi = __builtin_bit_cast(uint32_t, b);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {  // a rare, wavefront-uniform branch
+    lo = bad ? 0x7F7F7F7Fu : lo;
+    hi = bad ? 0x7F7F7F7Fu : hi;
+  }
+  return make_uint2(lo, hi);
 }
 
 // 8 values -> 8 E2M1 codes packed in one word (element 2j in the low nibble).
@@ -259,7 +344,8 @@ __device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], BlockScal
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[2], y[3], scale, 1);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[4], y[5], scale, 2);
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[6], y[7], scale, 3);
-  return bad ? 0x77777777u : q;
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) q = bad ? 0x77777777u : q;
+  return q;
 }
 
 // Stochastic rounding: with q = |y| / 2^s in units of the local quantum,
@@ -417,6 +503,7 @@ struct NormArgs {
   int D;
   int K;
   float Kf;
+  float Kinv;  // 1/K when K is a power of two, else 0
   float p;
   int pmode;
   float Df;    // D, for the RMS statistic
@@ -428,12 +515,11 @@ struct NormArgs {
 
 // How the block maximum of |x * gamma| is taken:
 //   G_NONE  no gamma: the block maximum of |x| is reused (rounding is monotone);
-//   G_GAIN  gains: fp32 max with abs modifiers over the products. A NaN
-//           product can only come from a non-finite gain (a non-finite x
-//           already makes the row's normaliser NaN), and the staging of the
-//           gains turns every lane-group of 8 gains holding a NaN or Inf into
-//           8 NaNs, so that group's products are all NaN, the fp32 max is NaN
-//           and the block is flagged non-finite, as it must be.
+//   G_GAIN  gains: the IEEE-2019 maximum (gfx950 v_maximum3_f32, which returns
+//           NaN when any input is NaN) with abs modifiers over the products, so
+//           a product made NaN or Inf by a non-finite gain (a non-finite x
+//           already makes the row's normaliser NaN) flags its block
+//           non-finite, as it must.
 enum GMode { G_NONE = 0, G_GAIN = 1 };
 
 // First half of a chunk, needing no normaliser: v = x * gamma (exact: two
@@ -446,11 +532,12 @@ __device__ __forceinline__ uint32_t chunk_products(const uint4& xb, const float 
   if (GM == G_NONE) return mbits << 16;
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = v[j] * g[j];
-  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-  m = fmaxf(fmaxf(m, fabsf(v[3])), fabsf(v[4]));
-  m = fmaxf(fmaxf(m, fabsf(v[5])), fabsf(v[6]));
-  m = fmaxf(m, fabsf(v[7]));
-  // integer max of non-negative floats: NaN bits exceed every other value
+  auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  float m = mx(mx(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  m = mx(mx(m, fabsf(v[3])), fabsf(v[4]));
+  m = mx(mx(m, fabsf(v[5])), fabsf(v[6]));
+  m = mx(m, fabsf(v[7]));
+  // integer max of non-negative floats (or NaN): NaN bits exceed every other value
   return quad_max_u32(__float_as_uint(m));
 }
 
@@ -490,25 +577,6 @@ __device__ __forceinline__ uint32_t mxnorm_chunk(const NormArgs& A, uint8_t* cod
   return chunk_finish<ELEM, RND>(A, codes_row, nrow, d, v, vm, N);
 }
 
-// 8 bf16 quiet NaNs.
-__device__ __forceinline__ uint4 nan_group() {
-  return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-}
-
-// Whether any of 8 bf16 values is NaN or Inf (exponent field all ones): the
-// exponent fields alone, as 16-bit lanes, reach their largest value 0x7F80
-// exactly then.
-__device__ __forceinline__ bool nonfinite_bf16x8(const uint4& r) {
-  const uint32_t k = 0x7F807F80u;
-  const u16x2 a = __builtin_bit_cast(u16x2, r.x & k), b = __builtin_bit_cast(u16x2, r.y & k);
-  const u16x2 c = __builtin_bit_cast(u16x2, r.z & k), d = __builtin_bit_cast(u16x2, r.w & k);
-  const uint32_t m = __builtin_bit_cast(
-      uint32_t, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                          __builtin_elementwise_max(c, d)));
-  const u16x2 h = __builtin_bit_cast(u16x2, m);
-  return __builtin_elementwise_max(h.x, h.y) == 0x7F80u;
-}
-
 // gamma [D] goes to LDS as fp32, laid out [chunk][half][lane] (float4 each),
 // so each lane reads its 8 gains of a chunk as two conflict-free 16-byte LDS
 // reads. Staging is split in two: the global loads are issued first, ahead of
@@ -527,21 +595,16 @@ struct GammaStage {
     for (int k = 0; k < kItems; ++k) r[k] = g.load8(((int)threadIdx.x + k * NT) * 8);
   }
 
-  // Writes the gains to LDS (a group of 8 holding a NaN or Inf becomes 8
-  // NaNs, see G_GAIN; the replacement is skipped by the whole wavefront when
-  // none of its groups needs it) and waits for the whole workgroup. Items
-  // past the row end read zeros; the chunks they belong to are never
-  // encoded, so their gains are never read.
+  // Writes the gains to LDS and waits for the whole workgroup. Items past the
+  // row end read zeros; the chunks they belong to are never encoded, so their
+  // gains are never read.
   __device__ __forceinline__ void store(float4* g_lds) {
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
       const int i = (int)threadIdx.x + k * NT;
       if (i < NC * kWave) {
-        uint4 q = r[k];
-        const bool bad = nonfinite_bf16x8(q);
-        if (__builtin_amdgcn_ballot_w64(bad) != 0) q = bad ? nan_group() : q;
         float v[8];
-        unpack8(q, v);
+        unpack8(r[k], v);
         const int c = i / kWave, l = i % kWave;
         g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
         g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
@@ -560,28 +623,31 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
                                                const float4* g_lds, int64_t row, int lane,
                                                uint32_t* sc) {
   const int dl = lane * 8;
+  // chunks 0 .. NC-2 are whole (NC = ceil(D / 512)); only the last can end
+  // inside the row, and its lanes past the end are masked
+  const bool last_in = (NC - 1) * kChunk + dl < A.D;
   uint32_t mb[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    // every lane computes (the loads are clamped in bounds), then masks: no branch
-    const uint32_t valid = 0u - (uint32_t)(c * kChunk + dl < A.D);
-    mb[c] = quad_max_u32(absmax_bits8(raw[c]) & valid);
+    const uint32_t m = absmax_bits8(raw[c]);
+    mb[c] = quad_max_u32(c < NC - 1 ? m : (last_in ? m : 0u));
   }
   Normaliser N;
   if constexpr (STAT == S_RMS) {
-    float s = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
-    N = plain_normaliser(rms_normaliser(s, A.Df, A.eps));
+    const float s = row_sumsq<NC>(NC, [&](int c, float t) {
+      return (c < NC - 1 || last_in) ? sumsq8(raw[c], t) : t;
+    });
+    N = plain_normaliser(rms_inv(s, A.Df, A.eps));
   } else {
-    auto lane_max = [&]() {
+    auto mbf = [&](int c) { return mb[c]; };
+    auto row_max = [&]() {
       uint32_t m = 0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) m = max(m, mb[c]);
-      return m;
+      return max_over_quads(m);
     };
-    N = row_normaliser<NC>(NC, [&](int c) { return mb[c]; }, lane_max, A.pmode, A.p, A.Kf);
+    N = row_normaliser([&](int shift) { return row_terms<NC>(NC, mbf, shift, A.pmode, A.p); },
+                       row_max, A.pmode, A.p, A.Kf, A.Kinv);
   }
   if (lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
   // The empty asm claims to rewrite the packed row, so the compiler widens
@@ -597,7 +663,7 @@ __device__ __forceinline__ void mxnorm_row_reg(const NormArgs& A, uint4 (&raw)[N
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int d = c * kChunk + dl;
-    if (d < A.D) {
+    if (c < NC - 1 || last_in) {
       if (GM != G_NONE) gains(g_lds, c, lane, g);
       const uint32_t code = mxnorm_chunk<ELEM, RND, GM>(A, crow, nrow, d, raw[c], g, mb[c], N);
       // block d / 32 = 16 c + lane / 4: the chunk's part is an immediate offset
@@ -626,7 +692,8 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
   __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
   uint4 raw[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
+  for (int c = 0; c < NC - 1; ++c) raw[c] = load16_stream(xr + c * kChunk + dl);
+  raw[NC - 1] = load_chunk(xr, NC - 1, dl, A.D);  // the only chunk that can pass the row end
   __builtin_amdgcn_sched_barrier(0);
   if (GAMMA) gs.store(g_lds);  // the row loads stay in flight meanwhile
   if (!live) return;
@@ -635,6 +702,176 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
     mxnorm_row_reg<NC, ELEM, RND, G_NONE, STAT>(A, raw, g_lds, row, lane, sc);
   else
     mxnorm_row_reg<NC, ELEM, RND, G_GAIN, STAT>(A, raw, g_lds, row, lane, sc);
+}
+
+// ------------------------------------------------------------------ split rows
+
+constexpr int kSplitMaxWaves = 16;  // wavefronts per workgroup of the split-row kernel
+
+// A row split over W wavefronts: wave w holds chunks [w CPW, w CPW + CPW) of
+// the row in VGPRs, and R rows share a workgroup (R = 1 unless GLDS). Rows are
+// a whole number of chunks (D % 512 == 0). When the row's chunk count is not a
+// multiple of CPW, the last wave's surplus slots hold copies of the row's last
+// chunk: they are left out of the statistic, and they encode to the same codes
+// the real last chunk does (same data, gains, scale and random words), which
+// are written to the same place again; so the code has no chunk tests at all.
+// Each wave adds its groups' terms (CPW / kGroupChunks groups) in the canonical
+// order; the group totals meet in LDS and every wave of the row adds all of
+// them in group order, so the statistic has exactly the bits of the one-wave
+// kernels. Every wave then encodes its own chunks: the work after the row's
+// last byte arrives is spread over W wavefronts (and so over the CU's SIMDs)
+// instead of one. GLDS: the gains are staged once per workgroup in LDS as bf16
+// by direct-to-LDS loads and shared by the R rows; otherwise each wave loads
+// its own CPW chunks of gains into VGPRs ahead of its row loads.
+template <int CPW, bool GLDS, int ELEM, int RND, bool GAMMA, int STAT>
+__global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(NormArgs A, int nchunks,
+                                                                              int W, int R) {
+  constexpr int GPW = CPW / kGroupChunks;  // groups per wave
+  extern __shared__ uint4 g_lds[];         // GLDS gains: [nchunks * 64] x 8 bf16
+  __shared__ __align__(16) float part[kSplitMaxWaves * GPW];
+  __shared__ __align__(16) float part2[kSplitMaxWaves * GPW];
+  __shared__ __align__(16) uint32_t pmax[kSplitMaxWaves];
+  __shared__ uint32_t sc_lds[kSplitMaxWaves][CPW * 4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+  int rw = 0;
+  if constexpr (GLDS)
+    while (wid >= (rw + 1) * W) ++rw;  // row of the workgroup (R <= 5: a few scalar steps)
+  const int w = wid - rw * W;
+  const int64_t row = (int64_t)blockIdx.x * R + rw;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
+  const int dl = lane * 8;
+  const int c0 = w * CPW;
+  const int ncw = min(CPW, nchunks - c0);  // this wave's real chunks, >= 1
+  // Chunk slot c of this wave is row chunk min(c0 + c, nchunks - 1); loads are
+  // unconditional (a predicated load makes the compiler wait for the loads
+  // before it).
+  auto chunk_of = [&](int c) { return min(c0 + c, nchunks - 1); };
+
+  uint4 graw[GLDS ? 1 : CPW];
+  if (GAMMA) {
+    if constexpr (GLDS) {
+      for (int i = wid; i < nchunks; i += R * W)
+        __builtin_amdgcn_global_load_lds((const void*)(A.gamma + i * kChunk + dl),
+                                         (lds_void*)(g_lds + i * kWave), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) graw[c] = load16(A.gamma + chunk_of(c) * kChunk + dl);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
+  uint4 raw[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) raw[c] = load16_stream(xr + chunk_of(c) * kChunk + dl);
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint32_t mb[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) mb[c] = quad_max_u32(absmax_bits8(raw[c]));
+  auto mb_stat = [&](int c) { return c < ncw ? mb[c] : 0u; };  // surplus slots add nothing
+  auto wave_groups = [&](float* dst, int shift) {  // this wave's group totals -> dst
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      float t;
+      if constexpr (STAT == S_RMS)
+        t = group_sumsq<kGroupChunks>(j * kGroupChunks, j * kGroupChunks + kGroupChunks,
+                                      [&](int c, float u) { return c < ncw ? sumsq8(raw[c], u) : u; });
+      else
+        t = group_terms<kGroupChunks>(j * kGroupChunks, j * kGroupChunks + kGroupChunks, mb_stat,
+                                      shift, A.pmode, A.p);
+      if (lane == 0) dst[wid * GPW + j] = t;  // a group past the row end is never read
+    }
+  };
+  if (STAT == S_RMS || A.pmode != P_INF) wave_groups(part, 0);
+  if (STAT == S_PMEAN) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) m = max(m, mb[c]);  // copies of the last chunk change no maximum
+    m = max_over_quads(m);
+    if (lane == 0) pmax[wid] = m;
+  }
+  if (GLDS && GAMMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the gains' direct-to-LDS loads
+  __syncthreads();
+
+  const int ng = (nchunks + kGroupChunks - 1) / kGroupChunks;  // groups in a row
+  auto row_total = [&](const float* src, int r) {
+    float t = 0.0f;
+    if constexpr (!GLDS) {  // one row, at most 4 groups: one 16-byte LDS read
+      const float4 q = *reinterpret_cast<const float4*>(src);
+      t = q.x;
+      if (ng > 1) t += q.y;
+      if (ng > 2) t += q.z;
+      if (ng > 3) t += q.w;
+    } else {
+      for (int k = 0; k < ng; ++k) t += src[r * W * GPW + k];
+    }
+    return t;
+  };
+  auto row_max = [&](int r) {
+    uint32_t m = 0;
+    if constexpr (!GLDS) {
+      const uint4 q = *reinterpret_cast<const uint4*>(pmax);
+      m = q.x;
+      if (W > 1) m = max(m, q.y);
+      if (W > 2) m = max(m, q.z);
+      if (W > 3) m = max(m, q.w);
+    } else {
+      for (int j = 0; j < W; ++j) m = max(m, pmax[r * W + j]);
+    }
+    return m;
+  };
+  Normaliser N;
+  if constexpr (STAT == S_RMS) {
+    N = plain_normaliser(rms_inv(row_total(part, rw), A.Df, A.eps));
+  } else {
+    const bool pinf = A.pmode == P_INF;
+    const float s = pinf ? 0.0f : row_total(part, rw);
+    const uint32_t rmax = row_max(rw);
+    // the rescaled totals, when any row of the workgroup needs them (a
+    // workgroup-uniform decision, so every wave reaches the same barriers)
+    bool any = !pinf && rmax != 0u && rmax < 0x7F80u &&
+               !direct_total_suffices(s, A.pmode, A.p, A.Kf, A.Kinv);
+    if constexpr (GLDS) {  // the other rows of the workgroup
+      for (int r = 0; r < R; ++r) {
+        const uint32_t mr = row_max(r);
+        any |= r != rw && !pinf && mr != 0u && mr < 0x7F80u &&
+               !direct_total_suffices(row_total(part, r), A.pmode, A.p, A.Kf, A.Kinv);
+      }
+    }
+    float s2 = 0.0f;
+    if (any) {
+      wave_groups(part2, (rmax != 0u && rmax < 0x7F80u) ? -bf16_exponent(rmax) : 0);
+      __syncthreads();
+      s2 = row_total(part2, rw);
+    }
+    N = row_normaliser([&](int shift) { return shift == 0 ? s : s2; }, [&]() { return rmax; },
+                       A.pmode, A.p, A.Kf, A.Kinv);
+  }
+  if (!live) return;
+  if (w == 0 && lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)  // widen each chunk where it is used (see mxnorm_row_reg)
+    asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
+
+  const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
+  uint8_t* crow = code_row<ELEM>(A.codes, nrow);
+  uint32_t* sc = sc_lds[wid];
+  float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int d = chunk_of(c) * kChunk + dl;
+    uint32_t code;
+    if (!GAMMA) {
+      code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, raw[c], g, mb[c], N);
+    } else {
+      unpack8(GLDS ? g_lds[chunk_of(c) * kWave + lane] : graw[c], g);
+      code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, raw[c], g, 0u, N);
+    }
+    if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);  // surplus slots: not flushed
+  }
+  flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K + (uint64_t)(c0 * 16), ncw * 16,
+               A.sc_vec != 0, lane);
 }
 
 constexpr int kMaxLdsRows = 16;  // wavefronts (rows) per workgroup of the LDS-staged variant
@@ -664,7 +901,7 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
   if (GAMMA) {
     for (int i = threadIdx.x; i < nchunks * kWave; i += rows * kWave) {
       const uint4 r = (i * 8 < A.D) ? load16(A.gamma + i * 8) : make_uint4(0, 0, 0, 0);
-      g_lds[i] = nonfinite_bf16x8(r) ? nan_group() : r;  // see G_GAIN
+      g_lds[i] = r;
     }
   }
   if (live) {
@@ -680,20 +917,20 @@ __global__ __launch_bounds__(kMaxLdsRows * kWave) void mxnorm_lds_kernel(NormArg
   if (!live) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // lanes past the row end hold zeros (above), which add nothing
   auto mb = [&](int c) { return quad_max_u32(absmax_bits8(slice[c * kWave + lane])); };
   Normaliser N;
   if constexpr (STAT == S_RMS) {
-    float s = 0.0f;
-    for (int c = 0; c < nchunks; ++c)
-      if (c * kChunk + dl < A.D) s = sumsq8(slice[c * kWave + lane], s);
-    N = plain_normaliser(rms_normaliser(s, A.Df, A.eps));
+    const float s = row_sumsq<0>(nchunks, [&](int c, float t) { return sumsq8(slice[c * kWave + lane], t); });
+    N = plain_normaliser(rms_inv(s, A.Df, A.eps));
   } else {
-    auto lane_max = [&]() {
+    auto row_max = [&]() {
       uint32_t m = 0;
       for (int c = 0; c < nchunks; ++c) m = max(m, mb(c));
-      return m;
+      return max_over_quads(m);
     };
-    N = row_normaliser<0>(nchunks, mb, lane_max, A.pmode, A.p, A.Kf);
+    N = row_normaliser([&](int shift) { return row_terms<0>(nchunks, mb, shift, A.pmode, A.p); },
+                       row_max, A.pmode, A.p, A.Kf, A.Kinv);
   }
   if (lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
 
@@ -764,11 +1001,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
   uint4 raw[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (c * kChunk + dl < A.D) s = sumsq8(raw[c], s);
-  const float inv = rms_normaliser(s, A.Df, A.eps);
+  const float s = row_sumsq<NC>(NC, [&](int c, float t) {
+    return c * kChunk + dl < A.D ? sumsq8(raw[c], t) : t;
+  });
+  const float inv = rms_inv(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -785,10 +1021,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_wide_kernel(RmsArgs A, int n
   if (row >= A.T) return;
   const uint16_t* xr = A.x + row * A.ldx;
   const int dl = lane * 8;
-  float s = 0.0f;
-  for (int c = 0; c < nchunks; ++c)
-    if (c * kChunk + dl < A.D) s = sumsq8(load16(xr + c * kChunk + dl), s);
-  const float inv = rms_normaliser(s, A.Df, A.eps);
+  const float s = row_sumsq<0>(nchunks, [&](int c, float t) {
+    return c * kChunk + dl < A.D ? sumsq8(load16(xr + c * kChunk + dl), t) : t;
+  });
+  const float inv = rms_inv(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
   for (int c = 0; c < nchunks; ++c) {
     const int d = c * kChunk + dl;
@@ -924,23 +1160,55 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
   return MXQ_OK;
 }
 
+// Split rows: up to 16 chunks, 4 per wavefront with the gains in VGPRs and one
+// row (at most 4 wavefronts) per workgroup; longer rows 8 chunks per
+// wavefront with the gains shared in LDS by the rows of a workgroup of up to
+// 16 wavefronts.
+template <int CPW, bool GLDS, int ELEM, int RND, bool GAMMA, int STAT>
+mxq_status launch_mxnorm_split(const NormArgs& A, int nc, hipStream_t s) {
+  if (A.D % kChunk != 0) return MXQ_ERR_UNSUPPORTED;  // whole chunks only
+  const int W = (nc + CPW - 1) / CPW;
+  if (W > kSplitMaxWaves) return MXQ_ERR_UNSUPPORTED;
+  const int R = GLDS ? max(1, kSplitMaxWaves / W) : 1;
+  if ((A.T + R - 1) / R > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
+  const size_t lds = (GLDS && GAMMA) ? (size_t)nc * kWave * sizeof(uint4) : 0;
+  auto kern = mxnorm_split_kernel<CPW, GLDS, ELEM, RND, GAMMA, STAT>;
+  if (lds > 0 &&
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return MXQ_ERR_HIP;
+  const unsigned grid = (unsigned)((A.T + R - 1) / R);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * R * W), lds, s, A, nc, W, R);
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+enum Variant { V_REG = 0, V_LDS = 1, V_SPLIT = 2 };
+
 template <int ELEM, int RND, int STAT>
-mxq_status dispatch_mxnorm(const NormArgs& A, bool gamma, bool lds, int nc, hipStream_t s) {
-  if (lds)
+mxq_status dispatch_mxnorm(const NormArgs& A, bool gamma, int variant, int nc, hipStream_t s) {
+  if (variant == V_LDS)
     return gamma ? launch_mxnorm_lds<ELEM, RND, true, STAT>(A, nc, s)
                  : launch_mxnorm_lds<ELEM, RND, false, STAT>(A, nc, s);
+  if (variant == V_SPLIT) {
+    if (nc <= 4 * kGroupChunks)
+      return gamma ? launch_mxnorm_split<4, false, ELEM, RND, true, STAT>(A, nc, s)
+                   : launch_mxnorm_split<4, false, ELEM, RND, false, STAT>(A, nc, s);
+    return gamma ? launch_mxnorm_split<8, true, ELEM, RND, true, STAT>(A, nc, s)
+                 : launch_mxnorm_split<8, true, ELEM, RND, false, STAT>(A, nc, s);
+  }
   return gamma ? dispatch_mxnorm_reg<ELEM, RND, true, STAT>(A, nc, s)
                : dispatch_mxnorm_reg<ELEM, RND, false, STAT>(A, nc, s);
 }
 
 template <int STAT>
 mxq_status dispatch_norm_cast(const NormArgs& A, mxq_elem elem, mxq_round rnd, bool gamma,
-                              bool lds, int nc, hipStream_t s) {
+                              int variant, int nc, hipStream_t s) {
   if (elem == MXQ_E4M3)
-    return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E4M3, MXQ_SR, STAT>(A, gamma, lds, nc, s)
-                         : dispatch_mxnorm<MXQ_E4M3, MXQ_RNE, STAT>(A, gamma, lds, nc, s);
-  return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E2M1, MXQ_SR, STAT>(A, gamma, lds, nc, s)
-                       : dispatch_mxnorm<MXQ_E2M1, MXQ_RNE, STAT>(A, gamma, lds, nc, s);
+    return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E4M3, MXQ_SR, STAT>(A, gamma, variant, nc, s)
+                         : dispatch_mxnorm<MXQ_E4M3, MXQ_RNE, STAT>(A, gamma, variant, nc, s);
+  return rnd == MXQ_SR ? dispatch_mxnorm<MXQ_E2M1, MXQ_SR, STAT>(A, gamma, variant, nc, s)
+                       : dispatch_mxnorm<MXQ_E2M1, MXQ_RNE, STAT>(A, gamma, variant, nc, s);
 }
 
 template <int NC, bool GAMMA>
@@ -1022,11 +1290,12 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
                      float p, float eps, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,
                      uint32_t flags, uint8_t* codes, uint8_t* scales, float* inv_out,
                      void* stream) {
-  if (flags & ~(uint32_t)(MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS | MXQ_FLAG_SCALE_CEIL))
-    return MXQ_ERR_ARG;
-  if ((flags & MXQ_FLAG_FORCE_REG) && (flags & MXQ_FLAG_FORCE_LDS)) return MXQ_ERR_ARG;
+  constexpr uint32_t kForce = MXQ_FLAG_FORCE_REG | MXQ_FLAG_FORCE_LDS | MXQ_FLAG_FORCE_SPLIT;
+  if (flags & ~(kForce | (uint32_t)MXQ_FLAG_SCALE_CEIL)) return MXQ_ERR_ARG;
+  if (__builtin_popcount(flags & kForce) > 1) return MXQ_ERR_ARG;
   if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
   if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
+  if ((flags & MXQ_FLAG_FORCE_SPLIT) && D % kChunk != 0) return MXQ_ERR_UNSUPPORTED;
   if (T == 0) return MXQ_OK;
   if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
   if (inv_out != nullptr && !aligned(inv_out, 4)) return MXQ_ERR_ALIGN;
@@ -1042,6 +1311,7 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   A.D = (int)D;
   A.K = (int)(D / 32);
   A.Kf = (float)(D / 32);
+  A.Kinv = ((D / 32) & (D / 32 - 1)) == 0 ? 1.0f / (float)(D / 32) : 0.0f;
   A.p = p;
   A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
   A.Df = (float)D;
@@ -1050,8 +1320,19 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   A.ceil_rule = (flags & MXQ_FLAG_SCALE_CEIL) != 0;
   A.rng = make_stream(rng);
   const int nc = (int)((D + kChunk - 1) / kChunk);
-  const bool lds = (flags & MXQ_FLAG_FORCE_LDS) || (!(flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG);
-  return dispatch_norm_cast<STAT>(A, elem, rnd, gamma != nullptr, lds, nc, (hipStream_t)stream);
+  // automatic: rows of whole chunks longer than 4096 elements split over
+  // several wavefronts; otherwise one wavefront per row up to 8192 elements,
+  // LDS staging beyond. At 4096 elements the two measure the same within a
+  // few percent either way over 2048..32768 rows; from 8192 the split rows
+  // are faster (shorter per-wave work after the row lands, fewer VGPRs)
+  const bool whole = D % kChunk == 0;
+  const int variant = (flags & MXQ_FLAG_FORCE_LDS)       ? V_LDS
+                      : (flags & MXQ_FLAG_FORCE_REG)     ? V_REG
+                      : (flags & MXQ_FLAG_FORCE_SPLIT)   ? V_SPLIT
+                      : (whole && nc > 2 * kGroupChunks) ? V_SPLIT
+                      : D > MXQ_MAX_D_REG                ? V_LDS
+                                                         : V_REG;
+  return dispatch_norm_cast<STAT>(A, elem, rnd, gamma != nullptr, variant, nc, (hipStream_t)stream);
 }
 
 }  // namespace

@@ -106,15 +106,6 @@ __device__ __forceinline__ float sumsq8(const uint4& r, float s) {
   return s;
 }
 
-// RMSNorm's normaliser 1 / sqrt(S / D + eps) from a lane's partial sum of
-// squares: the lanes' sums are added by the wave butterfly. Every RMS path
-// (two-pass and single-pass, register and LDS rows) sums in this order: each
-// lane its chunks in chunk order, then the butterfly, so all give the same bits.
-__device__ __forceinline__ float rms_normaliser(float lane_sum, float Df, float eps) {
-  const float s = sum_over_wave(lane_sum);
-  return 1.0f / sqrtf(s / Df + eps);
-}
-
 // ------------------------------------------------------------------ memory
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

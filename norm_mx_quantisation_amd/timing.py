@@ -26,6 +26,8 @@ HBM_PEAK_GBS = 8000.0
 # (case, workload, operation, options)
 CASES = (
     ("llama3_8b_preattn mxnorm p=2", "llama3_8b_preattn", "mxnorm", {"p": 2.0}),
+    ("llama3_8b_preattn mxnorm p=2 split rows", "llama3_8b_preattn", "mxnorm",
+     {"p": 2.0, "flags": mxq.MXQ_FLAG_FORCE_SPLIT}),
     # bytes-only reference kernels with the fused call's traffic and layout
     # (libmxq_floor.so): what moving these bytes alone reaches at this size,
     # then with the normaliser's row dependency and the gain staging added
@@ -43,14 +45,25 @@ CASES = (
      {"p": 2.0, "flags": mxq.MXQ_FLAG_SCALE_CEIL}),
     ("llama3_8b_preattn rms single-pass", "llama3_8b_preattn", "rms_fused", {}),
     ("llama3_8b_preattn two-pass", "llama3_8b_preattn", "two_pass", {}),
+    ("longseq_t3 mxnorm split rows", "longseq_t3", "mxnorm", {}),
     ("longseq_t3 mxnorm register rows", "longseq_t3", "mxnorm",
      {"flags": mxq.MXQ_FLAG_FORCE_REG}),
     ("longseq_t3 mxnorm LDS rows", "longseq_t3", "mxnorm", {"flags": mxq.MXQ_FLAG_FORCE_LDS}),
+    # rows wider than one wavefront's registers, N(0,1) with gains, 2^28 elements:
+    # the automatic (split-row) kernel and the LDS-staged one
+    ("wide D=16384 mxnorm split rows", "wide", "mxnorm", {"shape": (16384, 16384)}),
+    ("wide D=16384 mxnorm LDS rows", "wide", "mxnorm",
+     {"shape": (16384, 16384), "flags": mxq.MXQ_FLAG_FORCE_LDS}),
+    ("wide D=32768 mxnorm split rows", "wide", "mxnorm", {"shape": (8192, 32768)}),
+    ("wide D=32768 mxnorm LDS rows", "wide", "mxnorm",
+     {"shape": (8192, 32768), "flags": mxq.MXQ_FLAG_FORCE_LDS}),
     ("swiglu_downproj mxcast rne", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_RNE}),
     ("swiglu_downproj mxcast sr", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_SR}),
     ("swiglu_downproj mxcast rne round-up scales", "swiglu_downproj", "mxcast",
      {"rnd": mxq.MXQ_RNE, "flags": mxq.MXQ_FLAG_SCALE_CEIL}),
     ("mxfp4 mxnorm e2m1", "mxfp4", "mxnorm", {"elem": mxq.MXQ_E2M1}),
+    ("mxfp4 mxnorm e2m1 split rows", "mxfp4", "mxnorm",
+     {"elem": mxq.MXQ_E2M1, "flags": mxq.MXQ_FLAG_FORCE_SPLIT}),
     ("llama3_8b_preattn backward dx+dgamma", "llama3_8b_preattn", "backward", {}),
     ("llama3_8b_preattn backward dx only", "llama3_8b_preattn", "backward", {"dgamma": False}),
     ("mxfp4 backward dx+dgamma", "mxfp4", "backward", {}),
@@ -184,8 +197,12 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
         return run_gemm(torch, name, wl, opt, steps, warmup)
     if op == "libgemm":
         return run_libgemm(torch, name, wl, opt, steps, warmup)
-    w = workloads.WORKLOADS[wl]
-    x0, g = workloads.make_inputs(wl, device="cuda")
+    if "shape" in opt:
+        T, D = opt["shape"]
+        x0 = workloads.random_rows(T, D, seed=13, device="cuda")
+        g = workloads.random_gamma(D, seed=14, device="cuda")
+    else:
+        x0, g = workloads.make_inputs(wl, device="cuda")
     T, D = x0.shape
     if not opt.get("gamma", True):
         g = None

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_messages():
-    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 2
+    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 3
     for st in range(7):
         assert isinstance(mxq.mxq_strerror(st), str) and mxq.mxq_strerror(st)
     assert mxq.mxq_strerror(99) == "unknown status"
@@ -125,10 +125,15 @@ def test_mxnorm_argument_errors():
     assert norm(p=0.0) == mxq.MXQ_ERR_ARG
     assert norm(p=-1.0) == mxq.MXQ_ERR_ARG
     assert norm(p=float("nan")) == mxq.MXQ_ERR_ARG
-    assert norm(flags=3) == mxq.MXQ_ERR_ARG
-    assert norm(flags=8) == mxq.MXQ_ERR_ARG
+    assert norm(flags=3) == mxq.MXQ_ERR_ARG                      # two variants forced
+    assert norm(flags=mxq.MXQ_FLAG_FORCE_SPLIT | mxq.MXQ_FLAG_FORCE_LDS) == mxq.MXQ_ERR_ARG
+    assert norm(flags=mxq.MXQ_FLAG_FORCE_SPLIT | mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_ARG
+    assert norm(flags=16) == mxq.MXQ_ERR_ARG                     # unknown bit
     assert norm(flags=mxq.MXQ_FLAG_SCALE_CEIL | 3) == mxq.MXQ_ERR_ARG
     assert norm(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
+    # the split-row kernel takes rows of whole 512-element chunks only
+    assert norm(D=4128, ldx=4128, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
+    assert norm(D=256, ldx=256, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(gamma=A8) == mxq.MXQ_ERR_ALIGN
     assert norm(inv_norm=A16 + 2) == mxq.MXQ_ERR_ALIGN
@@ -140,6 +145,7 @@ def test_rms_fused_argument_errors():
     assert rms_fused(eps=float("inf")) == mxq.MXQ_ERR_ARG
     assert rms_fused(flags=3) == mxq.MXQ_ERR_ARG
     assert rms_fused(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
+    assert rms_fused(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
     assert rms_fused(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
     assert rms_fused(gamma=A8) == mxq.MXQ_ERR_ALIGN
     assert rms_fused(inv=A16 + 2) == mxq.MXQ_ERR_ALIGN
@@ -159,7 +165,8 @@ def test_cast_flags_take_only_the_scale_rule(call):
     # the two-pass path and the plain cast have no variants to force
     assert call(flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_ARG
     assert call(flags=mxq.MXQ_FLAG_FORCE_LDS) == mxq.MXQ_ERR_ARG
-    assert call(flags=mxq.MXQ_FLAG_SCALE_CEIL | 8) == mxq.MXQ_ERR_ARG
+    assert call(flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_ARG
+    assert call(flags=mxq.MXQ_FLAG_SCALE_CEIL | 16) == mxq.MXQ_ERR_ARG
     # the flag is validated after the shape: a bad shape still reports SHAPE
     assert call(D=0, flags=mxq.MXQ_FLAG_SCALE_CEIL) == mxq.MXQ_ERR_SHAPE
 

@@ -208,9 +208,12 @@ def test_mxnorm_strided_rows():
     assert np.array_equal(c1, np_(c2)) and np.array_equal(s1, np_(s2)) and np.array_equal(i1, np_(i2))
 
 
+@pytest.mark.parametrize("D", [512, 4096])
 @pytest.mark.parametrize("p", [1.0, 2.0, 3.5, math.inf])
-def test_mxnorm_special_rows(p):
-    D = 512
+def test_mxnorm_special_rows(p, D):
+    # D = 4096 runs the split-row kernel, two rows per workgroup: rows that
+    # need the rescaled statistic (4, 5, 6) share workgroups with rows that
+    # do not (7) and with NaN, Inf and zero rows
     x = workloads.random_rows(10, D, seed=77).clone()
     x[0] = 0.0
     x[0, 5] = -0.0
@@ -221,12 +224,18 @@ def test_mxnorm_special_rows(p):
     x[5] = x[5] * 1e30               # m^2 overflows fp32: rescaled sum
     x[6] = x[6] * 1e-30              # m^2 underflows fp32: rescaled sum
     x[7, :32] = 0.0                  # an all-zero block inside a normal row
-    x[8] = torch.where(x[8] > 0, 3.0, -3.0)   # constant magnitude: G == 3 for every p
+    # constant magnitude: G == 3 exactly for p = 1, 2, inf (the fp32 sums of 9s
+    # and 3s are exact). Every element then sits at y = +-1, an E8M0 boundary,
+    # so for p = 3.5, whose exp2/log2 terms add with rounding over four chunks
+    # per lane at D = 4096, the row takes one magnitude per block instead.
+    const = p != 3.5 or D == 512
+    mag = 3.0 if const else (torch.arange(D) // 32 % 3 + 1).float()
+    x[8] = torch.where(x[8] > 0, mag, -mag)
     xg = x.to(DEV)
     codes, scales, inv = check_mxnorm(xg, None, p, what=f"special p={p}")
     assert inv[0] == 0 and math.isnan(inv[1]) and math.isnan(inv[2]) and math.isnan(inv[3])
     assert (scales[1] == 255).all() and (codes[1] == 0x7F).all()
-    assert inv[8] == np.float32(1.0 / 3.0)
+    assert not const or inv[8] == np.float32(1.0 / 3.0)
     g = workloads.random_gamma(D, seed=78, device=DEV)
     check_mxnorm(xg, g, p, what=f"special gamma p={p}")
 
@@ -248,7 +257,22 @@ def _tiny_rows(D):
     return x.to(torch.bfloat16)          # row 5 stays N(0, 1)
 
 
-@pytest.mark.parametrize("flags", [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS])
+ALL_VARIANTS = [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS, mxq.MXQ_FLAG_FORCE_SPLIT]
+
+
+def variants_for(D):
+    """The forced variants that take rows of D elements: the one-wave kernel
+    up to MXQ_MAX_D_REG, the split-row kernel for whole 512-element chunks,
+    the LDS-staged kernel always."""
+    v = [mxq.MXQ_FLAG_FORCE_LDS]
+    if D <= mxq.MXQ_MAX_D_REG:
+        v.append(mxq.MXQ_FLAG_FORCE_REG)
+    if D % 512 == 0:
+        v.append(mxq.MXQ_FLAG_FORCE_SPLIT)
+    return v
+
+
+@pytest.mark.parametrize("flags", ALL_VARIANTS)
 @pytest.mark.parametrize("p", [1.0, 2.0, 3.5, math.inf])
 def test_mxnorm_normaliser_past_fp32_range(p, flags):
     # Rows of bf16 subnormals: G can fall below 2^-128, where 1/G exceeds fp32.
@@ -277,7 +301,7 @@ def test_mxnorm_normaliser_past_fp32_range(p, flags):
         assert_bits(c[:5], c2, what + " scale invariance (codes)")
 
 
-@pytest.mark.parametrize("flags", [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS])
+@pytest.mark.parametrize("flags", ALL_VARIANTS)
 def test_mxnorm_nonfinite_gains(flags):
     # a NaN or Inf gain makes its products non-finite: those blocks get scale
     # 0xFF and NaN codes in every row; Inf * 0 (zero row) is NaN too
@@ -308,9 +332,46 @@ def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma, elem, rnd)
     x[5, :64] *= 40.0
     g = workloads.random_gamma(D, seed=80, device=DEV) if gamma else None
     for p in (1.0, 2.0, 3.5, math.inf):
-        a = gpu_mxnorm(x, g, p, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_REG)
-        b = gpu_mxnorm(x, g, p, elem, rnd, flags=mxq.MXQ_FLAG_FORCE_LDS)
-        assert same_outputs(a, b), p
+        a = gpu_mxnorm(x, g, p, elem, rnd)
+        for flags in variants_for(D):
+            b = gpu_mxnorm(x, g, p, elem, rnd, flags=flags)
+            assert same_outputs(a, b), (p, flags)
+
+
+@pytest.mark.parametrize("D", [8224, 12288, 14336, 16384, 24576, 24608, 32768])
+@pytest.mark.parametrize("gamma", [False, True])
+@pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e2m1", "sr")])
+def test_wide_rows_split_and_lds_variants_are_bit_identical(D, gamma, elem, rnd):
+    # rows past one wavefront's registers: the LDS-staged kernel and, for
+    # whole chunks, the split-row kernel (8 chunks per wavefront, gains shared
+    # in LDS; 14336 leaves the last wavefront half full) give the same bits as
+    # the automatic choice
+    x = workloads.random_rows(11, D, seed=87 + D, device=DEV)
+    x[4, :96] *= 40.0
+    x[7] = x[7] * 2.0**-131                  # normaliser past fp32: the rescaled exchange
+    g = workloads.random_gamma(D, seed=88, device=DEV) if gamma else None
+    for p in (1.0, 2.0, 3.5, math.inf):
+        a = gpu_mxnorm(x, g, p, elem, rnd)
+        for flags in variants_for(D):
+            b = gpu_mxnorm(x, g, p, elem, rnd, flags=flags)
+            assert same_outputs(a, b), (p, flags)
+
+
+@pytest.mark.parametrize("D", [512, 1024, 2560, 3584, 4096, 6144, 8192, 14336, 16384, 32768])
+def test_mxnorm_split_variant_against_the_oracle(D):
+    # the split-row kernel on its own: one to four wavefronts of 4 chunks, a
+    # short last wavefront (2560, 3584: its spare slots repeat the last
+    # chunk), and 8-chunk wavefronts with the gains in LDS (D > 8192; 14336
+    # has a half-full last wavefront)
+    x = workloads.random_rows(9, D, seed=89 + D, device=DEV)
+    x[2, :96] *= 25.0
+    x[5] = 0.0
+    g = workloads.random_gamma(D, seed=90, device=DEV)
+    for p in (2.0, 3.5):
+        check_mxnorm(x, g, p, flags=mxq.MXQ_FLAG_FORCE_SPLIT, what=f"split D={D} p={p}")
+    check_mxnorm(x, None, 1.0, "e2m1", "sr", flags=mxq.MXQ_FLAG_FORCE_SPLIT,
+                 what=f"split D={D} e2m1 sr")
+    check_rms_fused(x, g, flags=mxq.MXQ_FLAG_FORCE_SPLIT, what=f"split rms D={D}")
 
 
 @pytest.mark.parametrize("elem,rnd", [("e2m1", "rne"), ("e4m3", "rne"), ("e2m1", "sr")])
@@ -325,13 +386,14 @@ def test_mxnorm_lds_variant_against_the_oracle(elem, rnd, D):
                  what=f"lds {elem} {rnd} D={D} no gamma")
 
 
-@pytest.mark.parametrize("flags", [0, mxq.MXQ_FLAG_FORCE_LDS])
+@pytest.mark.parametrize("flags", [0] + ALL_VARIANTS)
 @pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
-def test_mxnorm_strided_rows_both_variants(flags, elem):
-    # rows inside a wider buffer (ldx > D) through either kernel
-    x = workloads.random_rows(11, 1024, seed=83, device=DEV, ldx=1056)
-    assert x.stride(0) == 1056
-    g = workloads.random_gamma(1024, seed=84, device=DEV)
+@pytest.mark.parametrize("D", [1024, 4096])
+def test_mxnorm_strided_rows_every_variant(flags, elem, D):
+    # rows inside a wider buffer (ldx > D) through each kernel
+    x = workloads.random_rows(11, D, seed=83, device=DEV, ldx=D + 32)
+    assert x.stride(0) == D + 32
+    g = workloads.random_gamma(D, seed=84, device=DEV)
     c1, s1, i1 = check_mxnorm(x, g, 2.0, elem, flags=flags, what=f"strided {elem} flags={flags}")
     c2, s2, i2 = gpu_mxnorm(x.contiguous(), g, 2.0, elem, flags=flags)
     assert np.array_equal(c1, np_(c2)) and np.array_equal(s1, np_(s2)) and np.array_equal(i1, np_(i2))
@@ -434,10 +496,11 @@ def test_rms_fused_formats(elem, rnd, T):
 def test_rms_fused_register_and_lds_variants_are_bit_identical(D):
     x = workloads.random_rows(37, D, seed=95 + D, device=DEV)
     g = workloads.random_gamma(D, seed=96, device=DEV)
-    a = mxq.rmsnorm_mxcast_fused(x, g, flags=mxq.MXQ_FLAG_FORCE_REG)
-    b = mxq.rmsnorm_mxcast_fused(x, g, flags=mxq.MXQ_FLAG_FORCE_LDS)
-    torch.cuda.synchronize()
-    assert same_outputs(a, b)
+    a = mxq.rmsnorm_mxcast_fused(x, g)
+    for flags in variants_for(D):
+        b = mxq.rmsnorm_mxcast_fused(x, g, flags=flags)
+        torch.cuda.synchronize()
+        assert same_outputs(a, b), flags
 
 
 def test_rms_fused_special_rows():
@@ -847,14 +910,11 @@ def test_ceil_rule_mxnorm_variants_and_special_rows(D):
     x[4] = x[4] * 1e30
     xg = x.to(DEV)
     g = workloads.random_gamma(D, seed=98, device=DEV)
-    for flags in ((mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS) if D <= mxq.MXQ_MAX_D_REG
-                  else (mxq.MXQ_FLAG_FORCE_LDS,)):
+    a = gpu_mxnorm(xg, g, 2.0, rule="ceil")
+    for flags in variants_for(D):
         check_mxnorm(xg, g, 2.0, flags=flags, what=f"ceil special D={D} flags={flags}",
                      rule="ceil")
-    if D <= mxq.MXQ_MAX_D_REG:
-        a = gpu_mxnorm(xg, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_REG, rule="ceil")
-        b = gpu_mxnorm(xg, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_LDS, rule="ceil")
-        assert same_outputs(a, b)
+        assert same_outputs(a, gpu_mxnorm(xg, g, 2.0, flags=flags, rule="ceil")), flags
 
 
 @pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e4m3", "sr"), ("e2m1", "rne")])
@@ -901,6 +961,9 @@ def test_workload_longseq_full_and_variants_identical():
     lds = gpu_mxnorm(x, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_LDS)
     assert same_outputs(reg, lds)
     del lds
+    split = gpu_mxnorm(x, g, 2.0, flags=mxq.MXQ_FLAG_FORCE_SPLIT)
+    assert same_outputs(reg, split)
+    del split
     auto = gpu_mxnorm(x, g, 2.0)
     assert same_outputs(reg, auto)
     del auto
