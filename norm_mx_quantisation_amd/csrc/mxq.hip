@@ -708,39 +708,31 @@ __global__ __launch_bounds__(kThreads) void mxnorm_reg_kernel(NormArgs A) {
 
 constexpr int kSplitMaxWaves = 16;  // wavefronts per workgroup of the split-row kernel
 
-// A row split over W wavefronts: wave w holds chunks [w CPW, w CPW + CPW) of
-// the row in VGPRs, and R rows share a workgroup (R = 1 unless GLDS). Rows are
-// a whole number of chunks (D % 512 == 0). When the row's chunk count is not a
-// multiple of CPW, the last wave's surplus slots hold copies of the row's last
-// chunk: they are left out of the statistic, and they encode to the same codes
-// the real last chunk does (same data, gains, scale and random words), which
-// are written to the same place again; so the code has no chunk tests at all.
-// Each wave adds its groups' terms (CPW / kGroupChunks groups) in the canonical
-// order; the group totals meet in LDS and every wave of the row adds all of
+// A row split over W wavefronts of one workgroup: wave w holds statistic group
+// w, chunks [4w, 4w + 4) of the row, in VGPRs, with the gains of those chunks.
+// Rows are a whole number of chunks (D % 512 == 0). When the row's chunk count
+// is not a multiple of 4, the last wave's spare slots hold copies of the row's
+// last chunk: they are left out of the statistic, and they encode to the same
+// codes the real last chunk does (same data, gains, scale and random words),
+// written to the same place again; so the code has no chunk tests at all.
+// Each wave's group total meets the others in LDS and every wave adds all of
 // them in group order, so the statistic has exactly the bits of the one-wave
 // kernels. Every wave then encodes its own chunks: the work after the row's
-// last byte arrives is spread over W wavefronts (and so over the CU's SIMDs)
-// instead of one. GLDS: the gains are staged once per workgroup in LDS as bf16
-// by direct-to-LDS loads and shared by the R rows; otherwise each wave loads
-// its own CPW chunks of gains into VGPRs ahead of its row loads.
-template <int CPW, bool GLDS, int ELEM, int RND, bool GAMMA, int STAT>
-__global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(NormArgs A, int nchunks,
-                                                                              int W, int R) {
-  constexpr int GPW = CPW / kGroupChunks;  // groups per wave
-  extern __shared__ uint4 g_lds[];         // GLDS gains: [nchunks * 64] x 8 bf16
-  __shared__ __align__(16) float part[kSplitMaxWaves * GPW];
-  __shared__ __align__(16) float part2[kSplitMaxWaves * GPW];
+// last byte arrives is spread over W wavefronts (and the CU's SIMDs) instead
+// of one, and a wave needs 16 KB of loads in flight at most, so the kernel
+// keeps the occupancy of the short rows at any D.
+template <int ELEM, int RND, bool GAMMA, int STAT>
+__global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(NormArgs A, int nchunks) {
+  constexpr int CPW = kGroupChunks;  // chunks per wave: one statistic group
+  __shared__ __align__(16) float part[kSplitMaxWaves];
+  __shared__ __align__(16) float part2[kSplitMaxWaves];
   __shared__ __align__(16) uint32_t pmax[kSplitMaxWaves];
   __shared__ uint32_t sc_lds[kSplitMaxWaves][CPW * 4];
+  const int W = (nchunks + CPW - 1) / CPW;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
-  int rw = 0;
-  if constexpr (GLDS)
-    while (wid >= (rw + 1) * W) ++rw;  // row of the workgroup (R <= 5: a few scalar steps)
-  const int w = wid - rw * W;
-  const int64_t row = (int64_t)blockIdx.x * R + rw;
-  const bool live = row < A.T;
-  const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = A.x + row * A.ldx;
   const int dl = lane * 8;
   const int c0 = w * CPW;
   const int ncw = min(CPW, nchunks - c0);  // this wave's real chunks, >= 1
@@ -749,16 +741,10 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
   // before it).
   auto chunk_of = [&](int c) { return min(c0 + c, nchunks - 1); };
 
-  uint4 graw[GLDS ? 1 : CPW];
+  uint4 graw[CPW];
   if (GAMMA) {
-    if constexpr (GLDS) {
-      for (int i = wid; i < nchunks; i += R * W)
-        __builtin_amdgcn_global_load_lds((const void*)(A.gamma + i * kChunk + dl),
-                                         (lds_void*)(g_lds + i * kWave), 16, 0, 0);
-    } else {
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) graw[c] = load16(A.gamma + chunk_of(c) * kChunk + dl);
-    }
+    for (int c = 0; c < CPW; ++c) graw[c] = load16(A.gamma + chunk_of(c) * kChunk + dl);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
   uint4 raw[CPW];
@@ -769,86 +755,71 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
   uint32_t mb[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) mb[c] = quad_max_u32(absmax_bits8(raw[c]));
-  auto mb_stat = [&](int c) { return c < ncw ? mb[c] : 0u; };  // surplus slots add nothing
-  auto wave_groups = [&](float* dst, int shift) {  // this wave's group totals -> dst
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      float t;
-      if constexpr (STAT == S_RMS)
-        t = group_sumsq<kGroupChunks>(j * kGroupChunks, j * kGroupChunks + kGroupChunks,
-                                      [&](int c, float u) { return c < ncw ? sumsq8(raw[c], u) : u; });
-      else
-        t = group_terms<kGroupChunks>(j * kGroupChunks, j * kGroupChunks + kGroupChunks, mb_stat,
-                                      shift, A.pmode, A.p);
-      if (lane == 0) dst[wid * GPW + j] = t;  // a group past the row end is never read
-    }
+  auto mb_stat = [&](int c) { return c < ncw ? mb[c] : 0u; };  // spare slots add nothing
+  auto wave_group = [&](float* dst, int shift) {  // this wave's group total -> dst[w]
+    float t;
+    if constexpr (STAT == S_RMS)
+      t = group_sumsq<CPW>(0, CPW, [&](int c, float u) { return c < ncw ? sumsq8(raw[c], u) : u; });
+    else
+      t = group_terms<CPW>(0, CPW, mb_stat, shift, A.pmode, A.p);
+    if (lane == 0) dst[w] = t;
   };
-  if (STAT == S_RMS || A.pmode != P_INF) wave_groups(part, 0);
+  if (STAT == S_RMS || A.pmode != P_INF) wave_group(part, 0);
   if (STAT == S_PMEAN) {
     uint32_t m = 0;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) m = max(m, mb[c]);  // copies of the last chunk change no maximum
     m = max_over_quads(m);
-    if (lane == 0) pmax[wid] = m;
+    if (lane == 0) pmax[w] = m;
   }
-  if (GLDS && GAMMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the gains' direct-to-LDS loads
   __syncthreads();
 
-  const int ng = (nchunks + kGroupChunks - 1) / kGroupChunks;  // groups in a row
-  auto row_total = [&](const float* src, int r) {
+  // 16-byte LDS reads; the group totals are added in group order
+  auto row_total = [&](const float* src) {
     float t = 0.0f;
-    if constexpr (!GLDS) {  // one row, at most 4 groups: one 16-byte LDS read
-      const float4 q = *reinterpret_cast<const float4*>(src);
-      t = q.x;
-      if (ng > 1) t += q.y;
-      if (ng > 2) t += q.z;
-      if (ng > 3) t += q.w;
-    } else {
-      for (int k = 0; k < ng; ++k) t += src[r * W * GPW + k];
+#pragma unroll
+    for (int k4 = 0; k4 < kSplitMaxWaves; k4 += 4) {
+      if (k4 >= W) break;
+      const float4 q = *reinterpret_cast<const float4*>(src + k4);
+      t = k4 == 0 ? q.x : t + q.x;
+      if (k4 + 1 < W) t += q.y;
+      if (k4 + 2 < W) t += q.z;
+      if (k4 + 3 < W) t += q.w;
     }
     return t;
   };
-  auto row_max = [&](int r) {
+  auto row_max = [&]() {
     uint32_t m = 0;
-    if constexpr (!GLDS) {
-      const uint4 q = *reinterpret_cast<const uint4*>(pmax);
-      m = q.x;
-      if (W > 1) m = max(m, q.y);
-      if (W > 2) m = max(m, q.z);
-      if (W > 3) m = max(m, q.w);
-    } else {
-      for (int j = 0; j < W; ++j) m = max(m, pmax[r * W + j]);
+#pragma unroll
+    for (int j4 = 0; j4 < kSplitMaxWaves; j4 += 4) {
+      if (j4 >= W) break;
+      const uint4 q = *reinterpret_cast<const uint4*>(pmax + j4);
+      m = max(m, q.x);
+      if (j4 + 1 < W) m = max(m, q.y);
+      if (j4 + 2 < W) m = max(m, q.z);
+      if (j4 + 3 < W) m = max(m, q.w);
     }
     return m;
   };
   Normaliser N;
   if constexpr (STAT == S_RMS) {
-    N = plain_normaliser(rms_inv(row_total(part, rw), A.Df, A.eps));
+    N = plain_normaliser(rms_inv(row_total(part), A.Df, A.eps));
   } else {
     const bool pinf = A.pmode == P_INF;
-    const float s = pinf ? 0.0f : row_total(part, rw);
-    const uint32_t rmax = row_max(rw);
-    // the rescaled totals, when any row of the workgroup needs them (a
-    // workgroup-uniform decision, so every wave reaches the same barriers)
-    bool any = !pinf && rmax != 0u && rmax < 0x7F80u &&
-               !direct_total_suffices(s, A.pmode, A.p, A.Kf, A.Kinv);
-    if constexpr (GLDS) {  // the other rows of the workgroup
-      for (int r = 0; r < R; ++r) {
-        const uint32_t mr = row_max(r);
-        any |= r != rw && !pinf && mr != 0u && mr < 0x7F80u &&
-               !direct_total_suffices(row_total(part, r), A.pmode, A.p, A.Kf, A.Kinv);
-      }
-    }
+    const float s = pinf ? 0.0f : row_total(part);
+    const uint32_t rmax = row_max();
+    const bool finite_nonzero = rmax != 0u && rmax < 0x7F80u;
     float s2 = 0.0f;
-    if (any) {
-      wave_groups(part2, (rmax != 0u && rmax < 0x7F80u) ? -bf16_exponent(rmax) : 0);
+    // the rescaled totals: a workgroup-uniform decision, so every wave
+    // reaches the barrier
+    if (!pinf && finite_nonzero && !direct_total_suffices(s, A.pmode, A.p, A.Kf, A.Kinv)) {
+      wave_group(part2, -bf16_exponent(rmax));
       __syncthreads();
-      s2 = row_total(part2, rw);
+      s2 = row_total(part2);
     }
     N = row_normaliser([&](int shift) { return shift == 0 ? s : s2; }, [&]() { return rmax; },
                        A.pmode, A.p, A.Kf, A.Kinv);
   }
-  if (!live) return;
   if (w == 0 && lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
 #pragma unroll
   for (int c = 0; c < CPW; ++c)  // widen each chunk where it is used (see mxnorm_row_reg)
@@ -856,7 +827,7 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
 
   const uint64_t nrow = (uint64_t)row * (uint64_t)A.D;
   uint8_t* crow = code_row<ELEM>(A.codes, nrow);
-  uint32_t* sc = sc_lds[wid];
+  uint32_t* sc = sc_lds[w];
   float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
@@ -865,10 +836,10 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
     if (!GAMMA) {
       code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, raw[c], g, mb[c], N);
     } else {
-      unpack8(GLDS ? g_lds[chunk_of(c) * kWave + lane] : graw[c], g);
+      unpack8(graw[c], g);
       code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, raw[c], g, 0u, N);
     }
-    if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);  // surplus slots: not flushed
+    if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);  // spare slots: not flushed
   }
   flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K + (uint64_t)(c0 * 16), ncw * 16,
                A.sc_vec != 0, lane);
@@ -1160,25 +1131,16 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
   return MXQ_OK;
 }
 
-// Split rows: up to 16 chunks, 4 per wavefront with the gains in VGPRs and one
-// row (at most 4 wavefronts) per workgroup; longer rows 8 chunks per
-// wavefront with the gains shared in LDS by the rows of a workgroup of up to
-// 16 wavefronts.
-template <int CPW, bool GLDS, int ELEM, int RND, bool GAMMA, int STAT>
+// Split rows: 4 chunks per wavefront, one row per workgroup of up to 16
+// wavefronts.
+template <int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_split(const NormArgs& A, int nc, hipStream_t s) {
   if (A.D % kChunk != 0) return MXQ_ERR_UNSUPPORTED;  // whole chunks only
-  const int W = (nc + CPW - 1) / CPW;
+  const int W = (nc + kGroupChunks - 1) / kGroupChunks;
   if (W > kSplitMaxWaves) return MXQ_ERR_UNSUPPORTED;
-  const int R = GLDS ? max(1, kSplitMaxWaves / W) : 1;
-  if ((A.T + R - 1) / R > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
-  const size_t lds = (GLDS && GAMMA) ? (size_t)nc * kWave * sizeof(uint4) : 0;
-  auto kern = mxnorm_split_kernel<CPW, GLDS, ELEM, RND, GAMMA, STAT>;
-  if (lds > 0 &&
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
-    return MXQ_ERR_HIP;
-  const unsigned grid = (unsigned)((A.T + R - 1) / R);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * R * W), lds, s, A, nc, W, R);
+  if (A.T > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((mxnorm_split_kernel<ELEM, RND, GAMMA, STAT>), dim3((unsigned)A.T),
+                     dim3(kWave * W), 0, s, A, nc);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
@@ -1190,13 +1152,9 @@ mxq_status dispatch_mxnorm(const NormArgs& A, bool gamma, int variant, int nc, h
   if (variant == V_LDS)
     return gamma ? launch_mxnorm_lds<ELEM, RND, true, STAT>(A, nc, s)
                  : launch_mxnorm_lds<ELEM, RND, false, STAT>(A, nc, s);
-  if (variant == V_SPLIT) {
-    if (nc <= 4 * kGroupChunks)
-      return gamma ? launch_mxnorm_split<4, false, ELEM, RND, true, STAT>(A, nc, s)
-                   : launch_mxnorm_split<4, false, ELEM, RND, false, STAT>(A, nc, s);
-    return gamma ? launch_mxnorm_split<8, true, ELEM, RND, true, STAT>(A, nc, s)
-                 : launch_mxnorm_split<8, true, ELEM, RND, false, STAT>(A, nc, s);
-  }
+  if (variant == V_SPLIT)
+    return gamma ? launch_mxnorm_split<ELEM, RND, true, STAT>(A, nc, s)
+                 : launch_mxnorm_split<ELEM, RND, false, STAT>(A, nc, s);
   return gamma ? dispatch_mxnorm_reg<ELEM, RND, true, STAT>(A, nc, s)
                : dispatch_mxnorm_reg<ELEM, RND, false, STAT>(A, nc, s);
 }

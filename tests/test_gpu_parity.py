@@ -343,9 +343,9 @@ def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma, elem, rnd)
 @pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e2m1", "sr")])
 def test_wide_rows_split_and_lds_variants_are_bit_identical(D, gamma, elem, rnd):
     # rows past one wavefront's registers: the LDS-staged kernel and, for
-    # whole chunks, the split-row kernel (8 chunks per wavefront, gains shared
-    # in LDS; 14336 leaves the last wavefront half full) give the same bits as
-    # the automatic choice
+    # whole chunks, the split-row kernel (up to 16 wavefronts of 4 chunks;
+    # 14336 leaves the last wavefront with one spare slot) give the same bits
+    # as the automatic choice
     x = workloads.random_rows(11, D, seed=87 + D, device=DEV)
     x[4, :96] *= 40.0
     x[7] = x[7] * 2.0**-131                  # normaliser past fp32: the rescaled exchange
@@ -359,10 +359,9 @@ def test_wide_rows_split_and_lds_variants_are_bit_identical(D, gamma, elem, rnd)
 
 @pytest.mark.parametrize("D", [512, 1024, 2560, 3584, 4096, 6144, 8192, 14336, 16384, 32768])
 def test_mxnorm_split_variant_against_the_oracle(D):
-    # the split-row kernel on its own: one to four wavefronts of 4 chunks, a
-    # short last wavefront (2560, 3584: its spare slots repeat the last
-    # chunk), and 8-chunk wavefronts with the gains in LDS (D > 8192; 14336
-    # has a half-full last wavefront)
+    # the split-row kernel on its own: one to sixteen wavefronts of 4 chunks,
+    # and a short last wavefront (2560, 3584, 14336: its spare slots repeat
+    # the row's last chunk)
     x = workloads.random_rows(9, D, seed=89 + D, device=DEV)
     x[2, :96] *= 25.0
     x[5] = 0.0
