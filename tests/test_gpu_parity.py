@@ -687,6 +687,64 @@ def random_mx_operand(rows, K, seed, scale_lo=115, scale_hi=135, fmt="e4m3"):
     return codes.to(DEV), scales.to(DEV)
 
 
+def _e4m3_pow2(e, neg=False):
+    """E4M3 code of +-2^e for e in [-9, 8] (subnormal below 2^-6)."""
+    c = (e + 7) << 3 if e >= -6 else 1 << (e + 9)
+    return c | (0x80 if neg else 0)
+
+
+@pytest.mark.parametrize("fmt_b", ["e4m3", "e2m1"])
+def test_gemm_block_sum_precision_characterised(fmt_b):
+    # The evidence for gemm_bound: the scaled matrix instruction adds a block's
+    # products at less than fp32 precision, so results are not those of an fp32
+    # sum in any order. One row of A per pattern: in one aligned 8-element group
+    # of block 1, a product 2^e_big and n_small products +-2^e_small (A's
+    # elements times B = 1, at scale 2^0); everything else zero. Checks: every
+    # row within the bound; the loss at most 2^-11 of sum |a b|; and a loss
+    # that an fp32 sum would not make (products 2^14 apart are exact in fp32
+    # with room to spare) does occur, so a bit-exact bar would be wrong.
+    K, N = 128, 16
+    pats = []
+    for e_big in (2, 5, 8):
+        for e_small in (-9, -7, -6, -3, 0):
+            for n_small in (1, 3, 7):
+                for pos in (0, 5):
+                    for neg in (False, True):
+                        pats.append((e_big, e_small, n_small, pos, neg))
+    M = len(pats)
+    A = np.zeros((M, K), np.uint8)
+    for r, (e_big, e_small, n_small, pos, neg) in enumerate(pats):
+        g0 = 32 + 16                                  # block 1, group 2
+        others = [j for j in range(8) if j != pos][:n_small]
+        A[r, g0 + pos] = _e4m3_pow2(e_big)
+        for j in others:
+            A[r, g0 + j] = _e4m3_pow2(e_small, neg)
+    SA = np.full((M, K // 32), 127, np.uint8)
+    if fmt_b == "e4m3":
+        B = np.full((N, K), 0x38, np.uint8)           # 1.0
+    else:
+        B = np.full((N, K // 2), 0x22, np.uint8)      # two E2M1 1.0 codes per byte
+    SB = np.full((N, K // 32), 127, np.uint8)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    c = mxq.mx_matmul(t(A), t(SA), t(B), t(SB), fmt_b=fmt_b)
+    torch.cuda.synchronize()
+    c64, ab = oracle.mx_gemm(A, SA, B, SB, K, "e4m3", fmt_b)
+    got = c.double().cpu().numpy()
+    err = np.abs(got - c64)
+    assert (err <= gemm_bound(ab, K, c64, False)).all()
+    rel = err / ab
+    assert rel.max() <= 2.0 ** -11, rel.max()
+    apart = np.array([p[0] - p[1] >= 14 for p in pats])
+    assert (err[apart] > 0).any()                     # absorbed products
+    # the exact fp32 sum of these products: they are all representable and
+    # their sum needs at most 18 significant bits
+    f32 = np.array([[np.float64(np.float32(v)) for v in row] for row in c64])
+    assert np.array_equal(f32, c64)
+    for e_gap in sorted({p[0] - p[1] for p in pats}):
+        sel = np.array([p[0] - p[1] == e_gap for p in pats])
+        print(f"{fmt_b} gap 2^{e_gap}: max loss {rel[sel].max():.3e} of sum |ab|")
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (256, 512, 1024), (300, 200, 256),
                                    (1, 7, 4096), (513, 257, 384)])
 def test_gemm_random_operands(M, N, K):
