@@ -101,6 +101,12 @@ def lib():
             L.orc_mx_gemm.argtypes = [vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i64, i64,
                                       i64, vp, vp]
             L.orc_mx_gemm.restype = i32
+            L.orc_nvfp4_cast.argtypes = [vp, i64, i64, i64, dbl, vp, vp]
+            L.orc_nvfp4_cast.restype = i32
+            L.orc_mxnorm_nvfp4.argtypes = [vp, i64, vp, i64, i64, dbl, dbl, vp, vp, vp, vp]
+            L.orc_mxnorm_nvfp4.restype = i32
+            L.orc_nvfp4_block.argtypes = [vp, dbl, i32, vp, vp]
+            L.orc_nvfp4_block.restype = i32
             _lib = L
     return _lib
 
@@ -200,6 +206,55 @@ def mxnorm(x, gamma=None, p=2.0, elem="e4m3", rnd="rne", seed=0, offset=0,
             _ptr(codes[r0:]), _ptr(scales[r0:]), _ptr(inv[r0:]))
     _run([job(a, b) for a, b in _split(T, threads)], threads)
     return codes, scales, inv
+
+
+def nvfp4_cast(x, tensor_scale=1.0, threads=1):
+    """NVFP4 cast of bf16 rows: (codes [T, D/2] packed E2M1, scales [T, D/16] E4M3)."""
+    L = lib()
+    x, T, D, ldx = _rows_view(as_bf16_bits(x))
+    codes = np.zeros((T, D // 2), np.uint8)
+    scales = np.zeros((T, D // 16), np.uint8)
+    xb = x.ctypes.data
+
+    def job(r0, r1):
+        return lambda: L.orc_nvfp4_cast(ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, r1 - r0, D,
+                                        float(tensor_scale), _ptr(codes[r0:]), _ptr(scales[r0:]))
+    _run([job(a, b) for a, b in _split(T, threads)], threads)
+    return codes, scales
+
+
+def mxnorm_nvfp4(x, gamma=None, p=2.0, tensor_scale=1.0, inv_inject=None, threads=1):
+    """MXNorm over NVFP4 blocks. inv_inject=None: mode (R); else mode (I) with the
+    given fp32 per-row normalisers. Returns (codes, scales, inv float64 [T])."""
+    L = lib()
+    x, T, D, ldx = _rows_view(as_bf16_bits(x))
+    g = None if gamma is None else np.ascontiguousarray(as_bf16_bits(gamma).reshape(-1))
+    inj = None if inv_inject is None else np.ascontiguousarray(
+        np.asarray(inv_inject, dtype=np.float32).reshape(-1))
+    codes = np.zeros((T, D // 2), np.uint8)
+    scales = np.zeros((T, D // 16), np.uint8)
+    inv = np.zeros(T, np.float64)
+    xb = x.ctypes.data
+
+    def job(r0, r1):
+        return lambda: L.orc_mxnorm_nvfp4(
+            ctypes.c_void_p(xb + 2 * r0 * ldx), ldx, _ptr(g), r1 - r0, D, float(p),
+            float(tensor_scale), None if inj is None else _ptr(inj[r0:]), _ptr(codes[r0:]),
+            _ptr(scales[r0:]), _ptr(inv[r0:]))
+    _run([job(a, b) for a, b in _split(T, threads)], threads)
+    return codes, scales, inv
+
+
+def nvfp4_block(v, tensor_scale=1.0, fp32=True):
+    """NVFP4 encode of one block of 16 values: (16 unpacked E2M1 codes, E4M3 scale byte)."""
+    L = lib()
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(16))
+    codes = np.zeros(16, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    rc = L.orc_nvfp4_block(_ptr(a), float(tensor_scale), int(bool(fp32)), _ptr(codes), _ptr(sc))
+    if rc != 0:
+        raise ValueError(f"oracle returned error {rc}")
+    return codes, int(sc[0])
 
 
 def rmsnorm_mxcast(x, gamma=None, eps=1e-5, elem="e4m3", rnd="rne", seed=0, offset=0,

@@ -56,6 +56,22 @@
  *    separate normalisation op emits a bf16 tensor). The single-pass
  *    comparator uses the same statistic but casts y without the bf16 step.
  *
+ * NVFP4 (named by the MXNorm page, §3.2, and by a related-paper title on the
+ * MXFP8 recipes page, but defined on neither; the reading below is the
+ * published two-level format, written out in the design notes):
+ *  - elements E2M1 as above, packed the same way; blocks of 16 consecutive
+ *    elements along the row; one E4M3 scale byte per block; one fp32 tensor
+ *    scale s_t in [2^-32, 2^32] given by the caller (decode: e2m1 * e4m3(scale)
+ *    * s_t).
+ *  - per block with a = max |y|: the scale byte is the E4M3 encoding (round
+ *    to nearest even, saturating at 448) of RN32(a * k), k = RN32(1 / (6 s_t));
+ *    with Sd its value, each element is the E2M1 encoding (RNE, saturating) of
+ *    RN32(y * r), r = RN32(1 / RN32(Sd * s_t)), or r = 0 when Sd == 0 (the
+ *    block then holds signed zeros); a block holding NaN or Inf gets scale
+ *    0x7F (the E4M3 NaN) and element codes 0x7.
+ *  - MXNorm over NVFP4 takes its statistic from the same blocks: m_k over 16
+ *    elements, K = D / 16.
+ *
  * Two modes for the normalising ops:
  *  (R) reference: statistic and normaliser in fp64, y in fp64, cast directly.
  *  (I) injected: takes a per-row fp32 normaliser and applies the fp32
@@ -525,6 +541,140 @@ int orc_rmsnorm_fused_mxcast(const uint16_t* x, int64_t ldx, const uint16_t* gam
   }
   free(y);
   free(cu);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* NVFP4                                                               */
+/* ------------------------------------------------------------------ */
+
+/* One row of values y (D of them, D % 16 == 0) to NVFP4: unpacked E2M1 codes
+ * and D/16 E4M3 scale bytes. fp32 == 1: the fp32 operation order of the
+ * reading (RN32 after each product and reciprocal; every product here is
+ * exact in double, and the reciprocal of an fp32 value is never close enough
+ * to an fp32 rounding midpoint for the double-then-float rounding to differ
+ * from a direct one). fp32 == 0: the same rules in fp64 (reference mode of
+ * the normalising op). */
+static void nvfp4_row_f64(const double* y, int64_t D, double s_t, int fp32, uint8_t* code_row,
+                          uint8_t* scale_row) {
+  const double k = fp32 ? (double)rn32(1.0 / (6.0 * s_t)) : 1.0 / (6.0 * s_t);
+  for (int64_t b = 0; b < D / 16; ++b) {
+    const double* v = y + 16 * b;
+    double amax = 0;
+    int nonfinite = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (!isfinite(v[i])) nonfinite = 1;
+      else if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    }
+    if (nonfinite) {
+      scale_row[b] = 0x7F;
+      for (int i = 0; i < 16; ++i) code_row[16 * b + i] = 0x7;
+      continue;
+    }
+    double q = fp32 ? (double)rn32(amax * k) : amax * k;
+    if (q > FMT_E4M3.maxval) q = FMT_E4M3.maxval; /* saturating (also keeps an fp32 Inf out) */
+    const uint8_t sc = encode_value(&FMT_E4M3, ORC_RNE, q, 0);
+    scale_row[b] = sc;
+    const double Sd = orc_e4m3_decode(sc);
+    for (int i = 0; i < 16; ++i) {
+      double z;
+      if (Sd == 0) {
+        z = copysign(0.0, v[i]);
+      } else if (fp32) {
+        const double r = (double)rn32(1.0 / (double)rn32(Sd * s_t));
+        z = (double)rn32(v[i] * r);
+      } else {
+        z = v[i] / (Sd * s_t);
+      }
+      code_row[16 * b + i] = encode_value(&FMT_E2M1, ORC_RNE, z, 0);
+    }
+  }
+}
+
+/* The tensor scale is taken in [2^-32, 2^32], where every quantity above stays
+ * a finite, normal fp32 value. */
+static int nvfp4_scale_ok(double s_t) { return s_t >= ldexp(1.0, -32) && s_t <= ldexp(1.0, 32); }
+
+static int nvfp4_args(int64_t T, int64_t D, double s_t) {
+  if (T < 0 || D <= 0 || D % 32 != 0) return 2;
+  if (!nvfp4_scale_ok(s_t)) return 4;
+  return 0;
+}
+
+/* NVFP4 cast of a bf16 activation: codes [T, D/2], scales [T, D/16]. The
+ * fp32 order of the reading is the definition, so there is one mode. */
+int orc_nvfp4_cast(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, double s_t,
+                   uint8_t* codes, uint8_t* scales) {
+  int rc = nvfp4_args(T, D, s_t);
+  if (rc) return rc;
+  double* v = (double*)malloc(sizeof(double) * (size_t)D);
+  uint8_t* cu = (uint8_t*)malloc((size_t)D);
+  if (!v || !cu) { free(v); free(cu); return 6; }
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t d = 0; d < D; ++d) v[d] = orc_bf16_to_f64(x[t * ldx + d]);
+    nvfp4_row_f64(v, D, s_t, 1, cu, scales + t * (D / 16));
+    store_codes(ORC_E2M1, cu, D, codes + t * (D / 2));
+  }
+  free(v);
+  free(cu);
+  return 0;
+}
+
+/* MXNorm over NVFP4: G is the p-mean of the 16-element block maxima of |x|;
+ * y as in orc_mxnorm; then the NVFP4 cast of y. inv_inject == NULL: mode (R)
+ * (fp64 throughout); otherwise mode (I) with the given fp32 normalisers and
+ * the fp32 order. */
+int orc_mxnorm_nvfp4(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                     int64_t D, double p, double s_t, const float* inv_inject, uint8_t* codes,
+                     uint8_t* scales, double* inv_out) {
+  int rc = nvfp4_args(T, D, s_t);
+  if (rc) return rc;
+  if (!(p > 0)) return 5;
+  const int64_t K = D / 16;
+  double* y = (double*)malloc(sizeof(double) * (size_t)D);
+  double* m = (double*)malloc(sizeof(double) * (size_t)K);
+  uint8_t* cu = (uint8_t*)malloc((size_t)D);
+  if (!y || !m || !cu) { free(y); free(m); free(cu); return 6; }
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ldx;
+    double inv;
+    if (inv_inject) {
+      inv = (double)inv_inject[t];
+    } else {
+      int nonfinite = 0;
+      for (int64_t b = 0; b < K; ++b) {
+        double mb = 0;
+        for (int i = 0; i < 16; ++i) {
+          double xi = orc_bf16_to_f64(xr[16 * b + i]);
+          if (!isfinite(xi)) nonfinite = 1;
+          else if (fabs(xi) > mb) mb = fabs(xi);
+        }
+        m[b] = mb;
+      }
+      double G = orc_pmean(m, K, p);
+      inv = nonfinite ? NAN : (G == 0 ? 0.0 : 1.0 / G);
+    }
+    if (inv_out) inv_out[t] = inv;
+    for (int64_t d = 0; d < D; ++d) {
+      double xi = orc_bf16_to_f64(xr[d]);
+      double gi = gamma ? orc_bf16_to_f64(gamma[d]) : 1.0;
+      y[d] = inv_inject ? (double)rn32((double)rn32(xi * gi) * inv) : xi * gi * inv;
+    }
+    nvfp4_row_f64(y, D, s_t, inv_inject != NULL, cu, scales + t * K);
+    store_codes(ORC_E2M1, cu, D, codes + t * (D / 2));
+  }
+  free(y);
+  free(m);
+  free(cu);
+  return 0;
+}
+
+/* NVFP4 block encode of 16 doubles (test helper for the pins): fp32 as in
+ * nvfp4_row_f64. */
+int orc_nvfp4_block(const double* v, double s_t, int fp32, uint8_t* codes_unpacked,
+                    uint8_t* scale) {
+  if (!nvfp4_scale_ok(s_t)) return 4;
+  nvfp4_row_f64(v, 16, s_t, fp32, codes_unpacked, scale);
   return 0;
 }
 
