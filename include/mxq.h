@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 3
+#define MXQ_ABI_VERSION 4
 
 typedef enum {
   MXQ_OK = 0,
@@ -264,6 +264,40 @@ mxq_status mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* a_scales, int64
                    const uint8_t* b, int64_t ldb, const uint8_t* b_scales, int64_t ldsb,
                    int64_t M, int64_t N, int64_t K, mxq_elem elem_a, mxq_elem elem_b, void* c,
                    int64_t ldc, mxq_out_type c_type, void* stream);
+
+/*
+ * NVFP4 (MXNorm page, §3.2, names the format for its layer-level result; the
+ * pages do not define it, so the library takes the published two-level format
+ * as a reading): E2M1 elements packed two per byte as for MXQ_E2M1, blocks of
+ * 16 consecutive elements along a row, one E4M3 scale byte per block, and one
+ * fp32 tensor scale s_t from the caller; value = e2m1 * e4m3(scale) * s_t.
+ * Per block with a = max |y|: the scale byte is the E4M3 encoding (round to
+ * nearest even, saturating at 448) of RN32(a * RN32(1 / (6 s_t))); with Sd its
+ * value, each element is the E2M1 encoding (RNE, saturating) of
+ * RN32(y * RN32(1 / RN32(Sd * s_t))), or a signed zero when Sd == 0. A block
+ * holding NaN or Inf gets scale 0x7F (the E4M3 NaN) and element codes 0x7.
+ *   x            [T, D] bf16 bits, row stride ldx (D % 32 == 0, D <= 8192).
+ *   tensor_scale s_t, in [2^-32, 2^32] (1 for MXNorm's normalised output).
+ *   codes        [T, D/2] packed E2M1, contiguous; scales [T, D/16] E4M3 bytes.
+ * Errors: SHAPE, ARG (tensor_scale outside its range or NaN; p <= 0 or NaN),
+ * UNSUPPORTED (D > 8192, T * D >= 2^40), NULL, ALIGN (x, codes: 16 bytes;
+ * gamma: 16; inv_norm: 4), HIP.
+ *
+ * nvfp4_cast_fwd: the cast of x itself (y = x).
+ */
+mxq_status nvfp4_cast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D,
+                          float tensor_scale, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * MXNorm over NVFP4 blocks (MXNorm page, §2.1 with the blocks of the format
+ * being cast to): G is the power mean of the 16-element block maxima of |x|
+ * (K = D / 16), inv = RN32(1/G) as for mxnorm_fwd (reported in inv_norm, which
+ * may be NULL), y = RN32(RN32(x * gamma) * inv), then the NVFP4 encoding above.
+ * gamma may be NULL (gamma == 1); p > 0 or +INFINITY.
+ */
+mxq_status mxnorm_nvfp4_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                            int64_t D, float p, float tensor_scale, uint8_t* codes,
+                            uint8_t* scales, float* inv_norm, void* stream);
 
 /* Static message for a status code (never NULL). */
 const char* mxq_strerror(mxq_status status);

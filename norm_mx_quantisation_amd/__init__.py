@@ -27,11 +27,11 @@ MXQ_RNE, MXQ_SR = 0, 1
 MXQ_FLAG_FORCE_REG, MXQ_FLAG_FORCE_LDS, MXQ_FLAG_SCALE_CEIL, MXQ_FLAG_FORCE_SPLIT = 1, 2, 4, 8
 MXQ_OUT_F32, MXQ_OUT_BF16 = 0, 1
 MXQ_MAX_D_REG, MXQ_MAX_D = 8192, 32768
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("mxnorm_fwd", "rmsnorm_mxcast_fwd", "rmsnorm_mxcast_fused_fwd", "mxcast_fwd",
            "mxnorm_bwd", "mxnorm_bwd_workspace_size", "mxnorm_bwd_noalloc", "mx_gemm",
-           "mxq_strerror", "mxq_abi_version")
+           "nvfp4_cast_fwd", "mxnorm_nvfp4_fwd", "mxq_strerror", "mxq_abi_version")
 
 
 class mxq_rng(ctypes.Structure):
@@ -81,6 +81,10 @@ def lib():
             L.mx_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, i32, vp,
                                   i64, i32, vp]
             L.mx_gemm.restype = i32
+            L.nvfp4_cast_fwd.argtypes = [vp, i64, i64, i64, f32, vp, vp, vp]
+            L.nvfp4_cast_fwd.restype = i32
+            L.mxnorm_nvfp4_fwd.argtypes = [vp, i64, vp, i64, i64, f32, f32, vp, vp, vp, vp]
+            L.mxnorm_nvfp4_fwd.restype = i32
             L.mxq_strerror.argtypes = [i32]
             L.mxq_strerror.restype = ctypes.c_char_p
             L.mxq_abi_version.argtypes = []
@@ -122,6 +126,16 @@ def rmsnorm_mxcast_fused_fwd(x, ldx, gamma, T, D, eps, elem, rnd, rng, flags, co
 
 def mxcast_fwd(x, ldx, T, D, elem, rnd, rng, flags, codes, scales, stream) -> int:
     return lib().mxcast_fwd(x, ldx, T, D, elem, rnd, _rng(rng), flags, codes, scales, stream)
+
+
+def nvfp4_cast_fwd(x, ldx, T, D, tensor_scale, codes, scales, stream) -> int:
+    return lib().nvfp4_cast_fwd(x, ldx, T, D, tensor_scale, codes, scales, stream)
+
+
+def mxnorm_nvfp4_fwd(x, ldx, gamma, T, D, p, tensor_scale, codes, scales, inv_norm,
+                     stream) -> int:
+    return lib().mxnorm_nvfp4_fwd(x, ldx, gamma, T, D, p, tensor_scale, codes, scales, inv_norm,
+                                  stream)
 
 
 def mxnorm_bwd(x, ldx, gamma, dy, lddy, inv_norm, T, D, dx, row_dot, dgamma, workspace,
@@ -302,6 +316,48 @@ def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: i
     if st != MXQ_OK:
         raise MxqError(st, "mxcast_fwd")
     return codes, scales
+
+
+def _nvfp4_outputs(x, T, D, out, want_inv):
+    import torch
+    if out is None:
+        codes = torch.empty((T, D // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((T, D // 16), dtype=torch.uint8, device=x.device)
+        inv = torch.empty((T,), dtype=torch.float32, device=x.device) if want_inv else None
+        return codes, scales, inv
+    if not isinstance(out, (tuple, list)) or len(out) not in (2, 3):
+        raise ValueError("out must be (codes, scales) or (codes, scales, inv)")
+    codes, scales = out[0], out[1]
+    inv = out[2] if len(out) == 3 else None
+    _check_buf(codes, "codes", (T, D // 2), torch.uint8, x.device)
+    _check_buf(scales, "scales", (T, D // 16), torch.uint8, x.device)
+    if want_inv:
+        _check_buf(inv, "inv", (T,), torch.float32, x.device, optional=True)
+    return codes, scales, inv
+
+
+def nvfp4_cast(x, tensor_scale: float = 1.0, stream=None, out=None):
+    """NVFP4 cast. Returns (codes uint8 [T, D/2] packed E2M1, scales uint8 [T, D/16] E4M3)."""
+    T, D, ldx = _check_x(x)
+    codes, scales, _ = _nvfp4_outputs(x, T, D, out, False)
+    st = nvfp4_cast_fwd(_ptr(x), ldx, T, D, tensor_scale, _ptr(codes), _ptr(scales),
+                        _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "nvfp4_cast_fwd")
+    return codes, scales
+
+
+def mxnorm_nvfp4(x, gamma=None, p: float = 2.0, tensor_scale: float = 1.0, stream=None,
+                 out=None):
+    """MXNorm over NVFP4 blocks. Returns (codes, scales E4M3 [T, D/16], inv_norm fp32)."""
+    T, D, ldx = _check_x(x)
+    _check_gamma(gamma, D, x.device)
+    codes, scales, inv = _nvfp4_outputs(x, T, D, out, True)
+    st = mxnorm_nvfp4_fwd(_ptr(x), ldx, _ptr(gamma), T, D, p, tensor_scale, _ptr(codes),
+                          _ptr(scales), _ptr(inv), _stream(stream))
+    if st != MXQ_OK:
+        raise MxqError(st, "mxnorm_nvfp4_fwd")
+    return codes, scales, inv
 
 
 def mxnorm_backward(x, gamma, dy, inv_norm, want_dgamma: bool = True, stream=None, out=None):

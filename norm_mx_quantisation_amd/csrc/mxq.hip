@@ -1293,6 +1293,201 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   return dispatch_norm_cast<STAT>(A, elem, rnd, gamma != nullptr, variant, nc, (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------------ NVFP4
+
+// NVFP4 (a reading: the MXNorm page names the format in §3.2 without defining
+// it): E2M1 elements packed as for MXFP4, blocks of 16 consecutive elements,
+// one E4M3 scale byte per block, one fp32 tensor scale s_t from the caller.
+// Per block with a = max |y|: scale byte = E4M3 RNE (saturating at 448) of
+// RN32(a * k), k = RN32(1 / (6 s_t)); with Sd its value, element code = E2M1
+// RNE (saturating) of RN32(y * r), r = RN32(1 / RN32(Sd * s_t)), or r = 0 when
+// Sd == 0 (signed zeros); a block holding NaN or Inf gets scale 0x7F and codes
+// 0x7. MXNorm over NVFP4 takes G from the same 16-element blocks (K = D / 16)
+// and y = RN32(RN32(x * gamma) * inv) as for MX.
+//
+// One wavefront per row (D <= 8192), 4 rows per workgroup. A block is one lane
+// pair (8 elements each), so its maximum is one DPP step; the statistic adds
+// each lane's pair terms in chunk order, then the two pairs of a quad, then the
+// quads as the MX kernels do.
+struct Nvfp4Args {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* inv_out;
+  int64_t ldx;
+  int64_t T;
+  int D;
+  float Kf;
+  float Kinv;  // 1/K when K is a power of two, else 0
+  float p;
+  int pmode;
+  float k;     // RN32(1 / (6 s_t))
+  float s_t;
+};
+
+template <int NC, bool NORM, bool GAMMA>
+__global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nvfp4Args A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  if (row >= A.T) return;  // no barriers below
+  const uint16_t* xr = A.x + row * A.ldx;
+  const int dl = lane * 8;
+
+  uint4 graw[GAMMA ? NC : 1];
+  if (GAMMA) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) graw[c] = load16(A.gamma + min(c * kChunk + dl, A.D - 8));
+  }
+  uint4 raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
+  // only the last chunk can end inside the row; its lanes past the end
+  // re-read the row's last 16 bytes and are left out of statistic and stores
+  auto in_row = [&](int c) { return c < NC - 1 || c * kChunk + dl < A.D; };
+
+  Normaliser N = plain_normaliser(1.0f);
+  if constexpr (NORM) {
+    uint32_t mb[NC];  // the lane pair's block maximum of |x| as bf16 bits
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t m = in_row(c) ? absmax_bits8(raw[c]) : 0u;
+      mb[c] = max(m, dpp<kDppQuadSwap1>(m));
+    }
+    auto total = [&](int shift) {
+      float t;
+      auto blk = [&](int c) { return mb[c]; };
+      if (A.pmode == P_TWO)
+        t = lane_terms_p<NC, P_TWO>(0, NC, blk, shift, A.p);
+      else if (A.pmode == P_ONE)
+        t = lane_terms_p<NC, P_ONE>(0, NC, blk, shift, A.p);
+      else
+        t = lane_terms_p<NC, P_GEN>(0, NC, blk, shift, A.p);
+      // both lanes of a pair hold the pair's terms: the quad's two pairs, then the quads
+      const uint32_t u = __float_as_uint(t);
+      return sum_over_quads(__uint_as_float(f32_add_bits(u, dpp<kDppQuadSwap2>(u))));
+    };
+    auto row_max = [&]() {
+      uint32_t m = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) m = max(m, mb[c]);
+      return max_over_quads(max(m, dpp<kDppQuadSwap2>(m)));
+    };
+    N = row_normaliser(total, row_max, A.pmode, A.p, A.Kf, A.Kinv);
+    if (lane == 0 && A.inv_out) A.inv_out[row] = N.inv;
+  }
+
+  const uint64_t crow = (uint64_t)row * (uint64_t)(A.D / 2);
+  const uint64_t srow = (uint64_t)row * (uint64_t)(A.D / 16);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v[8];
+    unpack8(raw[c], v);
+    if (GAMMA) {
+      float g[8];
+      unpack8(graw[c], g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] *= g[j];  // exact: two bf16 values
+    }
+    // the block's maximum of |v| (NaN-propagating), then of |y| by monotone rounding
+    float am = __builtin_fabsf(v[0]);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) am = __builtin_elementwise_maximum(am, __builtin_fabsf(v[j]));
+    am = __builtin_elementwise_maximum(am, __uint_as_float(dpp<kDppQuadSwap1>(__float_as_uint(am))));
+    float y[8];
+    float a;
+    if constexpr (NORM) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (v[j] * N.pre) * N.apply;
+      a = (am * N.pre) * N.apply;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = v[j];
+      a = am;
+    }
+    const bool bad = !(a <= 0x1.fffffep127f);  // NaN or Inf in the block
+    // scale byte: E4M3 RNE of min(RN32(a k), 448) (the convert does not saturate)
+    const float q = __builtin_fminf(a * A.k, 448.0f);
+    short2_t sp = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2_t{0, 0}, q, q, 1.0f, false);
+    uint32_t sc = (uint32_t)__builtin_bit_cast(uint32_t, sp) & 0xFFu;
+    const float Sd = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+    const float r = Sd == 0.0f ? 0.0f : 1.0f / (Sd * A.s_t);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] *= r;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+    if (bad) {
+      w = 0x77777777u;
+      sc = 0x7Fu;
+    }
+    if (in_row(c)) {
+      const int d = c * kChunk + dl;
+      store4_stream(A.codes + crow + (uint64_t)(d >> 1), w);
+      if ((lane & 1) == 0) A.scales[srow + (uint64_t)(d >> 4)] = (uint8_t)sc;
+    }
+  }
+}
+
+template <bool NORM, bool GAMMA>
+mxq_status dispatch_nvfp4(const Nvfp4Args& A, int nc, hipStream_t s) {
+  const unsigned grid = (unsigned)((A.T + kRowsPerBlock - 1) / kRowsPerBlock);
+  switch (nc) {
+#define MXQ_CASE(N)                                                                     \
+  case N:                                                                               \
+    hipLaunchKernelGGL((nvfp4_kernel<N, NORM, GAMMA>), dim3(grid), dim3(kThreads), 0, s, A); \
+    break;
+    MXQ_CASE(1) MXQ_CASE(2) MXQ_CASE(3) MXQ_CASE(4) MXQ_CASE(5) MXQ_CASE(6) MXQ_CASE(7)
+    MXQ_CASE(8) MXQ_CASE(9) MXQ_CASE(10) MXQ_CASE(11) MXQ_CASE(12) MXQ_CASE(13) MXQ_CASE(14)
+    MXQ_CASE(15) MXQ_CASE(16)
+#undef MXQ_CASE
+    default:
+      return MXQ_ERR_UNSUPPORTED;
+  }
+  MXQ_LAUNCH_CHECK();
+  return MXQ_OK;
+}
+
+// Validation and launch shared by the two NVFP4 entry points.
+mxq_status nvfp4_run(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T, int64_t D,
+                     bool norm, float p, float tensor_scale, uint8_t* codes, uint8_t* scales,
+                     float* inv_out, void* stream) {
+  if (T < 0 || D <= 0 || D % 32 != 0 || ldx < D) return MXQ_ERR_SHAPE;
+  if (!(tensor_scale >= 0x1p-32f && tensor_scale <= 0x1p32f)) return MXQ_ERR_ARG;  // also NaN
+  if (norm && !(p > 0.0f)) return MXQ_ERR_ARG;
+  if (D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
+  if (T == 0) return MXQ_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned(x, 16) || ldx % 8 != 0 || !aligned(codes, 16)) return MXQ_ERR_ALIGN;
+  if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
+  if (inv_out != nullptr && !aligned(inv_out, 4)) return MXQ_ERR_ALIGN;
+  if ((uint64_t)T * (uint64_t)D >= (1ull << 40)) return MXQ_ERR_UNSUPPORTED;
+  if ((T + kRowsPerBlock - 1) / kRowsPerBlock > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
+  Nvfp4Args A;
+  A.x = x;
+  A.gamma = gamma;
+  A.codes = codes;
+  A.scales = scales;
+  A.inv_out = inv_out;
+  A.ldx = ldx;
+  A.T = T;
+  A.D = (int)D;
+  const int64_t K = D / 16;
+  A.Kf = (float)K;
+  A.Kinv = (K & (K - 1)) == 0 ? 1.0f / (float)K : 0.0f;
+  A.p = p;
+  A.pmode = isinf(p) ? P_INF : (p == 1.0f ? P_ONE : (p == 2.0f ? P_TWO : P_GEN));
+  A.k = (float)(1.0 / (6.0 * (double)tensor_scale));
+  A.s_t = tensor_scale;
+  const int nc = (int)((D + kChunk - 1) / kChunk);
+  hipStream_t s = (hipStream_t)stream;
+  if (!norm) return dispatch_nvfp4<false, false>(A, nc, s);
+  return gamma ? dispatch_nvfp4<true, true>(A, nc, s) : dispatch_nvfp4<true, false>(A, nc, s);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI
@@ -1408,5 +1603,17 @@ const char* mxq_strerror(mxq_status status) {
 }
 
 int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+mxq_status nvfp4_cast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D,
+                          float tensor_scale, uint8_t* codes, uint8_t* scales, void* stream) {
+  return nvfp4_run(x, ldx, nullptr, T, D, false, 2.0f, tensor_scale, codes, scales, nullptr,
+                   stream);
+}
+
+mxq_status mxnorm_nvfp4_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
+                            int64_t D, float p, float tensor_scale, uint8_t* codes,
+                            uint8_t* scales, float* inv_norm, void* stream) {
+  return nvfp4_run(x, ldx, gamma, T, D, true, p, tensor_scale, codes, scales, inv_norm, stream);
+}
 
 }  // extern "C"

@@ -64,6 +64,9 @@ CASES = (
     ("mxfp4 mxnorm e2m1", "mxfp4", "mxnorm", {"elem": mxq.MXQ_E2M1}),
     ("mxfp4 mxnorm e2m1 split rows", "mxfp4", "mxnorm",
      {"elem": mxq.MXQ_E2M1, "flags": mxq.MXQ_FLAG_FORCE_SPLIT}),
+    # the same rows in NVFP4 (16-element blocks, E4M3 scales, tensor scale 1)
+    ("mxfp4 mxnorm nvfp4", "mxfp4", "nvfp4", {}),
+    ("mxfp4 nvfp4 cast", "mxfp4", "nvfp4_cast", {}),
     ("llama3_8b_preattn backward dx+dgamma", "llama3_8b_preattn", "backward", {}),
     ("llama3_8b_preattn backward dx only", "llama3_8b_preattn", "backward", {"dgamma": False}),
     ("mxfp4 backward dx+dgamma", "mxfp4", "backward", {}),
@@ -95,6 +98,8 @@ def algorithmic_bytes(op, T, D, elem):
         return T * (2 * D + 2 * D + 2 * D + 4)
     if op == "two_pass":
         return T * (2 * D + 2 * D + 2 * D + code + D // 32)
+    if op in ("nvfp4", "nvfp4_cast"):
+        return T * (2 * D + D // 2 + D // 16)   # E2M1 codes, one E4M3 byte per 16
     return T * (2 * D + code + D // 32)
 
 
@@ -211,10 +216,12 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
     rng = mxq.mxq_rng(workloads.SR_SEED, workloads.SR_OFFSET)
     x_bytes = x0.numel() * 2
     R = max(2, min(10, -(-(1 << 30) // x_bytes)))      # >= 1 GB of inputs in rotation
-    cb = D // 2 if elem == mxq.MXQ_E2M1 else D
+    nv = op in ("nvfp4", "nvfp4_cast")
+    cb = D // 2 if (elem == mxq.MXQ_E2M1 or nv) else D
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
     codes = [torch.empty((T, cb), dtype=torch.uint8, device="cuda") for _ in range(R)]
-    scales = [torch.empty((T, D // 32), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    scales = [torch.empty((T, D // 16 if nv else D // 32), dtype=torch.uint8, device="cuda")
+              for _ in range(R)]
     invs = [torch.empty((T,), dtype=torch.float32, device="cuda") for _ in range(R)]
     ys = ([torch.empty((T, D), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
           if op in ("two_pass", "backward") else None)
@@ -254,6 +261,11 @@ def run_case(torch, name, wl, op, opt, steps, warmup):
             st = L.rmsnorm_mxcast_fwd(xp, D, gp, T, D, ctypes.c_float(1e-5), elem, rnd, rngp,
                                       opt.get("flags", 0), vp(ys[k].data_ptr()), cp, sp, ip,
                                       stream)
+        elif op == "nvfp4":
+            st = L.mxnorm_nvfp4_fwd(xp, D, gp, T, D, ctypes.c_float(opt.get("p", 2.0)),
+                                    ctypes.c_float(1.0), cp, sp, ip, stream)
+        elif op == "nvfp4_cast":
+            st = L.nvfp4_cast_fwd(xp, D, T, D, ctypes.c_float(1.0), cp, sp, stream)
         elif op == "floor":
             st = floor_lib().mxq_floor_stream(xp, gp, T, D, cp, sp, opt["variant"], stream)
         else:

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_messages():
-    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 3
+    assert mxq.mxq_abi_version() == mxq.ABI_VERSION == 4
     for st in range(7):
         assert isinstance(mxq.mxq_strerror(st), str) and mxq.mxq_strerror(st)
     assert mxq.mxq_strerror(99) == "unknown status"
@@ -80,6 +80,47 @@ def cast(**kw):
     a.update(kw)
     return mxq.mxcast_fwd(a["x"], a["ldx"], a["T"], a["D"], a["elem"], a["rnd"], a["rng"],
                           a["flags"], a["codes"], a["scales"], a["stream"])
+
+
+def nvcast(**kw):
+    a = dict(x=A16, ldx=4096, T=8, D=4096, ts=1.0, codes=A16, scales=A16, stream=None)
+    a.update(kw)
+    return mxq.nvfp4_cast_fwd(a["x"], a["ldx"], a["T"], a["D"], a["ts"], a["codes"], a["scales"],
+                              a["stream"])
+
+
+def nvnorm(**kw):
+    a = dict(x=A16, ldx=4096, gamma=None, T=8, D=4096, p=2.0, ts=1.0, codes=A16, scales=A16,
+             inv=None, stream=None)
+    a.update(kw)
+    return mxq.mxnorm_nvfp4_fwd(a["x"], a["ldx"], a["gamma"], a["T"], a["D"], a["p"], a["ts"],
+                                a["codes"], a["scales"], a["inv"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [nvcast, nvnorm])
+def test_nvfp4_argument_errors(call):
+    assert call(D=0) == mxq.MXQ_ERR_SHAPE
+    assert call(D=4000 + 16) == mxq.MXQ_ERR_SHAPE
+    assert call(T=-1) == mxq.MXQ_ERR_SHAPE
+    assert call(ldx=2048) == mxq.MXQ_ERR_SHAPE
+    for ts in (0.0, -1.0, float("nan"), float("inf"), 2.0 ** -33, 2.0 ** 33):
+        assert call(ts=ts) == mxq.MXQ_ERR_ARG, ts
+    assert call(D=8224, ldx=8224) == mxq.MXQ_ERR_UNSUPPORTED   # one wavefront per row: D <= 8192
+    assert call(x=None) == mxq.MXQ_ERR_NULL
+    assert call(codes=None) == mxq.MXQ_ERR_NULL
+    assert call(scales=None) == mxq.MXQ_ERR_NULL
+    assert call(x=A8) == mxq.MXQ_ERR_ALIGN
+    assert call(codes=A8) == mxq.MXQ_ERR_ALIGN
+    assert call(ldx=4100) == mxq.MXQ_ERR_ALIGN
+    assert call(T=0, x=None, codes=None, scales=None) == mxq.MXQ_OK    # empty: nothing to do
+    assert call(T=1 << 34, D=32, ldx=32) == mxq.MXQ_ERR_UNSUPPORTED
+
+
+def test_mxnorm_nvfp4_argument_errors():
+    for p in (0.0, -1.0, float("nan")):
+        assert nvnorm(p=p) == mxq.MXQ_ERR_ARG
+    assert nvnorm(gamma=A8) == mxq.MXQ_ERR_ALIGN
+    assert nvnorm(inv=A16 + 2) == mxq.MXQ_ERR_ALIGN
 
 
 @pytest.mark.parametrize("call", [norm, rms, rms_fused, cast])

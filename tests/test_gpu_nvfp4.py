@@ -1,0 +1,193 @@
+"""NVFP4 on the GPU against the oracle: the plain cast bit-exact, and MXNorm
+over NVFP4 blocks bit-exact in the oracle's injected mode (I) and within the
+reference mode's (R) tolerance. Calls go through the C ABI (the binding's
+nvfp4_cast / mxnorm_nvfp4 only allocate and marshal)."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import norm_mx_quantisation_amd as mxq
+import oracle
+from norm_mx_quantisation_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+THREADS = min(16, os.cpu_count() or 1)
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _e2m1_values():
+    tab = {}
+    for line in open(os.path.join(GOLDEN, "e2m1_values.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            c, v = line.split()
+            tab[int(c, 0)] = float(v)
+    return np.array([tab[c] for c in range(16)])
+
+
+E2M1 = _e2m1_values()
+E4M3 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def np_(t):
+    return t.cpu().numpy()
+
+
+def host(t):
+    return t.cpu() if t is not None else None
+
+
+def dequant(codes, scales, ts):
+    """Decoded values [T, D] (NaN for a 0x7F scale)."""
+    lo, hi = E2M1[codes & 0xF], E2M1[codes >> 4]
+    v = np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+    return v * np.repeat(E4M3[scales], 16, axis=1) * ts
+
+
+def assert_same(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    bad = np.argwhere(a != b)
+    assert bad.size == 0, f"{what}: {len(bad)} of {a.size} differ, first at {bad[:3].tolist()}"
+
+
+def check_cast(x, ts=1.0, what=""):
+    c, s = mxq.nvfp4_cast(x, ts)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.nvfp4_cast(host(x), ts, threads=THREADS)
+    assert_same(np_(s), os_, f"{what} scales")
+    assert_same(np_(c), oc, f"{what} codes")
+    return np_(c), np_(s)
+
+
+def check_norm(x, g, p, ts=1.0, what="", ref=True):
+    """Kernel against mode (I) (every row whose normaliser is finite) bit-exactly,
+    and against mode (R): normaliser within 1e-5, dequantised values equal
+    except on at most 0.1% of elements, each within one E2M1 step at the
+    larger of the two block scales."""
+    c, s, inv = mxq.mxnorm_nvfp4(x, g, p, ts)
+    torch.cuda.synchronize()
+    c, s, inv = np_(c), np_(s), np_(inv)
+    xs, gs = host(x), host(g)
+    fin = ~np.isposinf(inv)
+    if fin.any():
+        rows = np.flatnonzero(fin)
+        ic, is_, _ = oracle.mxnorm_nvfp4(xs[rows], gs, p, ts, inv_inject=inv[rows], threads=THREADS)
+        assert_same(s[rows], is_, f"{what} (I) scales")
+        assert_same(c[rows], ic, f"{what} (I) codes")
+    if not ref:
+        return c, s, inv
+    rc, rs, rinv = oracle.mxnorm_nvfp4(xs, gs, p, ts, threads=THREADS)
+    ok = np.isfinite(rinv) & np.isfinite(inv)
+    assert (np.isnan(inv) == np.isnan(rinv)).all(), what
+    big = ok & (rinv <= 3.4e38)
+    assert np.allclose(inv[big], rinv[big], rtol=1e-5, atol=0), what
+    a, b = dequant(c, s, ts), dequant(rc, rs, ts)
+    both = np.isfinite(a) & np.isfinite(b)
+    assert (np.isnan(a) == np.isnan(b)).all(), what
+    diff = both & (a != b)
+    n = a.size
+    assert diff.sum() <= math.ceil(1e-3 * n), (what, diff.sum(), n)
+    if diff.any():
+        sc = np.maximum(np.repeat(E4M3[s], 16, axis=1), np.repeat(E4M3[rs], 16, axis=1)) * ts
+        step = np.where(np.maximum(np.abs(a), np.abs(b)) / sc <= 2, 0.5, 2.0) * sc
+        assert (np.abs(a - b)[diff] <= step[diff] * (1 + 1e-6)).all(), what
+    return c, s, inv
+
+
+@pytest.mark.parametrize("D", [32, 96, 512, 4096, 8192])
+@pytest.mark.parametrize("ts", [1.0, 0.375, 3000.0])
+def test_nvfp4_cast_shapes(D, ts):
+    x = workloads.random_rows(7, D, seed=500 + D, scale=2.0, device=DEV)
+    x[3, : min(D, 64)] *= 1e4
+    check_cast(x, ts, f"cast D={D} ts={ts}")
+
+
+def test_nvfp4_cast_special_values_and_saturation():
+    x = workloads.random_rows(6, 512, seed=501).clone()
+    x[0] = 0.0
+    x[0, 7] = -0.0
+    x[1, 17] = float("nan")
+    x[2, 100] = float("inf")
+    x[2, 200] = float("-inf")
+    x[3] = x[3] * 2.0 ** -133                     # bf16 subnormals: scale 0
+    x[4] = x[4] * 1e36                            # scale saturates at 448
+    c, s = check_cast(x.to(DEV), 1.0, "cast special")
+    assert (s[1, 1] == 0x7F) and (s[2, 6] == 0x7F) and (s[2, 12] == 0x7F)
+    assert (s[0] == 0).all() and (s[3] == 0).all() and (s[4] == 0x7E).all()
+
+
+def test_nvfp4_cast_strided_rows():
+    x = workloads.random_rows(9, 1024, seed=502, device=DEV, ldx=1056)
+    a = check_cast(x, 1.0, "cast strided")
+    b = mxq.nvfp4_cast(x.contiguous(), 1.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0], np_(b[0])) and np.array_equal(a[1], np_(b[1]))
+
+
+@pytest.mark.parametrize("D", [32, 96, 512, 4096, 8192])
+@pytest.mark.parametrize("p", [1.0, 2.0, 3.5, math.inf])
+def test_mxnorm_nvfp4_shapes_and_p(D, p):
+    x = workloads.random_rows(5, D, seed=510 + D, device=DEV)
+    x[1, : min(D, 64)] *= 30.0
+    g = workloads.random_gamma(D, seed=511, device=DEV)
+    check_norm(x, g, p, 1.0, f"mxnorm-nvfp4 D={D} p={p}")
+    check_norm(x, None, p, 1.0, f"mxnorm-nvfp4 D={D} p={p} no gamma")
+
+
+@pytest.mark.parametrize("ts", [0.375, 3000.0, 2.0 ** -20])
+def test_mxnorm_nvfp4_tensor_scales(ts):
+    x = workloads.random_rows(33, 4096, seed=512, device=DEV)
+    g = workloads.random_gamma(4096, seed=513, device=DEV)
+    check_norm(x, g, 2.0, ts, f"mxnorm-nvfp4 ts={ts}")
+
+
+def test_mxnorm_nvfp4_special_rows():
+    x = workloads.random_rows(7, 512, seed=514).clone()
+    x[0] = 0.0
+    x[1, 17] = float("nan")
+    x[2, 100] = float("inf")
+    x[3] = x[3] * 1e30
+    x[4, :32] = 0.0
+    x[5] = x[5] * 2.0 ** -131                     # normaliser past the fp32 range (inv = +Inf)
+    g = workloads.random_gamma(512, seed=515)
+    for gam in (None, g):
+        gd = None if gam is None else gam.to(DEV)
+        c, s, inv = check_norm(x.to(DEV), gd, 2.0, 1.0, f"nvfp4 special gamma={gam is not None}")
+        assert inv[0] == 0 and (s[0] == 0).all()
+        assert math.isnan(inv[1]) and (s[1] == 0x7F).all()
+        assert math.isnan(inv[2]) and (s[2] == 0x7F).all()
+        assert np.isposinf(inv[5]) and (s[5] != 0x7F).all()
+        # MXNorm is invariant under x -> 2^64 x: the tiny row's bits equal the scaled row's
+        xs = (x[5:6].float() * 2.0 ** 64).to(torch.bfloat16)
+        c2, s2, inv2 = mxq.mxnorm_nvfp4(xs.to(DEV), gd, 2.0, 1.0)
+        torch.cuda.synchronize()
+        assert np.isfinite(np_(inv2)).all()
+        assert np.array_equal(c[5:6], np_(c2)) and np.array_equal(s[5:6], np_(s2))
+
+
+def test_mxnorm_nvfp4_mxfp4_workload_rows():
+    # the mxfp4 workload's rows [32768, 4096] (1% outlier channels x20) in three
+    # 2048-row windows spread over the tensor, both modes
+    x, g = workloads.make_inputs("mxfp4", device=DEV)
+    T = x.shape[0]
+    c, s, inv = mxq.mxnorm_nvfp4(x, g, 2.0, 1.0)
+    torch.cuda.synchronize()
+    for r0 in (0, T // 2 - 1024, T - 2048):
+        xr = x[r0:r0 + 2048]
+        cr, sr, ir = check_norm(xr, g, 2.0, 1.0, f"mxfp4 rows {r0}")
+        assert np.array_equal(cr, np_(c[r0:r0 + 2048])) and np.array_equal(sr, np_(s[r0:r0 + 2048]))
+    check_cast(x[:4096], 1.0, "mxfp4 cast rows")
+
+
+def test_nvfp4_empty_input():
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
+    c, s = mxq.nvfp4_cast(x)
+    c2, s2, inv = mxq.mxnorm_nvfp4(x)
+    torch.cuda.synchronize()
+    assert c.shape == (0, 128) and s.shape == (0, 16) and inv.shape == (0,)
