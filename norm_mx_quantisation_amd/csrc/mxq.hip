@@ -1305,8 +1305,8 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
 // 0x7. MXNorm over NVFP4 takes G from the same 16-element blocks (K = D / 16)
 // and y = RN32(RN32(x * gamma) * inv) as for MX.
 //
-// One wavefront per row (D <= 8192), 4 rows per workgroup. A block is one lane
-// pair (8 elements each), so its maximum is one DPP step; the statistic adds
+// One wavefront per row (D <= 8192), 4 rows per workgroup, the gains staged in
+// LDS. A block is one lane pair (8 elements each), so its maximum is one DPP step; the statistic adds
 // each lane's pair terms in chunk order, then the two pairs of a quad, then the
 // quads as the MX kernels do.
 struct Nvfp4Args {
@@ -1328,21 +1328,34 @@ struct Nvfp4Args {
 
 template <int NC, bool NORM, bool GAMMA>
 __global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nvfp4Args A) {
+  // r for every finite scale byte: RN32(1 / RN32(Sd * s_t)), 0 for Sd == 0,
+  // computed once per workgroup (a correctly rounded division each); the
+  // gains staged as fp32 in LDS, as in mxnorm_reg_kernel
+  __shared__ float rtab[128];
+  __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
-  if (row >= A.T) return;  // no barriers below
-  const uint16_t* xr = A.x + row * A.ldx;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
   const int dl = lane * 8;
 
-  uint4 graw[GAMMA ? NC : 1];
-  if (GAMMA) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) graw[c] = load16(A.gamma + min(c * kChunk + dl, A.D - 8));
-  }
+  GammaStage<GAMMA ? NC : 1, kThreads> gs;
+  if (GAMMA) gs.load(A.gamma, A.D);
+  __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
   uint4 raw[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
+  __builtin_amdgcn_sched_barrier(0);
+  if (threadIdx.x < 128) {
+    const float Sd = __builtin_amdgcn_cvt_f32_fp8((int)threadIdx.x, 0);
+    rtab[threadIdx.x] = (threadIdx.x == 0 || threadIdx.x == 0x7F) ? 0.0f : 1.0f / (Sd * A.s_t);
+  }
+  if (GAMMA)
+    gs.store(g_lds);  // includes the workgroup barrier
+  else
+    __syncthreads();
+  if (!live) return;  // no barriers below
   // only the last chunk can end inside the row; its lanes past the end
   // re-read the row's last 16 bytes and are left out of statistic and stores
   auto in_row = [&](int c) { return c < NC - 1 || c * kChunk + dl < A.D; };
@@ -1386,7 +1399,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nvfp4Args A) {
     unpack8(raw[c], v);
     if (GAMMA) {
       float g[8];
-      unpack8(graw[c], g);
+      gains(g_lds, c, lane, g);
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] *= g[j];  // exact: two bf16 values
     }
@@ -1410,9 +1423,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(Nvfp4Args A) {
     // scale byte: E4M3 RNE of min(RN32(a k), 448) (the convert does not saturate)
     const float q = __builtin_fminf(a * A.k, 448.0f);
     short2_t sp = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2_t{0, 0}, q, q, 1.0f, false);
-    uint32_t sc = (uint32_t)__builtin_bit_cast(uint32_t, sp) & 0xFFu;
-    const float Sd = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
-    const float r = Sd == 0.0f ? 0.0f : 1.0f / (Sd * A.s_t);
+    uint32_t sc = (uint32_t)__builtin_bit_cast(uint32_t, sp) & 0x7Fu;  // q >= 0 (or NaN: bad)
+    const float r = rtab[sc];
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] *= r;
