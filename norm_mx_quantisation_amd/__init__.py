@@ -318,6 +318,18 @@ def mxcast(x, fmt: str = "e4m3", rounding: str = "rne", seed: int = 0, offset: i
     return codes, scales
 
 
+def mx_views(codes, scales, fmt: str = "e4m3"):
+    """torch dtype views of the uint8 outputs, no copy: E4M3 codes as float8_e4m3fn, packed
+    E2M1 codes as float4_e2m1fn_x2 (two elements per byte, element 2j in the low nibble), E8M0
+    scales as float8_e8m0fnu, NVFP4's E4M3 scales (fmt "nvfp4") as float8_e4m3fn."""
+    import torch
+    if fmt not in ("e4m3", "e2m1", "nvfp4"):
+        raise ValueError('fmt must be "e4m3", "e2m1" or "nvfp4"')
+    cv = codes.view(torch.float8_e4m3fn) if fmt == "e4m3" else codes.view(torch.float4_e2m1fn_x2)
+    sv = scales.view(torch.float8_e4m3fn) if fmt == "nvfp4" else scales.view(torch.float8_e8m0fnu)
+    return cv, sv
+
+
 def _nvfp4_outputs(x, T, D, out, want_inv):
     import torch
     if out is None:

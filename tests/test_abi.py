@@ -375,3 +375,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         mxq.lib()
     with pytest.raises(RuntimeError, match="not built"):
         mxq.mxq_abi_version()
+
+
+def test_mx_views_are_the_torch_float8_and_float4_types():
+    # the binding's dtype views of the uint8 outputs decode to the format values
+    import torch
+    codes = torch.tensor([[0x38, 0xB8, 0x7E, 0x01]], dtype=torch.uint8)
+    scales = torch.tensor([[127, 130]], dtype=torch.uint8)
+    cv, sv = mxq.mx_views(codes, scales, "e4m3")
+    assert cv.dtype == torch.float8_e4m3fn and sv.dtype == torch.float8_e8m0fnu
+    assert cv.float().tolist() == [[1.0, -1.0, 448.0, 2.0 ** -9]]
+    assert sv.float().tolist() == [[1.0, 8.0]]
+    packed = torch.tensor([[0x72, 0x0F]], dtype=torch.uint8)   # (1.0, 6.0), (-6.0, 0.0)
+    cv, _ = mxq.mx_views(packed, scales, "e2m1")
+    assert cv.dtype == torch.float4_e2m1fn_x2
+    nv = torch.tensor([[0x38]], dtype=torch.uint8)
+    _, sv = mxq.mx_views(packed, nv, "nvfp4")
+    assert sv.dtype == torch.float8_e4m3fn and sv.float().item() == 1.0
+    with pytest.raises(ValueError):
+        mxq.mx_views(codes, scales, "e5m2")
