@@ -9,7 +9,7 @@
 // and accumulate in fp32. (With register operands it and its 16 x 16 x 128
 // sibling both issue at about 4.5 PFLOP/s with 8-bit operands; the 32 x 32 x
 // 64 form needs a quarter of the accumulators and half the instructions and
-// scale operands for a 128 x 128 wave tile.)
+// scale operands for a 128 x 64 wave tile.)
 //
 // Either operand may be E2M1 (FP4, packed two to a byte, element 2j in the
 // low nibble): the same instruction with format code 4 runs FP4 operands at
@@ -28,6 +28,7 @@
 // in the low nibble: exactly 16 consecutive bytes of a packed E2M1 row.
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <atomic>
@@ -44,7 +45,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;   // 4 waves, 2 x 2 over the tile
+// 8 waves, 2 x 4 over the tile, 128 x 64 each: two waves per SIMD, so one
+// wave's MFMAs run while the other waits on its LDS reads. (Four waves of
+// 128 x 128, one per SIMD with all 256 accumulation registers, left the
+// matrix pipe idle at every such wait: 8-9% slower on MXFP8, 3-4% on MXFP4.)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 256;        // tile rows (A)
 constexpr int kBN = 256;        // tile columns (B rows)
 constexpr int kBK = 128;        // K per step: 4 MX blocks, two MFMAs deep
@@ -92,6 +98,10 @@ struct Stage {
   uint32_t sa[kBM];
   uint32_t sb[kBN];
 };
+// the bf16 epilogue stages 8 KB per wave across a stage's a and b arrays
+static_assert(offsetof(Stage, b) == sizeof(uint4) * kBM * kChunks &&
+                  sizeof(uint4) * (kBM + kBN) * kChunks >= kWaves * 8192,
+              "a stage's code arrays hold the epilogue's slots");
 
 __device__ __forceinline__ int scale_row(int p) {
   return (p >> 7) * 128 + (p & 3) * 32 + ((p >> 2) & 31);
@@ -114,13 +124,14 @@ constexpr int kSpread = 4;
 // Direct-to-LDS loads of one operand's K step, CH chunks per row: a wave
 // instruction moves 64 x 16 bytes = 64 / CH rows; lane i lands at position
 // i, i.e. row i / CH, physical chunk i % CH, so it fetches logical chunk
-// (i % CH) ^ swz(row). Each wave moves CH such instructions. Rows past the
-// matrix end re-read its last row (their results are never stored).
+// (i % CH) ^ swz(row). Each of the 8 waves moves CH / 2 such instructions
+// (256 rows in all). Rows past the matrix end re-read its last row (their
+// results are never stored).
 template <int CH>
 __device__ __forceinline__ void load_one(const uint8_t* base, int64_t ld, int rows_valid,
                                          uint4* dst, int r0, int ks, int wave, int lane, int q) {
   constexpr int kRows = kWave / CH;
-  const int blk = wave * CH + q;
+  const int blk = wave * (CH / 2) + q;
   const int r = blk * kRows + lane / CH;
   const int c = (lane % CH) ^ swz<CH>(r);
   __builtin_amdgcn_global_load_lds(
@@ -132,7 +143,7 @@ template <int CH>
 __device__ __forceinline__ void load_operand(const uint8_t* base, int64_t ld, int rows_valid,
                                              uint4* dst, int r0, int ks, int wave, int lane) {
 #pragma unroll
-  for (int q = 0; q < CH; ++q) load_one<CH>(base, ld, rows_valid, dst, r0, ks, wave, lane, q);
+  for (int q = 0; q < CH / 2; ++q) load_one<CH>(base, ld, rows_valid, dst, r0, ks, wave, lane, q);
 }
 
 // Piece `piece` (of kSpread) of a step's code DMA: its share of the A then
@@ -140,43 +151,51 @@ __device__ __forceinline__ void load_operand(const uint8_t* base, int64_t ld, in
 template <int FA, int FB>
 __device__ __forceinline__ void load_codes_piece(const GemmArgs& G, Stage* S, int m0, int n0,
                                                  int ks, int wave, int lane, int piece) {
-  constexpr int CA = chunks_of<FA>(), CB = chunks_of<FB>();
+  constexpr int CA = chunks_of<FA>() / 2, CB = chunks_of<FB>() / 2;
 #pragma unroll
   for (int t = 0; t < CA + CB; ++t) {
     if (t * kSpread / (CA + CB) != piece) continue;
     if (t < CA)
-      load_one<CA>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane, t);
+      load_one<2 * CA>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane, t);
     else
-      load_one<CB>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane, t - CA);
+      load_one<2 * CB>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane, t - CA);
   }
 }
 
 // Scale group gk (K steps kScaleSteps gk ...) of the tile's rows: lane i of
-// wave w moves row w * 64 + i's 16 bytes. Needs 16-byte aligned scale rows
-// with at least 16 (gk + 1) bytes.
+// wave w < 4 moves A row w * 64 + i's 16 bytes, of wave w >= 4 B row
+// (w - 4) * 64 + i's. Needs 16-byte aligned scale rows with at least
+// 16 (gk + 1) bytes.
 __device__ __forceinline__ void load_scale_group(const GemmArgs& G, ScaleGroup* SG, int m0, int n0,
                                                  int gk, int wave, int lane) {
-  const int r = wave * kWave + lane;
-  __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + r, G.M - 1) * G.ldsa + gk * 16),
-                                   (lds_void*)&SG->a[wave * kWave], 16, 0, 0);
-  __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + r, G.N - 1) * G.ldsb + gk * 16),
-                                   (lds_void*)&SG->b[wave * kWave], 16, 0, 0);
+  if (wave < 4) {
+    const int r = wave * kWave + lane;
+    __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + r, G.M - 1) * G.ldsa + gk * 16),
+                                     (lds_void*)&SG->a[wave * kWave], 16, 0, 0);
+  } else {
+    const int r = (wave - 4) * kWave + lane;
+    __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + r, G.N - 1) * G.ldsb + gk * 16),
+                                     (lds_void*)&SG->b[(wave - 4) * kWave], 16, 0, 0);
+  }
 }
 
 // A whole step's codes and, step by step (GROUPED false), its scales: 4
 // bytes (the step's 4 blocks) per row; lane i of wave w fills position
-// w * 64 + i.
+// (w % 4) * 64 + i of A's scales (w < 4) or B's (w >= 4).
 template <int FA, int FB, bool GROUPED>
 __device__ __forceinline__ void load_stage(const GemmArgs& G, Stage* S, int m0, int n0, int ks,
                                            int wave, int lane) {
   load_operand<chunks_of<FA>()>(G.a, G.lda, G.M, S->a, m0, ks, wave, lane);
   load_operand<chunks_of<FB>()>(G.b, G.ldb, G.N, S->b, n0, ks, wave, lane);
   if (GROUPED) return;
-  const int rs = scale_row(wave * kWave + lane);
-  __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + rs, G.M - 1) * G.ldsa + ks * 4),
-                                   (lds_void*)&S->sa[wave * kWave], 4, 0, 0);
-  __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + rs, G.N - 1) * G.ldsb + ks * 4),
-                                   (lds_void*)&S->sb[wave * kWave], 4, 0, 0);
+  const int w4 = wave & 3;
+  const int rs = scale_row(w4 * kWave + lane);
+  if (wave < 4)
+    __builtin_amdgcn_global_load_lds((const void*)(G.sa + (int64_t)min(m0 + rs, G.M - 1) * G.ldsa + ks * 4),
+                                     (lds_void*)&S->sa[w4 * kWave], 4, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((const void*)(G.sb + (int64_t)min(n0 + rs, G.N - 1) * G.ldsb + ks * 4),
+                                     (lds_void*)&S->sb[w4 * kWave], 4, 0, 0);
 }
 
 // The MFMA operand of lane (row r, half g) for the K half kk of the step.
@@ -203,11 +222,11 @@ __device__ __forceinline__ uint4 scale_words(const uint32_t* sc, int h, int rl) 
 // requires the other bytes to be zero).
 __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >> (8 * b)) & 0xFFu); }
 
-// One K step of the wave's 128 x 128 quarter: the next step's DMA into
+// One K step of the wave's 128 x 64 eighth: the next step's DMA into
 // `fill`, then this step's operands from `use` into the MFMAs, in two K
 // halves of 64 (the MX blocks 2 kk and 2 kk + 1 of the step). Per half, the
-// 4 B operands are read first and the A operand one 32-row block ahead of
-// the 4 MFMAs that use it, so the reads overlap the MFMAs. That `use` has
+// 2 B operands are read first and the A operand one 32-row block ahead of
+// the 2 MFMAs that use it, so the reads overlap the MFMAs. That `use` has
 // landed is the caller's wait and barrier.
 //
 // GROUPED: `fill` and `use` are two distinct LDS objects known at compile
@@ -221,7 +240,7 @@ __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >
 template <int FA, int FB, bool GROUPED>
 __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Stage* use, int fm0,
                                        int fn0, int fks, int wave, int lane, int wm, int wn,
-                                       v16f (&acc)[4][4], const ScaleGroup* sg, int sstep,
+                                       v16f (&acc)[4][2], const ScaleGroup* sg, int sstep,
                                        ScaleGroup* sg_fill, int sm0, int sn0, int sgk) {
   constexpr int CA = chunks_of<FA>(), CB = chunks_of<FB>();
   if (!GROUPED) {
@@ -233,23 +252,23 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
   if (GROUPED) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sbw4[j] = reinterpret_cast<const uint32_t*>(&sg->b[wn * 128 + j * 32 + rl])[sstep];
+      if (j < 2) sbw4[j] = reinterpret_cast<const uint32_t*>(&sg->b[wn * 64 + j * 32 + rl])[sstep];
       saw4[j] = reinterpret_cast<const uint32_t*>(&sg->a[wm * 128 + j * 32 + rl])[sstep];
     }
     if (sg_fill) load_scale_group(G, sg_fill, sm0, sn0, sgk, wave, lane);
   } else {
-    const uint4 sbw = scale_words(use->sb, wn, rl);
+    const uint2 sbw = *reinterpret_cast<const uint2*>(use->sb + (wn >> 1) * 128 + rl * 4 + (wn & 1) * 2);
     const uint4 saw = scale_words(use->sa, wm, rl);
-    sbw4[0] = sbw.x, sbw4[1] = sbw.y, sbw4[2] = sbw.z, sbw4[3] = sbw.w;
+    sbw4[0] = sbw.x, sbw4[1] = sbw.y, sbw4[2] = 0, sbw4[3] = 0;
     saw4[0] = saw.x, saw4[1] = saw.y, saw4[2] = saw.z, saw4[3] = saw.w;
   }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    v8i bo[4];
-    int sbv[4];
+    v8i bo[2];
+    int sbv[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bo[j] = operand<CB>(use->b, wn * 128 + j * 32 + rl, kk, g);
+    for (int j = 0; j < 2; ++j) {
+      bo[j] = operand<CB>(use->b, wn * 64 + j * 32 + rl, kk, g);
       sbv[j] = scale_byte(sbw4[j], 2 * kk + g);
     }
     v8i ao = operand<CA>(use->a, wm * 128 + rl, kk, g);
@@ -261,7 +280,7 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
       const int sav = scale_byte(saw4[i], 2 * kk + g);
       // B is the first operand, so each lane's results are consecutive columns of C
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo[j], ao, acc[i][j], FB, FA,
                                                                     0, sbv[j], 0, sav);
       if (i + 1 < 4) ao = ao_next;
@@ -311,18 +330,18 @@ __device__ __forceinline__ void store4(void* c, int64_t off, const v4f& v) {
 // are cleared for the next tile.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(const GemmArgs& G, int m0, int n0, int wm, int wn,
-                                           int lane, v16f (&acc)[4][4]) {
+                                           int lane, v16f (&acc)[4][2]) {
   const int g = lane >> 5, rl = lane & 31;
   if (G.vec && m0 + kBM <= G.M && n0 + kBN <= G.N) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = m0 + wm * 128 + i * 32 + rl;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const v16f& a = acc[i][j];
-          store4<OUT_BF16>(G.c, row * G.ldc + n0 + wn * 128 + j * 32 + 8 * q + 4 * g,
+          store4<OUT_BF16>(G.c, row * G.ldc + n0 + wn * 64 + j * 32 + 8 * q + 4 * g,
                            v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});
         }
     }
@@ -331,10 +350,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& G, int m0, int n0, in
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + wm * 128 + i * 32 + rl;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * g;
+          const int col = n0 + wn * 64 + j * 32 + 8 * q + 4 * g;
           const v16f& a = acc[i][j];
           const v4f v = v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
           if (G.vec && row < G.M && col + 3 < G.N) {
@@ -356,54 +375,53 @@ __device__ __forceinline__ void store_tile(const GemmArgs& G, int m0, int n0, in
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 }
 
 // Epilogue of a whole bf16 tile through LDS. Stored straight from the
 // accumulators, each store instruction writes 8 bytes to each of 32 rows, so
 // every 128-byte line of C is assembled from 8 partial writes. Instead each
-// wave writes its 128 x 128 quarter, 64 rows at a time, into its own 16 KB
-// slot of a stage no wave reads any more (256 bytes per row; 16-byte group c
-// of slot row r at c ^ (r & 15), so the 16 rows a write instruction touches
-// land on distinct banks), then reads it back 16 contiguous bytes per lane
-// and stores whole lines: 4 rows of 256 bytes per instruction, non-temporal
-// (C is written once; streaming it keeps the operand panels in L2). A wave
-// reads back only what it wrote, and its LDS accesses complete in order.
+// wave writes its 128 x 64 eighth, 64 rows at a time, into its own 8 KB slot
+// of a stage no wave reads any more (128 bytes per row; 16-byte group c of
+// slot row r at c ^ (r & 7), which spreads rows of equal parity over the
+// banks), then reads it back 16 contiguous bytes per lane and stores whole
+// lines: 8 rows of 128 bytes per instruction, non-temporal (C is written
+// once; streaming it keeps the operand panels in L2). A wave reads back only
+// what it wrote, and its LDS accesses complete in order.
 __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& G, int m0, int n0, int wm,
-                                                    int wn, int wave, int lane, v16f (&acc)[4][4],
+                                                    int wn, int wave, int lane, v16f (&acc)[4][2],
                                                     uint4* stage) {
-  uint8_t* slot = reinterpret_cast<uint8_t*>(stage) + wave * 16384;
+  uint8_t* slot = reinterpret_cast<uint8_t*>(stage) + wave * 8192;
   const int g = lane >> 5, rl = lane & 31;
   uint16_t* C = static_cast<uint16_t*>(G.c);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int r = ii * 32 + rl;  // slot row; quarter row 64 h + r
+      const int r = ii * 32 + rl;  // slot row; wave-tile row 64 h + r
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const v16f& a = acc[2 * h + ii][j];
           const u32x2 w = {(uint32_t)bf16_rne(a[4 * q]) | ((uint32_t)bf16_rne(a[4 * q + 1]) << 16),
                            (uint32_t)bf16_rne(a[4 * q + 2]) | ((uint32_t)bf16_rne(a[4 * q + 3]) << 16)};
-          // columns j * 32 + 8 q + 4 g .. + 3: 16-byte group 4 j + q, half g
-          *reinterpret_cast<u32x2*>(slot + r * 256 + (((4 * j + q) ^ (r & 15)) << 4) + g * 8) = w;
+          *reinterpret_cast<u32x2*>(slot + r * 128 + (((4 * j + q) ^ (r & 7)) << 4) + g * 8) = w;
         }
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int r = 4 * k + (lane >> 4), c16 = lane & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(slot + r * 256 + ((c16 ^ (r & 15)) << 4));
+    for (int k = 0; k < 8; ++k) {
+      const int r = 8 * k + (lane >> 3), c16 = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(slot + r * 128 + ((c16 ^ (r & 7)) << 4));
       const int64_t row = m0 + wm * 128 + h * 64 + r;
       __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
-                                  reinterpret_cast<u32x4*>(C + row * G.ldc + n0 + wn * 128 + c16 * 8));
+                                  reinterpret_cast<u32x4*>(C + row * G.ldc + n0 + wn * 64 + c16 * 8));
     }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 }
 
 // Tile order: the 8 XCDs take workgroup ids round robin, so tile t is first
@@ -443,23 +461,23 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& G, int t, int& m0, i
 // Otherwise the stage alternates at run time, scales come step by step, and
 // each step's reads wait for the DMA it issued (correct, slower).
 template <bool OUT_BF16, bool GROUPED, int FA, int FB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mx_gemm_kernel(GemmArgs G) {
   __shared__ Stage S0, S1;
   __shared__ ScaleGroup SG0, SG1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int wm = wave >> 1, wn = wave & 1;   // wave's 128 x 128 quarter of the tile
+  const int wm = wave >> 2, wn = wave & 3;   // wave's 128 x 64 eighth of the tile
   const int nb = G.tiles_m * G.tiles_n;
   const int nk = G.K / kBK;
   const int my_tiles = (nb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   if (my_tiles <= 0) return;
 
-  v16f acc[4][4];
+  v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
   int m0, n0;
   tile_origin(G, blockIdx.x, m0, n0);
@@ -501,7 +519,8 @@ void mx_gemm_kernel(GemmArgs G) {
     }
     if (GROUPED && OUT_BF16 && G.vec16 && m0 + kBM <= G.M && n0 + kBN <= G.N) {
       // the tile's last step read S1 (the next tile's first DMA fills S0):
-      // once every wave's reads of it are complete, S1 stages the epilogue;
+      // once every wave's reads of it are complete, S1 stages the epilogue
+      // (8 slots of 8 KB over its a and b arrays, which are contiguous);
       // the next tile's first wait and barrier order its refill after
       // every wave's epilogue reads (s_waitcnt lgkmcnt(0) alone: 0xC07F)
       __builtin_amdgcn_s_waitcnt(0xC07F);

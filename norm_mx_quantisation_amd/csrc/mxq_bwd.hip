@@ -232,37 +232,41 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
 }
 
 // dgamma[d] = sum of in[r][d] over the rows r < rows (rows <= kBwdMaxGroups;
-// rows == 0 writes zeros and reads nothing). A workgroup covers 4 float4
-// columns. Wave w adds rows [w q, w q + q) (q = ceil(rows / 4)): lane l takes
-// float4 column l % 4 of rows w q + l / 4 + 16 k, k = 0..7, in that order,
-// so that one load instruction reads 16 rows of 64 contiguous bytes and the
-// eight loads go out together (one memory round trip). The 16 lanes of a
-// column then combine by a butterfly over lane bits 2..5 (every lane ends
-// with the same sum), and the four wave sums as (w0 + w1) + (w2 + w3).
+// rows == 0 writes zeros and reads nothing). A workgroup covers 8 float4
+// columns, one whole 128-byte line of each row, so that no line is fetched by
+// two workgroups (neighbouring workgroups usually run on different XCDs,
+// whose L2s do not share lines). Wave w adds rows [w q, w q + q)
+// (q = ceil(rows / 4)): lane l takes float4 column l % 8 of rows
+// w q + l / 8 + 8 k, k = 0..15, in that order, so that one load instruction
+// reads 8 whole lines and the sixteen loads go out together (one memory round
+// trip). The 8 lanes of a column then combine by a butterfly over lane bits
+// 3..5 (every lane ends with the same sum), and the four wave sums as
+// (w0 + w1) + (w2 + w3).
+constexpr int kColLoads = 16;  // loads per lane: 8 rows each, 128 rows per wave
 __global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int rows, int D4,
                                                            float* out) {
-  __shared__ float4 part[3][4];
+  __shared__ float4 part[3][8];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int c = lane & 3, rs = lane >> 2;
-  const int q = blockIdx.x * 4 + c;  // float4 column, < D4 (D4 % 4 == 0)
+  const int c = lane & 7, rs = lane >> 3;
+  const int q = blockIdx.x * 8 + c;  // float4 column, < D4 (D4 % 8 == 0)
   float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (rows > 0) {
     const int per = (rows + 3) / 4;
     const int r0 = wave * per;
     const int r1 = min(rows, r0 + per);
     const float4* src = reinterpret_cast<const float4*>(in);
-    float4 v[8];
+    float4 v[kColLoads];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(r0 + rs + 16 * k, rows - 1) * D4 + q];
+    for (int k = 0; k < kColLoads; ++k) v[k] = src[(size_t)min(r0 + rs + 8 * k, rows - 1) * D4 + q];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (r0 + rs + 16 * k < r1) {
+    for (int k = 0; k < kColLoads; ++k)
+      if (r0 + rs + 8 * k < r1) {
         a.x += v[k].x; a.y += v[k].y; a.z += v[k].z; a.w += v[k].w;
       }
   }
 #pragma unroll
-  for (int m = 4; m < kWave; m <<= 1) {
+  for (int m = 8; m < kWave; m <<= 1) {
     a.x += __shfl_xor(a.x, m);
     a.y += __shfl_xor(a.y, m);
     a.z += __shfl_xor(a.z, m);
@@ -283,9 +287,9 @@ __global__ __launch_bounds__(kThreads) void col_sum_kernel(const float* in, int 
 
 // Backward launch geometry: rows per workgroup, a multiple of 4, so that at
 // most kBwdMaxGroups partial rows are written; one column-sum launch then
-// adds them (each wave of it covers at most 128 rows: 16 per load, 8 loads).
+// adds them (each wave of it covers at most 128 rows: 8 per load, 16 loads).
 constexpr int64_t kBwdMaxGroups = 512;
-static_assert(kBwdMaxGroups <= 4 * 16 * 8, "the column sum reads at most 512 rows");
+static_assert(kBwdMaxGroups <= 4 * 8 * kColLoads, "the column sum reads at most 512 rows");
 
 struct BwdPlan {
   int64_t rows_per_group, groups;
@@ -338,7 +342,7 @@ mxq_status dispatch_bwd(const BwdArgs& A, int nc, unsigned groups, hipStream_t s
 
 mxq_status launch_col_sum(const float* in, int rows, int D, float* out, hipStream_t s) {
   const int D4 = D / 4;  // a multiple of 8 (D % 32 == 0)
-  hipLaunchKernelGGL(col_sum_kernel, dim3(D4 / 4), dim3(kThreads), 0, s, in, rows, D4, out);
+  hipLaunchKernelGGL(col_sum_kernel, dim3(D4 / 8), dim3(kThreads), 0, s, in, rows, D4, out);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }

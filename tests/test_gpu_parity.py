@@ -567,10 +567,10 @@ def check_backward(x, g, dy, inv, what="", dgamma=True):
         dg64, absum = oracle.mxnorm_bwd_dgamma(xs, dys, iv)
         # per column: each term rounds twice; in the main kernel each wave adds
         # its rows in order and the 4 wave sums combine in 2 levels; the column
-        # sum then adds up to 8 partial rows per lane in order, a 4-level
+        # sum then adds up to 16 partial rows per lane in order, a 3-level
         # butterfly and 2 levels over its waves
         per_wave = -(-T // 4)
-        n = min(per_wave, 64) + 2 + 8 + 4 + 2 + 2
+        n = min(per_wave, 64) + 2 + 16 + 3 + 2 + 2
         assert (np.abs(np_(dg) - dg64) <= n * U24 * absum + 1e-30).all(), what
     return dx, row_dot, dg
 
