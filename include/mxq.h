@@ -100,9 +100,9 @@ typedef struct {
 } mxq_rng;
 
 /* Forward flags. FORCE_REG / FORCE_LDS / FORCE_SPLIT select the variant of the
- * single-pass entry points (0 = automatic by D: split rows for D a multiple of
- * 512 above 4096, otherwise one wavefront per row up to 8192 and LDS staging
- * beyond; all variants give bit-identical results). SCALE_CEIL, accepted by every forward
+ * single-pass entry points (0 = automatic by D: one wavefront per row up to
+ * 4096, rows split over several wavefronts above; all variants give
+ * bit-identical results). SCALE_CEIL, accepted by every forward
  * entry point, replaces the OCP floor rule for the E8M0 block scale,
  * s = floor(log2 amax) - emax, by the round-up rule: the smallest s with
  * amax <= maxval * 2^s (maxval 448 for E4M3, 6 for E2M1), so no element of
@@ -112,7 +112,7 @@ enum {
   MXQ_FLAG_FORCE_REG = 1u,   /* row held in one wavefront's registers (D <= 8192) */
   MXQ_FLAG_FORCE_LDS = 2u,   /* row staged in LDS (D <= MXQ_MAX_D)                */
   MXQ_FLAG_SCALE_CEIL = 4u,  /* round-up E8M0 scale rule                          */
-  MXQ_FLAG_FORCE_SPLIT = 8u  /* row split over wavefronts' registers (D % 512 == 0) */
+  MXQ_FLAG_FORCE_SPLIT = 8u  /* row split over wavefronts' registers (D <= MXQ_MAX_D) */
 };
 
 /* Largest D of the register-resident MXNorm path and of any path. */
@@ -132,8 +132,7 @@ enum {
  *   codes, scales  outputs; inv_norm [T] fp32 output, may be NULL.
  * Errors: NULL (x, codes, scales), SHAPE, ALIGN, ARG (p <= 0 or NaN, unknown
  * elem/rnd/flags, SR without rng), UNSUPPORTED (D too large for the path,
- * FORCE_SPLIT with D not a multiple of 512, T * D >= 2^40, or more than
- * 2^31 - 1 workgroups of rows), HIP.
+ * T * D >= 2^40, or more than 2^31 - 1 workgroups of rows), HIP.
  */
 mxq_status mxnorm_fwd(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int64_t T,
                       int64_t D, float p, mxq_elem elem, mxq_round rnd, const mxq_rng* rng,

@@ -713,18 +713,20 @@ constexpr int kSplitMaxWaves = 16;  // wavefronts per workgroup of the split-row
 
 // A row split over W wavefronts of one workgroup: wave w holds statistic group
 // w, chunks [4w, 4w + 4) of the row, in VGPRs, with the gains of those chunks.
-// Rows are a whole number of chunks (D % 512 == 0). When the row's chunk count
-// is not a multiple of 4, the last wave's spare slots hold copies of the row's
-// last chunk: they are left out of the statistic, and they encode to the same
-// codes the real last chunk does (same data, gains, scale and random words),
-// written to the same place again; so the code has no chunk tests at all.
+// When the row's chunk count is not a multiple of 4, the last wave's spare
+// slots hold copies of the row's last chunk: they are left out of the
+// statistic, and they encode to the same codes the real last chunk does (same
+// data, gains, scale and random words), written to the same place again; so
+// the loads and the encode need no chunk tests. The row's last chunk may end
+// inside the row (D % 512 != 0): its lanes past the end count nothing and
+// store nothing, as in the one-wave kernel.
 // Each wave's group total meets the others in LDS and every wave adds all of
 // them in group order, so the statistic has exactly the bits of the one-wave
 // kernels. Every wave then encodes its own chunks: the work after the row's
 // last byte arrives is spread over W wavefronts (and the CU's SIMDs) instead
 // of one, and a wave needs 16 KB of loads in flight at most, so the kernel
 // keeps the occupancy of the short rows at any D.
-template <int ELEM, int RND, bool GAMMA, int STAT>
+template <int ELEM, int RND, bool GAMMA, int STAT, bool RAGGED>
 __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(NormArgs A, int nchunks) {
   constexpr int CPW = kGroupChunks;  // chunks per wave: one statistic group
   __shared__ __align__(16) float part[kSplitMaxWaves];
@@ -741,28 +743,38 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
   const int ncw = min(CPW, nchunks - c0);  // this wave's real chunks, >= 1
   // Chunk slot c of this wave is row chunk min(c0 + c, nchunks - 1); loads are
   // unconditional (a predicated load makes the compiler wait for the loads
-  // before it).
+  // before it). Only the row's last chunk can end inside the row; a lane's 8
+  // elements lie wholly inside or past the end (D % 32 == 0), and a lane past
+  // it re-reads the row's last 16 bytes and stores nothing.
+  // (RAGGED: D % 512 != 0; otherwise every lane is inside and nothing is tested)
   auto chunk_of = [&](int c) { return min(c0 + c, nchunks - 1); };
+  const bool last_in = !RAGGED || (nchunks - 1) * kChunk + dl < A.D;
+  auto lane_in = [&](int c) { return !RAGGED || c0 + c < nchunks - 1 || last_in; };
+  auto elem_of = [&](int c) {
+    return RAGGED ? min(chunk_of(c) * kChunk + dl, A.D - 8) : chunk_of(c) * kChunk + dl;
+  };
 
   uint4 graw[CPW];
   if (GAMMA) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) graw[c] = load16(A.gamma + chunk_of(c) * kChunk + dl);
+    for (int c = 0; c < CPW; ++c) graw[c] = load16(A.gamma + elem_of(c));
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
   uint4 raw[CPW];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) raw[c] = load16_stream(xr + chunk_of(c) * kChunk + dl);
+  for (int c = 0; c < CPW; ++c) raw[c] = load16_stream(xr + elem_of(c));
   __builtin_amdgcn_sched_barrier(0);
 
   uint32_t mb[CPW];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) mb[c] = quad_max_u32(absmax_bits8(raw[c]));
+  for (int c = 0; c < CPW; ++c) mb[c] = quad_max_u32(lane_in(c) ? absmax_bits8(raw[c]) : 0u);
   auto mb_stat = [&](int c) { return c < ncw ? mb[c] : 0u; };  // spare slots add nothing
   auto wave_group = [&](float* dst, int shift) {  // this wave's group total -> dst[w]
     float t;
     if constexpr (STAT == S_RMS)
-      t = group_sumsq<CPW>(0, CPW, [&](int c, float u) { return c < ncw ? sumsq8(raw[c], u) : u; });
+      t = group_sumsq<CPW>(0, CPW, [&](int c, float u) {
+        return c < ncw && lane_in(c) ? sumsq8(raw[c], u) : u;
+      });
     else
       t = group_terms<CPW>(0, CPW, mb_stat, shift, A.pmode, A.p);
     if (lane == 0) dst[w] = t;
@@ -834,18 +846,22 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void mxnorm_split_kernel(No
   float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
-    const int d = chunk_of(c) * kChunk + dl;
-    uint32_t code;
-    if (!GAMMA) {
-      code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, raw[c], g, mb[c], N);
-    } else {
-      unpack8(graw[c], g);
-      code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, raw[c], g, 0u, N);
+    if (lane_in(c)) {  // a whole quad (one block) is in or out
+      const int d = chunk_of(c) * kChunk + dl;
+      uint32_t code;
+      if (!GAMMA) {
+        code = mxnorm_chunk<ELEM, RND, G_NONE>(A, crow, nrow, d, raw[c], g, mb[c], N);
+      } else {
+        unpack8(graw[c], g);
+        code = mxnorm_chunk<ELEM, RND, G_GAIN>(A, crow, nrow, d, raw[c], g, 0u, N);
+      }
+      if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);  // spare slots: not flushed
     }
-    if ((lane & 3) == 0) put_scale(sc, c * 16 + (lane >> 2), code);  // spare slots: not flushed
   }
-  flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K + (uint64_t)(c0 * 16), ncw * 16,
-               A.sc_vec != 0, lane);
+  // this wave's blocks: 16 per real chunk, fewer in a last chunk that ends
+  // inside the row
+  flush_scales(sc, A.scales + (uint64_t)row * (uint64_t)A.K + (uint64_t)(c0 * 16),
+               min(ncw * 16, A.K - c0 * 16), A.sc_vec != 0, lane);
 }
 
 constexpr int kMaxLdsRows = 16;  // wavefronts (rows) per workgroup of the LDS-staged variant
@@ -1138,12 +1154,15 @@ mxq_status launch_mxnorm_lds(const NormArgs& A, int nc, hipStream_t s) {
 // wavefronts.
 template <int ELEM, int RND, bool GAMMA, int STAT>
 mxq_status launch_mxnorm_split(const NormArgs& A, int nc, hipStream_t s) {
-  if (A.D % kChunk != 0) return MXQ_ERR_UNSUPPORTED;  // whole chunks only
   const int W = (nc + kGroupChunks - 1) / kGroupChunks;
   if (W > kSplitMaxWaves) return MXQ_ERR_UNSUPPORTED;
   if (A.T > kMaxGrid) return MXQ_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((mxnorm_split_kernel<ELEM, RND, GAMMA, STAT>), dim3((unsigned)A.T),
-                     dim3(kWave * W), 0, s, A, nc);
+  if (A.D % kChunk != 0)
+    hipLaunchKernelGGL((mxnorm_split_kernel<ELEM, RND, GAMMA, STAT, true>), dim3((unsigned)A.T),
+                       dim3(kWave * W), 0, s, A, nc);
+  else
+    hipLaunchKernelGGL((mxnorm_split_kernel<ELEM, RND, GAMMA, STAT, false>), dim3((unsigned)A.T),
+                       dim3(kWave * W), 0, s, A, nc);
   MXQ_LAUNCH_CHECK();
   return MXQ_OK;
 }
@@ -1256,7 +1275,6 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   if (__builtin_popcount(flags & kForce) > 1) return MXQ_ERR_ARG;
   if (D > MXQ_MAX_D) return MXQ_ERR_UNSUPPORTED;
   if ((flags & MXQ_FLAG_FORCE_REG) && D > MXQ_MAX_D_REG) return MXQ_ERR_UNSUPPORTED;
-  if ((flags & MXQ_FLAG_FORCE_SPLIT) && D % kChunk != 0) return MXQ_ERR_UNSUPPORTED;
   if (T == 0) return MXQ_OK;
   if (gamma != nullptr && !aligned(gamma, 16)) return MXQ_ERR_ALIGN;
   if (inv_out != nullptr && !aligned(inv_out, 4)) return MXQ_ERR_ALIGN;
@@ -1281,18 +1299,16 @@ mxq_status norm_cast(const uint16_t* x, int64_t ldx, const uint16_t* gamma, int6
   A.ceil_rule = (flags & MXQ_FLAG_SCALE_CEIL) != 0;
   A.rng = make_stream(rng);
   const int nc = (int)((D + kChunk - 1) / kChunk);
-  // automatic: rows of whole chunks longer than 4096 elements split over
-  // several wavefronts; otherwise one wavefront per row up to 8192 elements,
-  // LDS staging beyond. At 4096 elements the two measure the same within a
-  // few percent either way over 2048..32768 rows; from 8192 the split rows
-  // are faster (shorter per-wave work after the row lands, fewer VGPRs)
-  const bool whole = D % kChunk == 0;
-  const int variant = (flags & MXQ_FLAG_FORCE_LDS)       ? V_LDS
-                      : (flags & MXQ_FLAG_FORCE_REG)     ? V_REG
-                      : (flags & MXQ_FLAG_FORCE_SPLIT)   ? V_SPLIT
-                      : (whole && nc > 2 * kGroupChunks) ? V_SPLIT
-                      : D > MXQ_MAX_D_REG                ? V_LDS
-                                                         : V_REG;
+  // automatic: rows longer than 4096 elements split over several
+  // wavefronts, shorter ones take one wavefront per row. At 4096 elements the
+  // two measure the same within a few percent either way over 2048..32768
+  // rows; from 8192 the split rows are faster (shorter per-wave work after
+  // the row lands, fewer VGPRs). The LDS-staged variant only when forced.
+  const int variant = (flags & MXQ_FLAG_FORCE_LDS)     ? V_LDS
+                      : (flags & MXQ_FLAG_FORCE_REG)   ? V_REG
+                      : (flags & MXQ_FLAG_FORCE_SPLIT) ? V_SPLIT
+                      : nc > 2 * kGroupChunks          ? V_SPLIT
+                                                       : V_REG;
   return dispatch_norm_cast<STAT>(A, elem, rnd, gamma != nullptr, variant, nc, (hipStream_t)stream);
 }
 

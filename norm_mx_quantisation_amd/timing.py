@@ -57,6 +57,10 @@ CASES = (
     ("wide D=32768 mxnorm split rows", "wide", "mxnorm", {"shape": (8192, 32768)}),
     ("wide D=32768 mxnorm LDS rows", "wide", "mxnorm",
      {"shape": (8192, 32768), "flags": mxq.MXQ_FLAG_FORCE_LDS}),
+    # rows that end inside their last 512-element chunk (16352 = 31.9 chunks)
+    ("wide D=16352 mxnorm split rows", "wide", "mxnorm", {"shape": (16384, 16352)}),
+    ("wide D=16352 mxnorm LDS rows", "wide", "mxnorm",
+     {"shape": (16384, 16352), "flags": mxq.MXQ_FLAG_FORCE_LDS}),
     ("swiglu_downproj mxcast rne", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_RNE}),
     ("swiglu_downproj mxcast sr", "swiglu_downproj", "mxcast", {"rnd": mxq.MXQ_SR}),
     ("swiglu_downproj mxcast rne round-up scales", "swiglu_downproj", "mxcast",

@@ -172,10 +172,9 @@ def test_mxnorm_argument_errors():
     assert norm(flags=16) == mxq.MXQ_ERR_ARG                     # unknown bit
     assert norm(flags=mxq.MXQ_FLAG_SCALE_CEIL | 3) == mxq.MXQ_ERR_ARG
     assert norm(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
-    # the split-row kernel takes rows of whole 512-element chunks only
-    assert norm(D=4128, ldx=4128, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
-    assert norm(D=256, ldx=256, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
+    assert norm(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32,
+                flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
     assert norm(gamma=A8) == mxq.MXQ_ERR_ALIGN
     assert norm(inv_norm=A16 + 2) == mxq.MXQ_ERR_ALIGN
 
@@ -186,7 +185,8 @@ def test_rms_fused_argument_errors():
     assert rms_fused(eps=float("inf")) == mxq.MXQ_ERR_ARG
     assert rms_fused(flags=3) == mxq.MXQ_ERR_ARG
     assert rms_fused(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_REG) == mxq.MXQ_ERR_UNSUPPORTED
-    assert rms_fused(D=8224, ldx=8224, flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
+    assert rms_fused(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32,
+                     flags=mxq.MXQ_FLAG_FORCE_SPLIT) == mxq.MXQ_ERR_UNSUPPORTED
     assert rms_fused(D=mxq.MXQ_MAX_D + 32, ldx=mxq.MXQ_MAX_D + 32) == mxq.MXQ_ERR_UNSUPPORTED
     assert rms_fused(gamma=A8) == mxq.MXQ_ERR_ALIGN
     assert rms_fused(inv=A16 + 2) == mxq.MXQ_ERR_ALIGN

@@ -262,13 +262,10 @@ ALL_VARIANTS = [mxq.MXQ_FLAG_FORCE_REG, mxq.MXQ_FLAG_FORCE_LDS, mxq.MXQ_FLAG_FOR
 
 def variants_for(D):
     """The forced variants that take rows of D elements: the one-wave kernel
-    up to MXQ_MAX_D_REG, the split-row kernel for whole 512-element chunks,
-    the LDS-staged kernel always."""
-    v = [mxq.MXQ_FLAG_FORCE_LDS]
+    up to MXQ_MAX_D_REG, the split-row and LDS-staged kernels always."""
+    v = [mxq.MXQ_FLAG_FORCE_LDS, mxq.MXQ_FLAG_FORCE_SPLIT]
     if D <= mxq.MXQ_MAX_D_REG:
         v.append(mxq.MXQ_FLAG_FORCE_REG)
-    if D % 512 == 0:
-        v.append(mxq.MXQ_FLAG_FORCE_SPLIT)
     return v
 
 
@@ -338,14 +335,14 @@ def test_mxnorm_register_and_lds_variants_are_bit_identical(D, gamma, elem, rnd)
             assert same_outputs(a, b), (p, flags)
 
 
-@pytest.mark.parametrize("D", [8224, 12288, 14336, 16384, 24576, 24608, 32768])
+@pytest.mark.parametrize("D", [8224, 12288, 14336, 16384, 24576, 24608, 32736, 32768])
 @pytest.mark.parametrize("gamma", [False, True])
 @pytest.mark.parametrize("elem,rnd", [("e4m3", "rne"), ("e2m1", "sr")])
 def test_wide_rows_split_and_lds_variants_are_bit_identical(D, gamma, elem, rnd):
-    # rows past one wavefront's registers: the LDS-staged kernel and, for
-    # whole chunks, the split-row kernel (up to 16 wavefronts of 4 chunks;
-    # 14336 leaves the last wavefront with one spare slot) give the same bits
-    # as the automatic choice
+    # rows past one wavefront's registers: the LDS-staged kernel and the
+    # split-row kernel (up to 16 wavefronts of 4 chunks; 14336 leaves the last
+    # wavefront with one spare slot; 8224, 24608 and 32736 end inside their
+    # last chunk) give the same bits as the automatic choice
     x = workloads.random_rows(11, D, seed=87 + D, device=DEV)
     x[4, :96] *= 40.0
     x[7] = x[7] * 2.0**-131                  # normaliser past fp32: the rescaled exchange
@@ -357,11 +354,13 @@ def test_wide_rows_split_and_lds_variants_are_bit_identical(D, gamma, elem, rnd)
             assert same_outputs(a, b), (p, flags)
 
 
-@pytest.mark.parametrize("D", [512, 1024, 2560, 3584, 4096, 6144, 8192, 14336, 16384, 32768])
+@pytest.mark.parametrize("D", [32, 96, 512, 1024, 1056, 2560, 3584, 4096, 4128, 6144, 8192,
+                               8224, 14336, 16384, 24608, 32736, 32768])
 def test_mxnorm_split_variant_against_the_oracle(D):
     # the split-row kernel on its own: one to sixteen wavefronts of 4 chunks,
-    # and a short last wavefront (2560, 3584, 14336: its spare slots repeat
-    # the row's last chunk)
+    # a short last wavefront (2560, 3584, 14336: its spare slots repeat the
+    # row's last chunk), and rows that end inside their last chunk (32 ...
+    # 32736; 1056 and 8224 with one block in it, 4128 also spare slots)
     x = workloads.random_rows(9, D, seed=89 + D, device=DEV)
     x[2, :96] *= 25.0
     x[5] = 0.0
@@ -458,16 +457,19 @@ def test_two_pass_special_rows(gamma, elem):
 
 @pytest.mark.parametrize("D", [mxq.MXQ_MAX_D, mxq.MXQ_MAX_D - 32])
 def test_widest_rows(D):
-    # the largest rows the C ABI accepts: the LDS-staged kernels with one row
-    # (and its bf16 gains) filling most of a workgroup's LDS; D - 32 leaves a
-    # ragged last chunk
+    # the largest rows the C ABI accepts: 16 wavefronts of the split-row
+    # kernel (automatic), and the LDS-staged kernels with one row (and its
+    # bf16 gains) filling most of a workgroup's LDS; D - 32 leaves a ragged
+    # last chunk
     x = workloads.random_rows(5, D, seed=97 + D, device=DEV)
     x[3, :64] *= 30.0
     g = workloads.random_gamma(D, seed=98, device=DEV)
-    check_mxnorm(x, g, 2.0, what=f"widest D={D}")
-    check_mxnorm(x, None, math.inf, what=f"widest D={D} p=inf no gamma")
-    check_mxnorm(x, g, 2.0, "e2m1", "sr", what=f"widest D={D} e2m1 sr")
-    check_rms_fused(x, g, what=f"widest D={D} rms-fused")
+    lds = mxq.MXQ_FLAG_FORCE_LDS
+    for flags in (0, lds):
+        check_mxnorm(x, g, 2.0, flags=flags, what=f"widest D={D} flags={flags}")
+        check_mxnorm(x, None, math.inf, flags=flags, what=f"widest D={D} p=inf no gamma")
+        check_mxnorm(x, g, 2.0, "e2m1", "sr", flags=flags, what=f"widest D={D} e2m1 sr")
+        check_rms_fused(x, g, flags=flags, what=f"widest D={D} rms-fused flags={flags}")
     check_two_pass(x, g, what=f"widest D={D} two-pass")
     check_mxcast(x, "e4m3", "sr", what=f"widest D={D} mxcast sr")
 
