@@ -340,7 +340,7 @@ __device__ __forceinline__ uint2 encode8_e4m3_rne(const float y[8], BlockScale s
 
 // 8 values -> 8 E2M1 codes packed in one word (element 2j in the low nibble).
 __device__ __forceinline__ uint32_t encode8_e2m1_rne(const float y[8], BlockScale s) {
-  const bool bad = s.bad;  // as for E4M3: select, no branch
+  const bool bad = s.bad;  // replaced after a wave-wide test, which compiles to selects here
   const float scale = __uint_as_float(s.code << 23);
   uint32_t q = __float_as_uint(y[0]);  // all four bytes are written below
   q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, y[0], y[1], scale, 0);
