@@ -53,7 +53,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 256;        // tile rows (A)
 constexpr int kBN = 256;        // tile columns (B rows)
-constexpr int kBK = 128;        // K per step: 4 MX blocks, two MFMAs deep
+constexpr int kBK = 128;        // K per step: 4 MX blocks, two MFMAs deep (FP4 x FP4: 256, see below)
 constexpr int kChunks = kBK / 16;   // 16-byte chunks per row and step (8-bit codes)
 
 // MFMA format codes of the element types, and the 16-byte chunks a row of
@@ -119,8 +119,9 @@ struct ScaleGroup {
   uint4 b[kBN];
 };
 
-// Steps to spread one step's code DMA over (blocks of 4 MFMAs each), so that
-// the wave does not stall issuing it all at once.
+// Pieces to spread one step's code DMA over (the first sub-step's 4 blocks of
+// MFMAs, one 32-row A block each), so that the wave does not stall issuing it
+// all at once.
 constexpr int kSpread = 4;
 
 // Direct-to-LDS loads of one operand's K step, CH chunks per row: a wave
