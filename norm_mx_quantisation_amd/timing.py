@@ -38,6 +38,18 @@ CASES = (
     ("llama3_8b_preattn floor nt row-gated", "llama3_8b_preattn", "floor", {"variant": 7}),
     ("llama3_8b_preattn floor nt row-gated staged", "llama3_8b_preattn", "floor",
      {"variant": 15}),
+    # the same call and floor probe at other row counts (D = 4096, N(0, 1) rows
+    # with gains): how much of the launch's ramp and drain the size amortises
+    ("rows T=2048 mxnorm p=2", "rows", "mxnorm", {"shape": (2048, 4096)}),
+    ("rows T=2048 floor nt row-gated staged", "rows", "floor", {"shape": (2048, 4096), "variant": 15}),
+    ("rows T=4096 mxnorm p=2", "rows", "mxnorm", {"shape": (4096, 4096)}),
+    ("rows T=4096 floor nt row-gated staged", "rows", "floor", {"shape": (4096, 4096), "variant": 15}),
+    ("rows T=16384 mxnorm p=2", "rows", "mxnorm", {"shape": (16384, 4096)}),
+    ("rows T=16384 floor nt row-gated staged", "rows", "floor", {"shape": (16384, 4096), "variant": 15}),
+    ("rows T=32768 mxnorm p=2", "rows", "mxnorm", {"shape": (32768, 4096)}),
+    ("rows T=32768 floor nt row-gated staged", "rows", "floor", {"shape": (32768, 4096), "variant": 15}),
+    ("rows T=65536 mxnorm p=2", "rows", "mxnorm", {"shape": (65536, 4096)}),
+    ("rows T=65536 floor nt row-gated staged", "rows", "floor", {"shape": (65536, 4096), "variant": 15}),
     ("llama3_8b_preattn mxnorm p=1", "llama3_8b_preattn", "mxnorm", {"p": 1.0}),
     ("llama3_8b_preattn mxnorm p=2 gamma folded", "llama3_8b_preattn", "mxnorm",
      {"p": 2.0, "gamma": False}),
