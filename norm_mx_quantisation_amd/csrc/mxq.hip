@@ -959,14 +959,13 @@ struct RmsArgs {
 };
 
 
+// y for one chunk; g holds the chunk's 8 gains when GAMMA.
 template <bool GAMMA>
 __device__ __forceinline__ void rms_chunk_out(const RmsArgs& A, int64_t row, int d, const uint4& xb,
-                                              float inv) {
+                                              float inv, const float g[8]) {
   float v[8];
   unpack8(xb, v);
   if (GAMMA) {
-    float g[8];
-    unpack8(load16(A.gamma + d), g);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = v[j] * g[j];
   }
@@ -982,24 +981,42 @@ __device__ __forceinline__ void rms_chunk_out(const RmsArgs& A, int64_t row, int
 
 // Row in registers (D <= NC * 512).
 template <int NC, bool GAMMA>
+// The workgroup's 4 rows share one LDS copy of gamma, staged as in
+// mxnorm_reg_kernel (gain loads first, the row loads in flight across the
+// staging barrier).
 __global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(RmsArgs A) {
+  __shared__ float4 g_lds[GAMMA ? NC * kWave * 2 : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= A.T) return;
-  const uint16_t* xr = A.x + row * A.ldx;
+  const bool live = row < A.T;
+  const uint16_t* xr = A.x + (live ? row : A.T - 1) * A.ldx;  // a dead wave reads the last row
   const int dl = lane * 8;
+  GammaStage<GAMMA ? NC : 1, kThreads> gs;
+  if (GAMMA) gs.load(A.gamma, A.D);
+  __builtin_amdgcn_sched_barrier(0);  // keep the gain loads ahead of the row loads
   uint4 raw[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) raw[c] = load_chunk(xr, c, dl, A.D);
+  __builtin_amdgcn_sched_barrier(0);
+  if (GAMMA) gs.store(g_lds);
+  if (!live) return;
   const float s = row_sumsq<NC>(NC, [&](int c, float t) {
     return c * kChunk + dl < A.D ? sumsq8(raw[c], t) : t;
   });
   const float inv = rms_inv(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  // widen each chunk again where it is used (see mxnorm_row_reg)
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w));
+  float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int d = c * kChunk + dl;
-    if (d < A.D) rms_chunk_out<GAMMA>(A, row, d, raw[c], inv);
+    if (d < A.D) {
+      if (GAMMA) gains(g_lds, c, lane, g);
+      rms_chunk_out<GAMMA>(A, row, d, raw[c], inv, g);
+    }
   }
 }
 
@@ -1016,9 +1033,13 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_wide_kernel(RmsArgs A, int n
   });
   const float inv = rms_inv(s, A.Df, A.eps);
   if (lane == 0 && A.inv_out) A.inv_out[row] = inv;
+  float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c = 0; c < nchunks; ++c) {
     const int d = c * kChunk + dl;
-    if (d < A.D) rms_chunk_out<GAMMA>(A, row, d, load16(xr + d), inv);
+    if (d < A.D) {
+      if (GAMMA) unpack8(load16(A.gamma + d), g);
+      rms_chunk_out<GAMMA>(A, row, d, load16(xr + d), inv, g);
+    }
   }
 }
 
