@@ -2,12 +2,14 @@
 
 Thin ctypes binding of libmxq.so. The functions named like the C entry points
 (mxnorm_fwd, rmsnorm_mxcast_fwd, rmsnorm_mxcast_fused_fwd, mxcast_fwd,
+mxnorm_bwd, mxnorm_bwd_noalloc, mx_gemm, nvfp4_cast_fwd, mxnorm_nvfp4_fwd,
 mxq_strerror, mxq_abi_version) take raw device pointers and sizes and return
 the status code, exactly as the C ABI does. The torch helpers (mxnorm,
-rmsnorm_mxcast, rmsnorm_mxcast_fused, mxcast) only check tensor metadata,
-allocate the outputs and pass pointers; every step of the computation runs in
-the HIP kernels. There is no CPU fallback: without the built library every
-call raises.
+rmsnorm_mxcast, rmsnorm_mxcast_fused, mxcast, mxnorm_backward, mx_matmul,
+nvfp4_cast, mxnorm_nvfp4) only check tensor metadata, allocate the outputs and
+pass pointers; every step of the computation runs in the HIP kernels.
+mx_views reinterprets outputs as torch's float8/float4 dtypes without a copy.
+There is no CPU fallback: without the built library every call raises.
 """
 
 from __future__ import annotations
