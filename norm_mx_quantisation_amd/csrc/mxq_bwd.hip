@@ -22,8 +22,10 @@ namespace {
 // normaliser inv = 1/G:  g = gamma * dy,  s = sum_i g_i x_i,
 // dx_i = inv * g_i - inv^3 * (s / D) * x_i,  dgamma_i = sum_t dy_ti x_ti inv_t.
 // fp32 order: g and dy * x are exact products of two bf16 values; s sums in
-// chunk order per lane, then over the wave as every RMS path does;
-// k = (inv * inv) * inv, c = k * (s / D), dx = bf16(inv * g - c * x).
+// chunk order per lane, then over the wave as every RMS path does, except for
+// rows of 2, 4, 6 or 8 chunks (split_dot below), where each half of the
+// row's chunks is summed that way and the two half sums add; k = (inv * inv)
+// * inv, c = k * (s / D), dx = bf16(inv * g - c * x).
 struct BwdArgs {
   const uint16_t* x;
   const uint16_t* dy;
@@ -39,6 +41,12 @@ struct BwdArgs {
   float Df;
   int rows_per_group;  // rows per workgroup, a multiple of kRowsPerBlock
 };
+
+// Rows of NC chunks whose dgamma backward splits each row over two
+// wavefronts (mxnorm_bwd_pair_kernel); every backward kernel then sums the row
+// dot by halves, so that dx and the row dot do not depend on whether dgamma
+// is wanted.
+constexpr bool split_dot(int nc) { return nc % 2 == 0 && nc <= 8; }
 
 // One workgroup of 4 waves takes rows [g R, g R + R); wave w takes rows
 // g R + w, g R + w + 4, ... in order and keeps its dgamma sums in registers
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
   for (int64_t row = row0 + wave; row < row_end; row += kRowsPerBlock) {
     const uint16_t* xr = A.x + row * A.ldx;
     const uint16_t* dr = A.dy + row * A.lddy;
-    float s = 0.0f;
+    float s = 0.0f, s_hi = 0.0f;  // s_hi: the second half's chunks (split_dot)
     float g[8] = {1, 1, 1, 1, 1, 1, 1, 1};
     const int64_t next = row + kRowsPerBlock;
     if (KEEP) {
@@ -138,8 +146,9 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
         unpack8(KEEP ? xk[c] : load16(xr + c * kChunk + dl), xv);
         unpack8(KEEP ? dk[c] : load16(dr + c * kChunk + dl), dv);
         if (GAMMA) gains(g_lds, c, lane, g);
+        float& t = (split_dot(NC) && c >= NC / 2) ? s_hi : s;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s = __builtin_fmaf(g[j] * dv[j], xv[j], s);
+        for (int j = 0; j < 8; ++j) t = __builtin_fmaf(g[j] * dv[j], xv[j], t);
       }
     }
     if (KEEP) {
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
         asm volatile("" : "+v"(dk[c].x), "+v"(dk[c].y), "+v"(dk[c].z), "+v"(dk[c].w));
       }
     }
-    s = sum_over_wave(s);
+    s = split_dot(NC) ? sum_over_wave(s) + sum_over_wave(s_hi) : sum_over_wave(s);
     const float a = A.inv[row];
     if (lane == 0 && A.row_dot) A.row_dot[row] = s;
     const float k = (a * a) * a;
@@ -226,6 +235,191 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
           *reinterpret_cast<float4*>(out + d) = make_float4(r[0], r[1], r[2], r[3]);
           *reinterpret_cast<float4*>(out + d + 4) = make_float4(r[4], r[5], r[6], r[7]);
         }
+      }
+    }
+  }
+}
+
+// dx and the dgamma partial rows with each row split over two wavefronts
+// (rows of NC = 2 H chunks, H <= 4). A workgroup of 8 waves takes rows
+// [g R, g R + R); wave w takes column half h = w & 1 (chunks [h H, h H + H))
+// of rows g R + r, g R + r + 4, ... (r = w >> 1), so a wave holds half the
+// registers of a whole-row wave and the workgroup keeps 4 waves per SIMD
+// where the whole-row kernel keeps 2. Each half's row dot (chunk order per
+// lane, then over the wave) meets its partner's in LDS at a barrier per step,
+// s = s_0 + s_1. Every wave runs the same number of steps, so the barriers
+// match; a step past a slot's last row does no work. The next row's half is
+// loaded once the current one is done with: holding both would take the wave
+// past 128 VGPRs, and with it the workgroup's 4 waves per SIMD. dgamma adds
+// the same terms in the same order as mxnorm_bwd_kernel (a slot's rows in
+// order, then (r0 + r2) + (r1 + r3) per column), so the partial rows are
+// bit-identical. dx leaves through non-temporal stores (measured faster on
+// [8192, 4096] and [32768, 4096]: 45.7-46.3 against 46.2-47.1 us per call,
+// 155.5 against 161.6-162.5 us).
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = kPairWaves * kWave;
+
+template <int H, bool GAMMA>
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void mxnorm_bwd_pair_kernel(BwdArgs A) {
+  constexpr int NC = 2 * H;
+  constexpr int kGFloat4 = GAMMA ? NC * kWave * 2 : 0;      // gains, as float4
+  constexpr int kRedFloat4 = 2 * 2 * H * 8 * kWave / 4;    // [half][slot][c][j][lane] floats
+  constexpr int kLds = kGFloat4 > kRedFloat4 ? kGFloat4 : kRedFloat4;
+  __shared__ float4 lds[kLds];   // the gains, then (after the last step) the dgamma combine
+  __shared__ float s_lds[2][4][2];  // [step parity][slot][half]
+  float4* g_lds = lds;
+  float* red = reinterpret_cast<float*>(lds);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int h = wave & 1, r = wave >> 1;
+  const int dl = lane * 8;
+  const int64_t row0 = (int64_t)blockIdx.x * A.rows_per_group;
+  const int64_t row_end = min(A.T, row0 + A.rows_per_group);
+  const int steps = (int)((row_end - row0 + kRowsPerBlock - 1) / kRowsPerBlock);  // uniform
+
+  constexpr int kGItems = (NC * kWave + kPairThreads - 1) / kPairThreads;
+  uint4 gr[GAMMA ? kGItems : 1];
+  if (GAMMA) {
+#pragma unroll
+    for (int k = 0; k < kGItems; ++k) {
+      const int i = min((int)threadIdx.x + k * kPairThreads, NC * kWave - 1);
+      gr[k] = load16(A.gamma + min(i * 8, A.D - 8));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The wave's chunks are h H + c, c < H; the last can end inside the row.
+  uint4 xk[H], dk[H];
+  auto load_half = [&](int64_t row, uint4 (&xb)[H], uint4 (&db)[H]) {
+#pragma unroll
+    for (int c = 0; c < H; ++c) {
+      xb[c] = load_chunk(A.x + row * A.ldx, h * H + c, dl, A.D);
+      db[c] = load_chunk(A.dy + row * A.lddy, h * H + c, dl, A.D);
+    }
+  };
+  if (row0 + r < row_end) load_half(row0 + r, xk, dk);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (GAMMA) {
+#pragma unroll
+    for (int k = 0; k < kGItems; ++k) {
+      const int i = (int)threadIdx.x + k * kPairThreads;
+      if (i < NC * kWave) {
+        float v[8];
+        unpack8(gr[k], v);
+        const int c = i / kWave, l = i % kWave;
+        g_lds[(2 * c) * kWave + l] = make_float4(v[0], v[1], v[2], v[3]);
+        g_lds[(2 * c + 1) * kWave + l] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc[H][8];
+#pragma unroll
+  for (int c = 0; c < H; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[c][j] = 0.0f;
+
+  for (int step = 0; step < steps; ++step) {
+    const int64_t row = row0 + r + (int64_t)step * kRowsPerBlock;
+    const int64_t next = row + kRowsPerBlock;
+    const bool live = row < row_end;  // uniform over the wave
+    float s = 0.0f;
+    float g[8] = {1, 1, 1, 1, 1, 1, 1, 1};
+    if (live) {
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        const int cc = h * H + c;
+        if (cc * kChunk + dl < A.D) {
+          float xv[8], dv[8];
+          unpack8(xk[c], xv);
+          unpack8(dk[c], dv);
+          if (GAMMA) gains(g_lds, cc, lane, g);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s = __builtin_fmaf(g[j] * dv[j], xv[j], s);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        asm volatile("" : "+v"(xk[c].x), "+v"(xk[c].y), "+v"(xk[c].z), "+v"(xk[c].w));
+        asm volatile("" : "+v"(dk[c].x), "+v"(dk[c].y), "+v"(dk[c].z), "+v"(dk[c].w));
+      }
+      s = sum_over_wave(s);
+      if (lane == 0) s_lds[step & 1][r][h] = s;
+    }
+    // Both halves' sums are in LDS after this barrier. The slot written at
+    // step + 2 is this step's again; no wave gets there before every wave has
+    // passed the barrier of step + 1, so after its read here.
+    __syncthreads();
+    if (live) {
+      s = s_lds[step & 1][r][0] + s_lds[step & 1][r][1];
+      const float a = A.inv[row];
+      if (h == 0 && lane == 0 && A.row_dot) A.row_dot[row] = s;
+      const float k = (a * a) * a;
+      const float cf = k * (s / A.Df);
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        const int cc = h * H + c;
+        const int d = cc * kChunk + dl;
+        if (d < A.D) {
+          float xv[8], dv[8], o[8];
+          unpack8(xk[c], xv);
+          unpack8(dk[c], dv);
+          if (GAMMA) gains(g_lds, cc, lane, g);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = a * (g[j] * dv[j]) - cf * xv[j];
+          const u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+          u32x4* dst = reinterpret_cast<u32x4*>(A.dx + (uint64_t)row * (uint64_t)A.D + (uint64_t)d);
+          __builtin_nontemporal_store(w, dst);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[c][j] += (dv[j] * xv[j]) * a;
+        }
+      }
+    }
+    if (next < row_end) load_half(next, xk, dk);
+  }
+
+  // The slots' sums per column: (r0 + r2) + (r1 + r3), through LDS (the gains
+  // are dead: the barrier below follows every wave's last read of them).
+  auto slot = [&](int sl, int c, int j) -> float& {
+    return red[(((h * 2 + sl) * H + c) * 8 + j) * kWave + lane];
+  };
+  __syncthreads();
+  if (r >= 2) {
+#pragma unroll
+    for (int c = 0; c < H; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) slot(r - 2, c, j) = acc[c][j];
+  }
+  __syncthreads();
+  if (r < 2) {
+#pragma unroll
+    for (int c = 0; c < H; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[c][j] += slot(r, c, j);
+  }
+  __syncthreads();
+  if (r == 1) {
+#pragma unroll
+    for (int c = 0; c < H; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) slot(0, c, j) = acc[c][j];
+  }
+  __syncthreads();
+  if (r == 0) {
+    float* out = A.partial + (uint64_t)blockIdx.x * (uint64_t)A.D;
+#pragma unroll
+    for (int c = 0; c < H; ++c) {
+      const int d = (h * H + c) * kChunk + dl;
+      if (d < A.D) {
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = acc[c][j] + slot(0, c, j);
+        *reinterpret_cast<float4*>(out + d) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(out + d + 4) = make_float4(o[4], o[5], o[6], o[7]);
       }
     }
   }
@@ -307,14 +501,23 @@ BwdPlan bwd_plan(int64_t T, int64_t D, bool dgamma = true) {
   return p;
 }
 
-// Non-temporal dx stores measured faster without dgamma (34.6 against
-// 34.8 us on [8192, 4096], 128 against 136 us on [32768, 4096]) and with it at
-// 64 rows per workgroup ([32768, 4096]: 157 against 163 us), but slower at 16
-// rows per workgroup ([8192, 4096]: 45.7 against 43.4 us); the dgamma kernel
+// With dgamma, rows of 2, 4, 6 or 8 chunks go to the pair kernel (on
+// [8192, 4096] 45.7-46.3 against 47.8-47.9 us per call for the whole-row
+// kernel, on [32768, 4096] 155.5 against 159 us). In the whole-row kernel,
+// non-temporal dx stores measured faster without dgamma (34.6 against 34.8 us
+// on [8192, 4096], 128 against 136 us on [32768, 4096]) and with it at 64
+// rows per workgroup ([32768, 4096]: 157 against 163 us), but slower at 16
+// rows per workgroup ([8192, 4096]: 45.7 against 43.4 us); its dgamma form
 // takes them from 32 rows per workgroup on.
 template <int NC, bool GAMMA, bool DGAMMA>
 mxq_status launch_bwd(const BwdArgs& A, unsigned groups, hipStream_t s) {
   constexpr bool kKeep = NC <= 8;
+  if constexpr (DGAMMA && split_dot(NC)) {
+    hipLaunchKernelGGL((mxnorm_bwd_pair_kernel<NC / 2, GAMMA>),
+                       dim3(groups), dim3(kPairThreads), 0, s, A);
+    MXQ_LAUNCH_CHECK();
+    return MXQ_OK;
+  }
   if (!DGAMMA || A.rows_per_group >= 32)
     hipLaunchKernelGGL((mxnorm_bwd_kernel<NC, GAMMA, DGAMMA, kKeep, true>), dim3(groups),
                        dim3(kThreads), 0, s, A);

@@ -577,7 +577,11 @@ def check_backward(x, g, dy, inv, what="", dgamma=True):
     return dx, row_dot, dg
 
 
-@pytest.mark.parametrize("D", [32, 96, 512, 1056, 4096, 8192])
+# D: one chunk or less (32, 96, 512), odd chunk counts (1056: 3, 2560: 5,
+# 8192: 16) and the row split over two wavefronts with dgamma (1024, 1568,
+# 3072, 3616, 4096: 2, 4, 6, 8, 8 chunks; 1568 and 3616 end inside their
+# last chunk)
+@pytest.mark.parametrize("D", [32, 96, 512, 1024, 1056, 1568, 2560, 3072, 3616, 4096, 8192])
 @pytest.mark.parametrize("gamma", [False, True])
 def test_backward_shapes(D, gamma):
     T = 13
@@ -589,10 +593,11 @@ def test_backward_shapes(D, gamma):
     check_backward(x, g, dy, inv, what=f"bwd D={D} gamma={gamma}")
 
 
-@pytest.mark.parametrize("T", [1, 4, 5, 64, 700, 3000])
-def test_backward_row_counts(T):
-    # ragged row blocks per workgroup, and more rows than partial groups
-    D = 512
+@pytest.mark.parametrize("D", [512, 2048])
+@pytest.mark.parametrize("T", [1, 4, 5, 64, 700, 3000, 20001])
+def test_backward_row_counts(T, D):
+    # ragged row blocks per workgroup (rows a workgroup's wavefronts do not
+    # all have), and more rows than partial groups
     x = workloads.random_rows(T, D, seed=304 + T, device=DEV)
     dy = workloads.random_rows(T, D, seed=305 + T, device=DEV)
     g = workloads.random_gamma(D, seed=306, device=DEV)
