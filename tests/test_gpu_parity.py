@@ -1219,3 +1219,46 @@ def test_graph_replays_match_eager():
         assert same_outputs(out, eager), rep
         assert same_outputs(out_tp, eager_tp[:3]) and torch.equal(y_tp, eager_tp[3]), rep
         assert same_outputs(out_c[:2], eager_c), rep
+
+
+def test_graph_replays_match_eager_backward_and_gemm():
+    # the backward (dx, row dot, dgamma through the workspace and the column
+    # sum) and the MX GEMM captured in a HIP graph and replayed several times,
+    # with eager work and synchronisations between replays, reproduce the
+    # eager outputs bit for bit
+    x, g = workloads.make_inputs("llama3_8b_preattn", device=DEV, rows=1000)
+    T, D = x.shape
+    dy = workloads.random_rows(T, D, seed=331, device=DEV)
+    codes, scales, inv = mxq.mxnorm(x, g, 2.0)
+    w = workloads.random_rows(384, D, seed=332, device=DEV)
+    wc, ws_, _ = mxq.mxnorm(w, None, 2.0)
+    eager_b = mxq.mxnorm_backward(x, g, dy, inv)
+    eager_c = mxq.mx_matmul(codes, scales, wc, ws_, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    wsb = mxq.mxnorm_bwd_workspace_size(T, D)
+    out_b = (torch.empty_like(eager_b[0]), torch.empty_like(eager_b[1]),
+             torch.empty_like(eager_b[2]), torch.empty((wsb // 4,), dtype=torch.float32, device=DEV))
+    out_c = torch.empty_like(eager_c)
+
+    def work():
+        mxq.mxnorm_backward(x, g, dy, inv, out=out_b)
+        mxq.mx_matmul(codes, scales, wc, ws_, out=out_c)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        for t in (*out_b, out_c):
+            t.view(torch.uint8).fill_(0xA5 + rep)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+                   for u, v in zip(out_b[:3], eager_b)), rep
+        assert torch.equal(out_c.view(torch.uint8), eager_c.view(torch.uint8)), rep

@@ -85,3 +85,41 @@ def test_noalloc_backward_empty_batch_zeroes_dgamma():
     _, _, dg = noalloc_backward(e, None, e, inv)
     torch.cuda.synchronize()
     assert (dg == 0).all()
+
+
+def test_noalloc_backward_in_a_graph_matches_the_workspace_entry_point():
+    # the callers this entry point serves capture it: replayed several times,
+    # with eager work and synchronisations between replays, the captured call
+    # reproduces mxnorm_bwd's outputs bit for bit
+    x, g, dy, inv = case(1500, 4096, seed=651)
+    ref = mxq.mxnorm_backward(x, g, dy, inv)
+    torch.cuda.synchronize()
+    T, D = x.shape
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device=DEV)
+    row_dot = torch.empty((T,), dtype=torch.float32, device=DEV)
+    dgamma = torch.empty((D,), dtype=torch.float32, device=DEV)
+
+    def work():
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        st = mxq.mxnorm_bwd_noalloc(_ptr(x), x.stride(0), _ptr(g), _ptr(dy), dy.stride(0),
+                                    _ptr(inv), T, D, _ptr(dx), _ptr(row_dot), _ptr(dgamma), stream)
+        assert st == mxq.MXQ_OK, mxq.mxq_strerror(st)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        for t in (dx, row_dot, dgamma):
+            t.view(torch.uint8).fill_(0x5A + rep)
+        check_same(*case(64, 2048, seed=661 + rep))   # other calls use the array in between
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx.view(torch.int16), ref[0].view(torch.int16)), rep
+        assert torch.equal(row_dot.view(torch.int32), ref[1].view(torch.int32)), rep
+        assert torch.equal(dgamma.view(torch.int32), ref[2].view(torch.int32)), rep
