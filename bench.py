@@ -8,9 +8,11 @@ MALL cannot serve a step from cache. Prints one JSON line.
 The same line carries, for context: the p = 1 variant, the two-pass
 RMSNorm -> MXCast comparison path and the single-pass exact-RMS comparator
 (each timed the same way), a plain
-device-to-device copy of the same byte count, the roofline of the fused
-kernel (per-launch HIP-event durations on the launch stream) and the CPU
-oracle timed on a bounded sample.
+device-to-device copy of the same byte count, a bytes-only kernel with the
+fused call's exact traffic, layout, row dependency and gain staging (the
+floor at this size; libmxq_floor.so, no method arithmetic), the roofline of
+the fused kernel (per-launch HIP-event durations on the launch stream) and
+the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -375,6 +377,21 @@ def main():
     def copy(i):
         dst[i % ROTATE].copy_(src[i % ROTATE])
 
+    # the bytes-only reference kernel on the same buffers: non-temporal loads
+    # and stores, stores gated on a wave-wide reduction of the whole row, the
+    # gains staged through LDS behind a barrier (variant 15)
+    from norm_mx_quantisation_amd import timing as mxq_timing
+    floor_lib = mxq_timing.floor_lib()
+    FLOOR_VARIANT = 15
+
+    def floor_probe(i):
+        k = i % ROTATE
+        st = floor_lib.mxq_floor_stream(vp(xs[k].data_ptr()), vp(g.data_ptr()), T, D,
+                                        vp(outs[k][0].data_ptr()), vp(outs[k][1].data_ptr()),
+                                        FLOOR_VARIANT, vp(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"mxq_floor_stream returned {st}")
+
     K, W = args.steps, args.warmup
     step_s, launch_s, graph_steps, graph_how = time_graph(torch, fused_raw(2.0), K, W)  # headline: p = 2
     main_t = time_launches(torch, fused_raw(2.0), K, W)              # per-launch kernel time
@@ -385,6 +402,7 @@ def main():
     tp_hot = time_launches(torch, two_pass_hot, K, W)
     rs_step_s = time_graph(torch, rms_fused_raw, K, W)[0]
     cp_t = time_launches(torch, copy, K, W)
+    floor_step_s = time_graph(torch, floor_probe, K, W)[0]
     tiny = tiny_latency(torch, mxq, workloads, K)
     linear = mxnormlinear(torch, mxq, workloads, xs, outs, ys, g, min(K, 40))
 
@@ -450,6 +468,14 @@ def main():
             },
             "d2d_copy_same_bytes": {"kernel_mean_us": round(cp_t["kernel_mean_s"] * 1e6, 3),
                                     "GB/s": round(2 * copy_n / cp_t["kernel_mean_s"] / 1e9, 2)},
+            "bytes_only_floor_probe": {
+                "what": "same traffic and layout, no method arithmetic: non-temporal loads and "
+                        "stores, stores gated on a wave-wide row reduction, gains staged in LDS",
+                "ms_per_step": round(floor_step_s * 1e3, 6),
+                "GB/s": round(nbytes / floor_step_s / 1e9, 2),
+                "pct_hbm_peak": round(100 * nbytes / floor_step_s / 1e9 / HBM_PEAK_GBS, 2),
+                "mxnorm_time_over_floor": round(step_s / floor_step_s, 4),
+            },
             "tiny_64x256_latency": tiny,
             # context: the MXNorm page reports +1.3% for a whole Llama 3 8B layer
             # in MXFP8 on GB200 (section 3.2); these steps are the norm and one
