@@ -190,10 +190,12 @@ mxq_status mxcast_fwd(const uint16_t* x, int64_t ldx, int64_t T, int64_t D, mxq_
  *   s_t      = sum_i g_i * x_i
  *   dx_ti    = inv_t * g_i - inv_t^3 * (s_t / D) * x_ti      (rounded to bf16)
  *   dgamma_i = sum_t dy_ti * x_ti * inv_t                      (fp32)
- * fp32 order: g and dy * x are exact; s sums each lane's chunks in order and
- * then the wave, as the RMS paths do; k = (inv*inv)*inv, c = k * (s/D),
- * dx = bf16(inv*g - c*x). dgamma sums rows in a fixed order (bit-reproducible
- * from run to run).
+ * fp32 order: g and dy * x are exact; s sums each lane's 512-element chunks
+ * in order and then the wave, as the RMS paths do, except for rows of 2, 4, 6
+ * or 8 chunks, where each half of the chunks is summed that way and the two
+ * half sums add (the same order with and without dgamma); k = (inv*inv)*inv,
+ * c = k * (s/D), dx = bf16(inv*g - c*x). dgamma sums rows in a fixed order
+ * (bit-reproducible from run to run).
  *   x [T, D] bf16, row stride ldx; dy [T, D] bf16, row stride lddy.
  *   gamma [D] bf16 or NULL (gamma == 1).  inv_norm [T] fp32.
  *   dx [T, D] bf16 contiguous output.  row_dot [T] fp32 output (s), may be NULL.
