@@ -353,7 +353,10 @@ void mxnorm_bwd_pair_kernel(BwdArgs A) {
     }
     // Both halves' sums are in LDS after this barrier. The slot written at
     // step + 2 is this step's again; no wave gets there before every wave has
-    // passed the barrier of step + 1, so after its read here.
+    // passed the barrier of step + 1, so after its read here. (A handshake
+    // between the two waves of a row alone, through per-slot step flags in
+    // LDS, measured no faster: 46.0-47.2 against 45.5-45.8 us per call on
+    // [8192, 4096].)
     __syncthreads();
     if (live) {
       s = s_lds[step & 1][r][0] + s_lds[step & 1][r][1];
