@@ -79,7 +79,19 @@ extern "C" {
 
 #define MXQ_ABI_VERSION 4
 
-typedef enum {
+/* The enumerations below are passed by value and checked by the library, so a
+ * caller may hand it any int (an unknown element type, say, is rejected with
+ * MXQ_ERR_ARG). Compiled as C++ (the library itself), each gets int as its
+ * fixed underlying type: every int is then a value of the type, so checking an
+ * out-of-range argument is defined behaviour, and the type keeps the size and
+ * calling convention of a C enum. */
+#ifdef __cplusplus
+#define MXQ_ENUM_INT : int
+#else
+#define MXQ_ENUM_INT
+#endif
+
+typedef enum MXQ_ENUM_INT {
   MXQ_OK = 0,
   MXQ_ERR_NULL = 1,        /* a required pointer is NULL                         */
   MXQ_ERR_SHAPE = 2,       /* T < 0, D <= 0, D % 32 != 0, or ldx < D             */
@@ -89,8 +101,8 @@ typedef enum {
   MXQ_ERR_HIP = 6          /* the HIP runtime refused the launch                 */
 } mxq_status;
 
-typedef enum { MXQ_E4M3 = 0, MXQ_E2M1 = 1 } mxq_elem;
-typedef enum { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
+typedef enum MXQ_ENUM_INT { MXQ_E4M3 = 0, MXQ_E2M1 = 1 } mxq_elem;
+typedef enum MXQ_ENUM_INT { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
 
 /* Stochastic-rounding stream: read only when rnd == MXQ_SR. The same
  * (seed, offset) reproduces the same bits; callers advance offset per call. */
@@ -236,7 +248,7 @@ mxq_status mxnorm_bwd_noalloc(const uint16_t* x, int64_t ldx, const uint16_t* ga
                               void* stream);
 
 /* Element type of a GEMM result. */
-typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;
+typedef enum MXQ_ENUM_INT { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_type;
 
 /*
  * MX GEMM, the consumer of the MX output (MXNorm page, §2.3: the gain is
