@@ -17,7 +17,7 @@ import norm_mx_quantisation_amd as mxq
 import oracle
 from norm_mx_quantisation_amd import workloads
 from parity_util import (assert_bf16_bits, assert_bits, check_normaliser, compare_reference, host,
-                         np_)
+                         np_, table)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -1072,6 +1072,50 @@ def test_workload_mxfp4_full():
     out = gpu_mxnorm(x, g, 2.0, "e2m1")
     for r0, r1 in _batches(x.shape[0], 8192):
         check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r1), out=out, what=f"mxfp4 rows {r0}")
+
+
+def _dequant_gpu(codes, scales, elem):
+    """Decoded MX values [T, D] as fp32 on the device (E4M3 through torch's
+    float8_e4m3fn view, E2M1 through its 16-entry value table)."""
+    if elem == "e4m3":
+        v = codes.view(torch.float8_e4m3fn).float()
+    else:
+        tab = torch.tensor(table("e2m1"), dtype=torch.float32, device=codes.device)
+        lo, hi = tab[(codes & 0xF).long()], tab[(codes >> 4).long()]
+        v = torch.stack([lo, hi], dim=-1).reshape(codes.shape[0], -1)
+    sc = torch.exp2(scales.float() - 127.0)
+    return v * sc.repeat_interleave(32, dim=1)
+
+
+@pytest.mark.parametrize("wl,elem", [("tiny", "e4m3"), ("llama3_8b_preattn", "e4m3"),
+                                     ("longseq_t3", "e4m3"), ("mxfp4", "e2m1")])
+@pytest.mark.parametrize("p", [1.0, 2.0])
+def test_output_bounds_every_workload(wl, elem, p):
+    # Whole tensors, any size: MXNorm's output is bounded through K (MXNorm
+    # page, §2.2): G >= (max_k m_k^p / K)^(1/p), so max |x| / G <= K^(1/p), and
+    # max |y| <= max |gamma| K^(1/p); RMSNorm's is max |gamma| sqrt(D) (§2.2's
+    # sqrt(D) bound), for the two-pass path and the single-pass comparator.
+    # The decoded codes exceed max |y| by at most their rounding: the block
+    # maximum sits in the scale's top binade (relative step 2^-3 for E4M3 at
+    # worst, 2^-2 for E2M1's top binade of 4 and 6, so at most 1/8 up).
+    x, g = workloads.make_inputs(wl, device=DEV)
+    T, D = x.shape
+    K = D // 32
+    slack = 1 + 2.0 ** -3
+    for gam in (None, g):
+        gmax = 1.0 if gam is None else float(gam.float().abs().max())
+        codes, scales, inv = gpu_mxnorm(x, gam, p, elem)
+        assert torch.isfinite(inv).all()
+        m = float(_dequant_gpu(codes, scales, elem).abs().max())
+        assert m <= gmax * K ** (1.0 / p) * slack, (wl, p, m, K ** (1.0 / p))
+        if p == 2.0:
+            for c, s in (mxq.rmsnorm_mxcast(x, gam, 1e-5, elem)[:2],
+                         mxq.rmsnorm_mxcast_fused(x, gam, 1e-5, elem)[:2]):
+                torch.cuda.synchronize()
+                m = float(_dequant_gpu(c, s, elem).abs().max())
+                assert m <= gmax * math.sqrt(D) * slack, (wl, m, math.sqrt(D))
+        del codes, scales, inv
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------- caller buffers
