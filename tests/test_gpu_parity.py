@@ -1074,6 +1074,50 @@ def test_workload_mxfp4_full():
         check_mxnorm(x, g, 2.0, "e2m1", rows=(r0, r1), out=out, what=f"mxfp4 rows {r0}")
 
 
+def _c_pB(p, B):
+    """c(p, B) for N(0,1) elements: (E[M^p])^(1/p), M the maximum of B i.i.d.
+    |N(0,1)| (by quadrature of its tail)."""
+    import scipy.integrate
+    import scipy.special
+    tail = lambda m: p * m ** (p - 1) * (1.0 - scipy.special.erf(m / math.sqrt(2.0)) ** B)
+    val, _ = scipy.integrate.quad(tail, 0, 60, limit=200)
+    return val ** (1.0 / p)
+
+
+@pytest.mark.parametrize("p", [1.0, 2.0])
+def test_kernel_statistic_theorem1_constant(p):
+    # MXNorm page, §2.2 (Theorem 1): over N(0,1) rows the power mean of the
+    # block maxima concentrates at c(p, 32) times the RMS. The kernel's own
+    # normaliser on 16384 rows of 4096, within 5 standard errors.
+    T, D = 16384, 4096
+    x = workloads.random_rows(T, D, seed=337, device=DEV)
+    _, _, inv = gpu_mxnorm(x, None, p)
+    rms = x.double().pow(2).mean(dim=1).sqrt()
+    ratio = (1.0 / inv.double()) / rms
+    c = _c_pB(p, 32)
+    sem = float(ratio.std()) / math.sqrt(T)
+    assert abs(float(ratio.mean()) - c) < 5 * sem + 1e-3, (float(ratio.mean()), c, sem)
+
+
+def test_kernel_statistics_on_constant_magnitude_rows():
+    # |x_i| = a everywhere: every block maximum is a, so G = a for every p and
+    # the RMS is a; each sum is exact in fp32 at these sizes, so every kernel
+    # statistic must report exactly RN32(1/a) (the comparator with eps = 0)
+    gen = torch.Generator().manual_seed(338)
+    for D in (256, 4096, 8192):
+        for a in (0.375, 3.0, 1.0 / 64):
+            sign = torch.where(torch.rand((6, D), generator=gen) < 0.5, -1.0, 1.0)
+            x = (sign * a).to(torch.bfloat16).to(DEV)
+            want = torch.full((6,), 1.0 / a, dtype=torch.float64).float().to(DEV)
+            for p in (1.0, 2.0, math.inf):
+                for flags in [0] + variants_for(D):
+                    _, _, inv = gpu_mxnorm(x, None, p, flags=flags)
+                    assert torch.equal(inv, want), (D, a, p, flags, inv)
+            _, _, inv_r = mxq.rmsnorm_mxcast_fused(x, None, 0.0)
+            torch.cuda.synchronize()
+            assert torch.equal(inv_r, want), (D, a, inv_r)
+
+
 def _dequant_gpu(codes, scales, elem):
     """Decoded MX values [T, D] as fp32 on the device (E4M3 through torch's
     float8_e4m3fn view, E2M1 through its 16-entry value table)."""
