@@ -18,8 +18,9 @@
 // Operand layout of that instruction for 8-bit data (probed on the device):
 // lane l carries row l % 32 of its 32 x 64 operand; its 32 bytes are K
 // [16 g, 16 g + 16) then [32 + 16 g, 32 + 16 g + 16), g = l / 32; the scale
-// of K block b (32 columns) of row r is the low byte of lane r + 32 b's scale
-// register, whose other bytes must be zero. Result element v of lane l is
+// of K block b (32 columns) of row r is the byte of lane r + 32 b's scale
+// register that the instruction's op_sel value (0-3) names; the other bytes
+// are ignored. Result element v of lane l is
 // row 8 (v / 4) + 4 (l / 32) + v % 4 (of the first operand) and column l % 32
 // (of the second). Here the instruction takes B as its first operand and A
 // as its second, so each lane's 16 results are C row l % 32 at 4 groups of 4
@@ -222,9 +223,19 @@ __device__ __forceinline__ uint4 scale_words(const uint32_t* sc, int h, int rl) 
   return *reinterpret_cast<const uint4*>(sc + h * 128 + rl * 4);
 }
 
-// E8M0 byte `b` of a scale word, alone in its register (the instruction
-// requires the other bytes to be zero).
-__device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >> (8 * b)) & 0xFFu); }
+// The scaled MFMA takes each operand's E8M0 scale from one byte of a 32-bit
+// register, the byte chosen by the instruction's op_sel field (an immediate,
+// the same for every lane). A scale word holds a row's 4 blocks of one
+// 128-deep K step, block b in byte b; the lanes of half g = 0 need blocks 0
+// and 2 (sub-steps 0 and 1), those of half g = 1 blocks 1 and 3. Shifting a
+// half-1 lane's word right by one byte puts its blocks in bytes 0 and 2 as
+// well, so one shift per word and step replaces a byte extraction per MFMA,
+// and sub-step kk selects byte 2 (kk & 1).
+template <int FB, int FA, int SEL>
+__device__ __forceinline__ v16f mfma_scaled(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, SEL, (int)sb, SEL,
+                                                          (int)sa);
+}
 
 // One K step of the wave's 128 x 64 eighth: the next step's DMA into
 // `fill`, then this step's operands from `use` into the MFMAs, in sub-steps
@@ -277,16 +288,25 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
     sbw4[0] = sbw.x, sbw4[1] = sbw.y, sbw4[2] = 0, sbw4[3] = 0;
     saw4[0] = saw.x, saw4[1] = saw.y, saw4[2] = saw.z, saw4[3] = saw.w;
   }
+  const uint32_t shift = 8u * (uint32_t)g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < 2) sbw4[j] >>= shift;
+    saw4[j] >>= shift;
+    if (WIDE) {
+      if (j < 2) sbw4h[j] >>= shift;
+      saw4h[j] >>= shift;
+    }
+  }
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    // the sub-step's MX block of the lane's half: byte 2 kk + g of the step's scales
-    const int sb = 2 * (kk & 1) + g;
+    // the sub-step's MX block of the lane's half: byte 2 (kk & 1) of its shifted word
     v8i bo[2];
-    int sbv[2];
+    uint32_t sbv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       bo[j] = operand<FB, CB>(use->b, wn * 64 + j * 32 + rl, kk, g);
-      sbv[j] = scale_byte(kk < 2 ? sbw4[j] : sbw4h[j], sb);
+      sbv[j] = kk < 2 ? sbw4[j] : sbw4h[j];
     }
     v8i ao = operand<FA, CA>(use->a, wm * 128 + rl, kk, g);
 #pragma unroll
@@ -294,12 +314,12 @@ __device__ __forceinline__ void k_step(const GemmArgs& G, Stage* fill, const Sta
       v8i ao_next;
       if (i + 1 < 4) ao_next = operand<FA, CA>(use->a, wm * 128 + (i + 1) * 32 + rl, kk, g);
       if (GROUPED && kk == 0) load_codes_piece<CA, CB>(G, fill, fm0, fn0, fks, wave, lane, i);
-      const int sav = scale_byte(kk < 2 ? saw4[i] : saw4h[i], sb);
+      const uint32_t sav = kk < 2 ? saw4[i] : saw4h[i];
       // B is the first operand, so each lane's results are consecutive columns of C
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo[j], ao, acc[i][j], FB, FA,
-                                                                    0, sbv[j], 0, sav);
+        acc[i][j] = (kk & 1) ? mfma_scaled<FB, FA, 2>(bo[j], ao, acc[i][j], sbv[j], sav)
+                             : mfma_scaled<FB, FA, 0>(bo[j], ao, acc[i][j], sbv[j], sav);
       if (i + 1 < 4) ao = ao_next;
       // keep the next block's reads ahead of this block's MFMAs (the
       // scheduler would otherwise sink them to their use and wait on each)
