@@ -252,7 +252,9 @@ __global__ __launch_bounds__(kThreads) void mxnorm_bwd_kernel(BwdArgs A) {
 // loaded once the current one is done with: holding both would take the wave
 // past 128 VGPRs, and with it the workgroup's 4 waves per SIMD (a form that
 // kept the column sums in LDS to make room for the next half measured 3-6%
-// slower: 47.6-48.9 against 45.9 us per call on [8192, 4096]). dgamma adds
+// slower: 47.6-48.9 against 45.9 us per call on [8192, 4096]; reloading each
+// chunk's registers with the next row's chunk as soon as its dx is stored
+// measured 47.4-47.8 against 45.4-46.3 us, the same on [32768, 4096]). dgamma adds
 // the same terms in the same order as mxnorm_bwd_kernel (a slot's rows in
 // order, then (r0 + r2) + (r1 + r3) per column), so the partial rows are
 // bit-identical. dx leaves through non-temporal stores (measured faster on
