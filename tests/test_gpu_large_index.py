@@ -1,6 +1,7 @@
 """Tensors past 2^32 elements: [2^20 + 3, 4096] bf16 rows (8 GiB of input).
 
-Element indices, input byte offsets and E4M3 code byte offsets pass 2^32 here,
+Element indices, input byte offsets and E4M3 code byte offsets pass 2^32 here
+(and on [2^18 + 3, 16384], rows of the split-row and LDS-staged kernels),
 and so does the stochastic-rounding counter, which is the element's index
 row * D + d (the Philox counter of the SR reading takes all 64 bits of it).
 A slip to 32-bit arithmetic anywhere in a kernel's row offsets or in its
@@ -19,6 +20,7 @@ import norm_mx_quantisation_amd as mxq
 import oracle
 from norm_mx_quantisation_amd import workloads
 from parity_util import assert_bits, host, np_
+from test_gpu_nvfp4 import assert_same, check_norm
 from test_gpu_parity import (OFFSET, SEED, THREADS, U24, check_mxcast, check_mxnorm,
                              check_rms_fused, check_two_pass)
 
@@ -26,6 +28,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 T, D = (1 << 20) + 3, 4096
 WINDOWS = [(0, 16), ((1 << 19) - 8, (1 << 19) + 8), ((1 << 20) - 8, T)]
+# rows past 8192: the split-row kernel (and the LDS-staged one, forced)
+TW, DW = (1 << 18) + 3, 16384
+WIDE_WINDOWS = [(0, 4), ((1 << 17) - 2, (1 << 17) + 2), ((1 << 18) - 2, TW)]
 
 
 @pytest.fixture(scope="module")
@@ -38,6 +43,19 @@ def big():
     x = workloads.random_rows(T, D, seed=9001, device=DEV)
     g = workloads.random_gamma(D, seed=9002, device=DEV)
     x[(1 << 20) + 1, :64] *= 100.0   # an outlier block in the last rows
+    torch.cuda.synchronize()
+    yield x, g
+    del x, g
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def wide():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert TW * DW > 1 << 32
+    x = workloads.random_rows(TW, DW, seed=9011, device=DEV)
+    g = workloads.random_gamma(DW, seed=9012, device=DEV)
     torch.cuda.synchronize()
     yield x, g
     del x, g
@@ -74,6 +92,32 @@ def test_two_pass_and_fused_rms_past_2_32_elements(big):
     check_two_pass(x, g, rows=w, what=f"two-pass rows {w}")
     torch.cuda.empty_cache()
     check_rms_fused(x, g, rnd="sr", rows=w, what=f"fused rms sr rows {w}")
+
+
+def test_nvfp4_past_2_32_elements(big):
+    x, g = big
+    out = mxq.mxnorm_nvfp4(x, g, 2.0, 1.0)
+    torch.cuda.synchronize()
+    for r0, r1 in WINDOWS:
+        check_norm(x[r0:r1], g, 2.0, 1.0, what=f"mxnorm nvfp4 rows {(r0, r1)}",
+                   out=tuple(t[r0:r1] for t in out))
+    del out
+    c, sc = mxq.nvfp4_cast(x, 1.0)
+    torch.cuda.synchronize()
+    for r0, r1 in WINDOWS:
+        oc, os_ = oracle.nvfp4_cast(host(x[r0:r1]), 1.0, threads=THREADS)
+        assert_same(np_(sc[r0:r1]), os_, f"nvfp4 cast scales rows {(r0, r1)}")
+        assert_same(np_(c[r0:r1]), oc, f"nvfp4 cast codes rows {(r0, r1)}")
+
+
+@pytest.mark.parametrize("flags", [0, mxq.MXQ_FLAG_FORCE_LDS])
+def test_wide_rows_sr_past_2_32_elements(wide, flags):
+    x, g = wide
+    out = mxq.mxnorm(x, g, 2.0, "e4m3", "sr", SEED, OFFSET, flags)
+    torch.cuda.synchronize()
+    for w in WIDE_WINDOWS:
+        check_mxnorm(x, g, 2.0, "e4m3", "sr", rows=w, out=out,
+                     what=f"wide mxnorm sr flags={flags} rows {w}")
 
 
 def test_backward_past_2_32_elements(big):
