@@ -9,7 +9,7 @@ counter would show in the last rows. Windows of rows at the start, across
 element 2^31 and from just before element 2^32 to the last row are compared
 with the oracle, which takes each window's first row, so that its row indices
 and counters are the tensor's own. The backward's dgamma, a sum over all rows,
-is compared on a few columns over every row.
+is compared on a few columns over every row. The MX GEMM takes A and C past 4 GiB.
 """
 
 import numpy as np
@@ -22,7 +22,7 @@ from norm_mx_quantisation_amd import workloads
 from parity_util import assert_bits, host, np_
 from test_gpu_nvfp4 import assert_same, check_norm
 from test_gpu_parity import (OFFSET, SEED, THREADS, U24, check_mxcast, check_mxnorm,
-                             check_rms_fused, check_two_pass)
+                             check_rms_fused, check_two_pass, gemm_bound, random_mx_operand)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -144,4 +144,30 @@ def test_backward_past_2_32_elements(big):
     got = np_(dg[cols])
     assert (np.abs(got - dg64) <= n * U24 * absum + 1e-30).all(), (got, dg64)
     del dx, row_dot, dg, dy
+    torch.cuda.empty_cache()
+
+
+def test_gemm_past_2_32_bytes():
+    """MXFP8 GEMM with A [2^20 + 40, 4096] (4 GiB of codes, a ragged last
+    tile) and bf16 C [2^20 + 40, 2048] (4 GiB): rows at the start, across
+    byte 2^31 and past byte 2^32 of A and C against the oracle, to the GEMM's
+    parity bound."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M, N, K = (1 << 20) + 40, 2048, 4096
+    gen = torch.Generator(device=DEV).manual_seed(9021)
+    A = torch.randint(0, 256, (M, K), generator=gen, device=DEV, dtype=torch.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x3C                          # no NaN codes
+    SA = torch.randint(115, 135, (M, K // 32), generator=gen, device=DEV, dtype=torch.uint8)
+    B, SB = random_mx_operand(N, K, seed=9022)
+    c = mxq.mx_matmul(A, SA, B, SB, torch.bfloat16)
+    torch.cuda.synchronize()
+    for r0, r1 in [(0, 8), ((1 << 19) - 4, (1 << 19) + 4), ((1 << 20) - 4, M)]:
+        c64, ab = oracle.mx_gemm(np_(A[r0:r1]), np_(SA[r0:r1]), np_(B), np_(SB), K, "e4m3",
+                                 "e4m3", threads=THREADS)
+        got = c[r0:r1].double().cpu().numpy()
+        bound = gemm_bound(ab, K, c64, True)
+        assert np.isfinite(c64).all() and np.isfinite(got).all()
+        assert (np.abs(got - c64) <= bound).all(), ((r0, r1), np.abs(got - c64).max())
+    del A, SA, c
     torch.cuda.empty_cache()
